@@ -1,0 +1,79 @@
+// aba_internal.h -- declarations shared by the HIP sources of libaba.so.
+// Kernels are written for gfx950 (CDNA4): 64-lane wavefronts, bf16 MFMA,
+// 160 KB LDS per CU, 256 CUs in 8 XCDs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace aba {
+
+constexpr int kBlock = 128;       // tokens per query block and per key block
+constexpr int kMaxBlocks = 1024;  // blocks per sequence the score/sample kernels hold in LDS
+constexpr int kMaxClusters = 8;
+
+enum Dtype : int { kF32 = 0, kBF16 = 1 };
+
+// Host launchers; each returns the HIP status of its launch.
+hipError_t launch_kmeans(const void *q, int dtype, int B, int H, int N, int N_pad, int D, int NB, int C, int T,
+                         float *cent, float *weight, hipStream_t s);
+hipError_t launch_pool(const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB, float *kbar,
+                       hipStream_t s);
+hipError_t launch_score(const float *cent, const float *weight, const float *kbar, int B, int H, int NB, int C, int D,
+                        float scale, float *scores, hipStream_t s);
+hipError_t launch_sample(const float *scores, int B, int H, int NB, int K, uint64_t seed, int cap, int32_t *idx,
+                         int32_t *cnt, float *w, hipStream_t s);
+hipError_t launch_attend(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad, int D,
+                         int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap, bool full,
+                         void *out, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+
+// Eight consecutive elements of a row as fp32.
+__device__ __forceinline__ void load8(const uint16_t *p, float out[8])
+{
+    uint4 r = *reinterpret_cast<const uint4 *>(p);
+    out[0] = bf16_lo(r.x); out[1] = bf16_hi(r.x);
+    out[2] = bf16_lo(r.y); out[3] = bf16_hi(r.y);
+    out[4] = bf16_lo(r.z); out[5] = bf16_hi(r.z);
+    out[6] = bf16_lo(r.w); out[7] = bf16_hi(r.w);
+}
+__device__ __forceinline__ void load8(const float *p, float out[8])
+{
+    float4 a = *reinterpret_cast<const float4 *>(p);
+    float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X.  Remap the
+// hardware id so that every XCD (with its own L2) works through one contiguous
+// range of logical ids: heads stay together and neighbouring query blocks of a
+// head, which keep overlapping key blocks, share an L2.
+__device__ __forceinline__ int xcd_contiguous_id(int hw_id, int n)
+{
+    constexpr int kXcds = 8;
+    const int per = n / kXcds, extra = n % kXcds;
+    const int xcd = hw_id % kXcds, k = hw_id / kXcds;
+    return xcd * per + (xcd < extra ? xcd : extra) + k;
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x)
+{
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+}  // namespace aba

@@ -1,0 +1,183 @@
+// api.hip -- the C ABI of libaba.so (declared in include/aba.h): argument
+// validation, workspace layout and kernel launches.  Host code only; every
+// computation runs in the kernels of kmeans.hip, pool_score.hip, sample.hip and
+// attend.hip.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/aba.h"
+#include "aba_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+aba_status fail(aba_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+aba_status fail(aba_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+aba_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ABA_OK;
+    return fail(ABA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Workspace {
+    size_t cent, weight, kbar, total;
+};
+
+Workspace workspace_layout(const aba_plan_t &p)
+{
+    const size_t rows = (size_t)p.batch * p.heads * p.n_blocks;
+    Workspace w;
+    w.cent = 0;
+    w.weight = align256(rows * p.n_clusters * p.head_dim * sizeof(float));
+    w.kbar = w.weight + align256(rows * p.n_clusters * sizeof(float));
+    w.total = w.kbar + align256(rows * p.head_dim * sizeof(float));
+    return w;
+}
+
+// A plan must be exactly what aba_plan produces for its own fields.
+aba_status check_plan(const aba_plan_t *p)
+{
+    if (!p) return fail(ABA_E_INVALID, "plan is NULL");
+    aba_plan_t ref;
+    const aba_status st = aba_plan(&ref, p->batch, p->heads, p->seq_len, p->head_dim, (aba_dtype)p->dtype,
+                                   p->n_clusters, p->kmeans_iters, p->budget, p->softmax_scale);
+    if (st != ABA_OK) return st;
+    if (ref.n_blocks != p->n_blocks || ref.seq_pad != p->seq_pad || ref.list_cap != p->list_cap ||
+        ref.block != p->block || ref.workspace_bytes != p->workspace_bytes)
+        return fail(ABA_E_INVALID, "plan fields are inconsistent; fill the plan with aba_plan");
+    return ABA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+aba_status aba_plan(aba_plan_t *p, int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim, aba_dtype dtype,
+                    int32_t n_clusters, int32_t kmeans_iters, int32_t budget, float softmax_scale)
+{
+    g_last_error.clear();
+    if (!p) return fail(ABA_E_INVALID, "plan is NULL");
+    if (batch < 1 || heads < 1 || seq_len < 1 || head_dim < 1)
+        return fail(ABA_E_INVALID, "sizes must be positive (batch=%d heads=%d seq_len=%d head_dim=%d)", batch, heads,
+                    seq_len, head_dim);
+    if (n_clusters < 1) return fail(ABA_E_INVALID, "n_clusters must be >= 1 (got %d)", n_clusters);
+    if (kmeans_iters < 0) return fail(ABA_E_INVALID, "kmeans_iters must be >= 0 (got %d)", kmeans_iters);
+    if (budget < 1) return fail(ABA_E_INVALID, "budget must be >= 1 (got %d)", budget);
+    if (!(std::isfinite(softmax_scale))) return fail(ABA_E_INVALID, "softmax_scale is not finite");
+    if (dtype != ABA_F32 && dtype != ABA_BF16) return fail(ABA_E_INVALID, "unknown dtype %d", (int)dtype);
+    if (dtype == ABA_BF16 && head_dim != 64 && head_dim != 128)
+        return fail(ABA_E_UNSUPPORTED, "bf16 kernels exist for head_dim 64 and 128 (got %d)", head_dim);
+    if (dtype == ABA_F32 && head_dim != 64)
+        return fail(ABA_E_UNSUPPORTED, "fp32 kernels exist for head_dim 64 (got %d)", head_dim);
+    if (n_clusters > ABA_MAX_CLUSTERS)
+        return fail(ABA_E_UNSUPPORTED, "at most %d clusters (got %d)", ABA_MAX_CLUSTERS, n_clusters);
+    if (kmeans_iters > 64) return fail(ABA_E_UNSUPPORTED, "at most 64 k-means rounds (got %d)", kmeans_iters);
+    const int64_t nb = ((int64_t)seq_len + ABA_BLOCK - 1) / ABA_BLOCK;
+    if (nb > ABA_MAX_BLOCKS)
+        return fail(ABA_E_UNSUPPORTED, "at most %d blocks of %d tokens (got %lld)", ABA_MAX_BLOCKS, ABA_BLOCK,
+                    (long long)nb);
+    if ((int64_t)batch * heads * nb > 0x7FFFFFFF) return fail(ABA_E_UNSUPPORTED, "batch*heads*blocks exceeds 2^31");
+
+    std::memset(p, 0, sizeof *p);
+    p->batch = batch;
+    p->heads = heads;
+    p->seq_len = seq_len;
+    p->head_dim = head_dim;
+    p->block = ABA_BLOCK;
+    p->n_blocks = (int32_t)nb;
+    p->seq_pad = (int32_t)nb * ABA_BLOCK;
+    p->n_clusters = n_clusters;
+    p->kmeans_iters = kmeans_iters;
+    p->budget = budget;
+    p->list_cap = (int32_t)nb;
+    p->dtype = dtype;
+    p->softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    p->workspace_bytes = workspace_layout(*p).total;
+    return ABA_OK;
+}
+
+aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *scores, float *centroids,
+                     float *cluster_w, float *pooled_k, void *workspace, hipStream_t stream)
+{
+    g_last_error.clear();
+    aba_status st = check_plan(p);
+    if (st != ABA_OK) return st;
+    if (!q || !k || !scores) return fail(ABA_E_INVALID, "q, k and scores must be non-NULL");
+    if ((!centroids || !cluster_w || !pooled_k) && !workspace)
+        return fail(ABA_E_INVALID, "workspace of %llu bytes is required unless every optional output is given",
+                    (unsigned long long)p->workspace_bytes);
+    const Workspace lay = workspace_layout(*p);
+    char *ws = static_cast<char *>(workspace);
+    float *cent = centroids ? centroids : reinterpret_cast<float *>(ws + lay.cent);
+    float *wgt = cluster_w ? cluster_w : reinterpret_cast<float *>(ws + lay.weight);
+    float *kbar = pooled_k ? pooled_k : reinterpret_cast<float *>(ws + lay.kbar);
+
+    const int B = p->batch, H = p->heads, N = p->seq_len, NP = p->seq_pad, D = p->head_dim, NB = p->n_blocks;
+    st = hip_status(aba::launch_kmeans(q, p->dtype, B, H, N, NP, D, NB, p->n_clusters, p->kmeans_iters, cent, wgt, stream),
+                    "kmeans launch");
+    if (st != ABA_OK) return st;
+    st = hip_status(aba::launch_pool(k, p->dtype, B, H, N, NP, D, NB, kbar, stream), "pool launch");
+    if (st != ABA_OK) return st;
+    return hip_status(aba::launch_score(cent, wgt, kbar, B, H, NB, p->n_clusters, D, p->softmax_scale, scores, stream),
+                      "score launch");
+}
+
+aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, int32_t *idx, int32_t *cnt, float *w,
+                      hipStream_t stream)
+{
+    g_last_error.clear();
+    aba_status st = check_plan(p);
+    if (st != ABA_OK) return st;
+    if (!scores || !idx || !cnt || !w) return fail(ABA_E_INVALID, "scores, idx, cnt and w must be non-NULL");
+    return hip_status(aba::launch_sample(scores, p->batch, p->heads, p->n_blocks, p->budget, seed, p->list_cap, idx, cnt,
+                                         w, stream),
+                      "sample launch");
+}
+
+aba_status aba_attend(const aba_plan_t *p, const void *q, const void *k, const void *v, const int32_t *idx,
+                      const int32_t *cnt, const float *w, void *out, hipStream_t stream)
+{
+    g_last_error.clear();
+    aba_status st = check_plan(p);
+    if (st != ABA_OK) return st;
+    if (!q || !k || !v || !idx || !cnt || !w || !out)
+        return fail(ABA_E_INVALID, "q, k, v, idx, cnt, w and out must be non-NULL");
+    return hip_status(aba::launch_attend(q, k, v, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad, p->head_dim,
+                                         p->n_blocks, p->softmax_scale, idx, cnt, w, p->list_cap, false, out, stream),
+                      "attend launch");
+}
+
+aba_status aba_attend_full(const aba_plan_t *p, const void *q, const void *k, const void *v, void *out,
+                           hipStream_t stream)
+{
+    g_last_error.clear();
+    aba_status st = check_plan(p);
+    if (st != ABA_OK) return st;
+    if (!q || !k || !v || !out) return fail(ABA_E_INVALID, "q, k, v and out must be non-NULL");
+    return hip_status(aba::launch_attend(q, k, v, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad, p->head_dim,
+                                         p->n_blocks, p->softmax_scale, nullptr, nullptr, nullptr, p->list_cap, true, out,
+                                         stream),
+                      "attend_full launch");
+}
+
+const char *aba_last_error(void) { return g_last_error.c_str(); }
+
+const char *aba_version(void) { return "aba 0.1.0 (gfx950)"; }
+
+}  // extern "C"
