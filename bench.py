@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the AB-Attention sparse attention layer on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic layer with its
+inputs resident in HBM:
+
+    aba_score  (IBCS: k-means clustering, key pooling, block scores)
+    aba_sample (SIP: inclusion probabilities, Philox draws, list compaction)
+    aba_attend (block-sparse flash attention with inverse-inclusion weights)
+
+The workload is the 32K-token single video DiT layer (batch 1, 12 heads,
+head_dim 128, bf16, 21x30x52 latent grid, 10% key-block density).  ``value`` is
+the effective (dense-equivalent) throughput 4*B*H*N^2*D / step time.  Printed as
+one JSON line, with the roofline of the dominant kernel (aba_attend, measured
+with HIP events on the stream it runs on) and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload single_layer]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from block_sparse_attention_38_amd import aba, synth  # noqa: E402
+from block_sparse_attention_38_amd.workloads import ALL, CLUSTERS, KMEANS_ITERS  # noqa: E402
+
+METRIC = "ms/call and effective TFLOP/s of sparse attention, 32K-token video layer"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+ATTEND_SRC = os.path.join(ROOT, "block_sparse_attention_38_amd", "csrc", "attend.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_single_layer_traffic.json")
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kept_flops(p, cnt: np.ndarray, idx: np.ndarray) -> float:
+    """4 * D * sum over kept (query block, key block) pairs of valid queries x valid keys."""
+    N, NB = p.seq_len, p.n_blocks
+    valid = np.minimum(128, N - 128 * np.arange(NB)).astype(np.float64)   # valid tokens per block
+    total = 0.0
+    flat_c = cnt.reshape(-1, NB)
+    flat_i = idx.reshape(-1, NB, idx.shape[-1])
+    for r in range(flat_c.shape[0]):
+        for qb in range(NB):
+            c = int(flat_c[r, qb])
+            total += valid[qb] * valid[flat_i[r, qb, :c]].sum()
+    return 4.0 * p.head_dim * total
+
+
+def source_digest(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_entry():
+    """HBM traffic per attend launch from the committed rocprofv3 counter runs, if the
+    kernel source has not changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("attend_src_sha256_16") != source_digest(ATTEND_SRC):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, p, q, k, v, seed: int, target_s: float):
+    """The oracle (as it stands) on a bounded sample: whole heads when it is fast
+    enough, else evenly spaced query blocks of head 0."""
+    import oracle
+
+    N, NB, D = w.seq_len, w.n_blocks, w.head_dim
+    valid = np.minimum(128, N - 128 * np.arange(NB))
+
+    def run(h, blocks):
+        qh, kh, vh = (np.ascontiguousarray(x[:1, h:h + 1].float().numpy()) for x in (q, k, v))
+        t0 = time.perf_counter()
+        cents, wts = [], []
+        for qb in blocks:
+            c, wt, _, _ = oracle.kmeans_block(qh[0, 0, qb * 128:qb * 128 + valid[qb]], C=p.n_clusters,
+                                              T=p.kmeans_iters)
+            cents.append(c)
+            wts.append(wt)
+        kbar = oracle.pool(kh, N)
+        s = oracle.score(np.stack(cents)[None, None], np.stack(wts)[None, None], kbar, p.softmax_scale)
+        idx_s, cnt_s, w_s, _ = oracle.sample(s.astype(np.float32), p.budget, seed)
+        idx = np.zeros((1, 1, NB, NB), np.int32)
+        cnt = np.zeros((1, 1, NB), np.int32)
+        wl = np.zeros((1, 1, NB, NB), np.float32)
+        for r, qb in enumerate(blocks):
+            idx[0, 0, qb], cnt[0, 0, qb], wl[0, 0, qb] = idx_s[0, 0, r], cnt_s[0, 0, r], w_s[0, 0, r]
+        oracle.attend(qh, kh, vh, N, idx, cnt, wl, items=[(0, 0, qb) for qb in blocks], scale=p.softmax_scale)
+        return time.perf_counter() - t0
+
+    probe = list(range(0, NB, max(1, NB // 16)))[:16]
+    per_block = run(0, probe) / len(probe)
+    n_blocks = target_s / max(per_block, 1e-6)
+    total_t, rows, what = 0.0, 0, ""
+    if n_blocks >= NB:
+        heads = 0
+        while heads < w.heads and total_t < target_s:
+            total_t += run(heads, list(range(NB)))
+            heads += 1
+        rows = heads * float(valid.sum())
+        what = f"every query block of heads 0..{heads - 1} ({heads} of {w.heads} heads)"
+    else:
+        blocks = sorted(set(np.linspace(0, NB - 1, max(len(probe), int(n_blocks))).astype(int).tolist()))
+        total_t = run(0, blocks)
+        rows = float(valid[blocks].sum())
+        what = f"{len(blocks)} of {NB} query blocks of head 0 (of {w.heads} heads)"
+    flops = 4.0 * D * N * rows          # dense-equivalent work of the sampled query rows
+    return {
+        "value": flops / total_t / 1e12,
+        "unit": "TFLOP/s (effective, dense-equivalent)",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"full layer pass (k-means, pooling, scores, sampling, attention) for {what}; "
+                  f"{total_t:.1f} s on {oracle.max_threads()} threads ({platform.machine()})",
+        "seconds": total_t,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="single_layer", choices=sorted(ALL))
+    ap.add_argument("--density", type=float, default=None)
+    ap.add_argument("--seed", type=int, default=7)
+    ap.add_argument("--dense-reps", type=int, default=5)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer shards over heads with no exchange, and no multi-GPU "
+              "figure is produced (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    w = ALL[args.workload]
+    density = w.densities[0] if args.density is None else args.density
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: {w.description}; density {density}")
+    t0 = time.perf_counter()
+    q, k, v = synth.make_inputs(w, seed=1001)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    p = aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, CLUSTERS, KMEANS_ITERS, w.budget(density))
+    B, H, NB, cap, D = p.batch, p.heads, p.n_blocks, p.list_cap, p.head_dim
+    scores = torch.empty(B, H, NB, NB, dtype=torch.float32, device=dev)
+    ws = aba.workspace(p, dev)
+    lists = (torch.empty(B, H, NB, cap, dtype=torch.int32, device=dev),
+             torch.empty(B, H, NB, dtype=torch.int32, device=dev),
+             torch.empty(B, H, NB, cap, dtype=torch.float32, device=dev))
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        aba.score(p, qd, kd, out=scores, ws=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        aba.sample(p, scores, args.seed, out=lists)
+        if ev is not None:
+            ev[2].record(stream)
+        aba.attend(p, qd, kd, vd, *lists, out=out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    score_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sample_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    attend_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (score {score_ms:.3f}, sample {sample_ms:.3f}, "
+        f"attend {attend_ms:.3f})")
+
+    idx, cnt, wt = (x.cpu().numpy() for x in lists)
+    kflops = kept_flops(p, cnt, idx)
+    dense_flops = w.dense_flops
+    realised_density = float(cnt.mean() / NB)
+
+    dense_ms = None
+    if not args.no_dense:
+        aba.attend_full(p, qd, kd, vd, out=out)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.dense_reps):
+            aba.attend_full(p, qd, kd, vd, out=out)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / args.dense_reps
+        log(f"[bench] dense attention: {dense_ms:.3f} ms")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB device-to-device copy done")
+
+    # scoring-stage bytes: q and k read once, centroids/weights/pooled keys written and re-read, scores written
+    elem = 2 if w.dtype == "bf16" else 4
+    rows = B * H * NB
+    score_bytes = (2 * B * H * w.seq_len * D * elem
+                   + 2 * 4 * rows * (p.n_clusters * D + p.n_clusters + D) + 4 * rows * NB)
+    attend_tflops = kflops / (attend_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": dense_flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s (effective, dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian-mixture video tokens; no model weights)",
+        "config": {
+            "workload": w.name, "batch": B, "heads": H, "seq_len": w.seq_len, "seq_pad": p.seq_pad,
+            "head_dim": D, "grid": list(w.grid), "density": density, "budget_blocks": p.budget,
+            "clusters": p.n_clusters, "kmeans_iters": p.kmeans_iters, "block": 128, "seed": args.seed,
+        },
+        "stages_ms": {"score": score_ms, "sample": sample_ms, "attend": attend_ms},
+        "dense_attention_ms": dense_ms,
+        "speedup_vs_dense": {"layer": dense_ms / ms_per_step, "attention": dense_ms / attend_ms} if dense_ms else None,
+        "realised_density": realised_density,
+        "kept_tflop_per_call": kflops / 1e12,
+        "attend_kept_tflops": attend_tflops,
+        "score_stage_gbs": score_bytes / (score_ms * 1e-3) / 1e9,
+        "score_stage_hbm_frac": score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "roofline": {
+            "kernel": "attend_bf16_kernel<128>" if w.dtype == "bf16" else "attend_f32_kernel<64>",
+            "bound": "mfma",
+            "achieved": attend_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": attend_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic_entry(),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, p, q, k, v, args.seed, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {result['cpu_baseline']['value']:.4g} TFLOP/s effective")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -52,11 +52,11 @@ __device__ __forceinline__ int vt_slot(int d, int s) { return d * 32 + (s ^ (d &
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
-template <int D>
+template <int D, bool full>
 __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
-    uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap, float scale_log2, int full)
+    uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap, float scale_log2)
 {
     constexpr int kChunks = D / 8;     // 16-byte chunks per K row
     constexpr int KS = D / 16;         // k-steps of S^T = K Q^T
@@ -234,12 +234,12 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
 // fp32 path: two lanes per query row, each owning half of the head dimension;
 // key/value tiles of 64 rows in LDS.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool full>
 __global__ __launch_bounds__(256) void attend_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                                          const float *__restrict__ v, const int32_t *__restrict__ idx,
                                                          const int32_t *__restrict__ cnt, const float *__restrict__ w,
                                                          float *__restrict__ out, int N, int N_pad, int NB, int cap,
-                                                         float scale_log2, int full)
+                                                         float scale_log2)
 {
     constexpr int kTile = 64, HD = D / 2, kChunk = 16;
     __shared__ float4 k_s[kTile][D / 4];
@@ -325,24 +325,35 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const float *__restrict
 
 }  // namespace
 
-hipError_t launch_attend(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad, int D,
-                         int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap, bool full,
-                         void *out, hipStream_t s)
+template <bool full>
+hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad,
+                           int D, int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap,
+                           void *out, hipStream_t s)
 {
     const dim3 grid((unsigned)((long)B * H * NB)), block(256);
     const float sl2 = scale * kLog2e;
     if (dtype == kBF16 && D == 128)
-        attend_bf16_kernel<128><<<grid, block, 0, s>>>((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
-                                                      idx, cnt, w, (uint16_t *)out, N, N_pad, NB, cap, sl2, full);
+        attend_bf16_kernel<128, full><<<grid, block, 0, s>>>((const uint16_t *)q, (const uint16_t *)k,
+                                                            (const uint16_t *)v, idx, cnt, w, (uint16_t *)out, N, N_pad,
+                                                            NB, cap, sl2);
     else if (dtype == kBF16 && D == 64)
-        attend_bf16_kernel<64><<<grid, block, 0, s>>>((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
-                                                     idx, cnt, w, (uint16_t *)out, N, N_pad, NB, cap, sl2, full);
+        attend_bf16_kernel<64, full><<<grid, block, 0, s>>>((const uint16_t *)q, (const uint16_t *)k,
+                                                           (const uint16_t *)v, idx, cnt, w, (uint16_t *)out, N, N_pad,
+                                                           NB, cap, sl2);
     else if (dtype == kF32 && D == 64)
-        attend_f32_kernel<64><<<grid, block, 0, s>>>((const float *)q, (const float *)k, (const float *)v, idx, cnt, w,
-                                                    (float *)out, N, N_pad, NB, cap, sl2, full);
+        attend_f32_kernel<64, full><<<grid, block, 0, s>>>((const float *)q, (const float *)k, (const float *)v, idx,
+                                                          cnt, w, (float *)out, N, N_pad, NB, cap, sl2);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+hipError_t launch_attend(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad, int D,
+                         int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap, bool full,
+                         void *out, hipStream_t s)
+{
+    return full ? launch_attend_t<true>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, out, s)
+                : launch_attend_t<false>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, out, s);
 }
 
 }  // namespace aba

@@ -45,6 +45,8 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     i32, i64, f64, u64 = ctypes.c_int, ctypes.c_long, ctypes.c_double, ctypes.c_uint64
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = i32
     lib.oracle_n_blocks.argtypes = [i32, i32]
     lib.oracle_n_blocks.restype = i32
     lib.oracle_kmeans_block.argtypes = [P, i64, i32, i32, i32, i32, P, P, P]
@@ -97,6 +99,11 @@ def _items(items, B, H, NB) -> np.ndarray:
     arr = np.ascontiguousarray(np.asarray(items, dtype=np.int32).reshape(-1, 3))
     assert np.all(arr[:, 0] < B) and np.all(arr[:, 1] < H) and np.all(arr[:, 2] < NB)
     return arr
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_max_threads())
 
 
 def default_scale(head_dim: int) -> float:

@@ -34,6 +34,20 @@
 
 #define TWO32 4294967296.0
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the OpenMP loops below use (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* ---------------------------------------------------------------------- */
 /* O0 -- blocks.  Query block / key block j covers tokens                  */
 /* [blk*j, min(blk*j + blk, N)): the page splits queries into contiguous     */

@@ -56,6 +56,7 @@ def test_kmeans_matches_oracle(aba, w):
     assert ok.mean() > 0.5, f"too many near-tie blocks ({(~ok).sum()} of {ok.size})"
     scale = np.abs(o_cent).max(axis=(-1, -2), keepdims=True)
     err = (np.abs(g_cent - o_cent) / scale).max(axis=(-1, -2))
+    print(f"[{w.name}] kmeans: {ok.sum()}/{ok.size} blocks compared, centroid rel err {err[ok].max():.3g}")
     assert err[ok].max() <= CENT_RTOL, f"centroid rel err {err[ok].max():.3g}"
     assert np.array_equal(g_w[ok].view(np.uint32), o_w[ok].astype(np.float32).view(np.uint32))
 
@@ -65,6 +66,7 @@ def test_pool_matches_oracle(aba, w):
     p, (q, k, v), _, s, cent, wgt, kbar = _score_stage(aba, w, seed=102)
     ref = oracle.pool(k, w.seq_len)
     got = kbar.cpu().numpy().astype(np.float64)
+    print(f"[{w.name}] pool: rel err {np.abs(got - ref).max() / np.abs(ref).max():.3g}")
     assert np.abs(got - ref).max() <= POOL_RTOL * np.abs(ref).max()
 
 
@@ -75,6 +77,7 @@ def test_scores_match_oracle_from_gpu_parts(aba, w):
                        p.softmax_scale)
     got = s.cpu().numpy().astype(np.float64)
     rel = np.abs(got - ref) / np.abs(ref)
+    print(f"[{w.name}] scores: max rel err {rel.max():.3g}")
     assert rel.max() <= SCORE_RTOL, f"score rel err {rel.max():.3g}"
     assert np.allclose(got.sum(-1), 1.0, atol=1e-5)
 
@@ -115,6 +118,7 @@ def test_attend_matches_oracle_on_oracle_lists(aba, w):
     items = oracle.layer_items(w.batch, w.heads, w.n_blocks)
     ref = oracle.attend(q, k, v, w.seq_len, idx, cnt, wt, items=items, scale=p.softmax_scale)
     err = np.abs(gpu_rows(out, items) - ref).max()
+    print(f"[{w.name}] attend: max abs err {err:.3g} (mean |out| {np.abs(ref).mean():.3g})")
     assert err <= att_tol(w), f"max abs err {err:.3g}"
     assert torch.all(out[:, :, w.seq_len:] == 0)
 
@@ -128,6 +132,7 @@ def test_attend_full_matches_oracle(aba, w):
     items = oracle.layer_items(w.batch, w.heads, w.n_blocks)
     ref = oracle.attend_full(q, k, v, w.seq_len, items=items, scale=p.softmax_scale)
     err = np.abs(gpu_rows(out, items) - ref).max()
+    print(f"[{w.name}] attend_full: max abs err {err:.3g}")
     assert err <= att_tol(w), f"max abs err {err:.3g}"
 
 
@@ -225,10 +230,12 @@ def test_single_layer_scores_pool_and_sampling(aba, single):
     ref = oracle.score(single["cent"].cpu().double().numpy(), single["wgt"].cpu().double().numpy(),
                        single["kbar"].cpu().double().numpy(), p.softmax_scale)
     got = single["s"].cpu().double().numpy()
+    print(f"[single] scores: max rel err {(np.abs(got - ref) / ref).max():.3g}")
     assert (np.abs(got - ref) / ref).max() <= SCORE_RTOL
     o_idx, o_cnt, o_w, _ = oracle.sample(single["s"].cpu().numpy(), p.budget, 7)
     assert compare_lists(single["idx"], single["cnt"], single["wt"], o_idx, o_cnt, o_w) == 0
     density = single["cnt"].float().mean().item() / w.n_blocks
+    print(f"[single] lists bit-exact over {o_cnt.size} rows; realised density {density:.4f}")
     assert abs(density - p.budget / w.n_blocks) < 0.02
 
 
@@ -247,6 +254,7 @@ def test_single_layer_kmeans_sampled(aba, single):
         assert np.abs(g_cent[b, h, qb] - cent).max() <= CENT_RTOL * np.abs(cent).max()
         assert np.array_equal(g_w[b, h, qb].view(np.uint32), wt.astype(np.float32).view(np.uint32))
         compared += 1
+    print(f"[single] kmeans: {compared}/{len(items)} sampled blocks compared")
     assert compared >= len(items) // 2
 
 
@@ -257,6 +265,7 @@ def test_single_layer_attention_sampled(aba, single):
     idx, cnt, wt = (x.cpu().numpy() for x in (single["idx"], single["cnt"], single["wt"]))
     ref = oracle.attend(q, k, v, w.seq_len, idx, cnt, wt, items=items, scale=p.softmax_scale)
     err = np.abs(gpu_rows(single["out"], items) - ref).max()
+    print(f"[single] attend: {len(items)} query blocks, max abs err {err:.3g}")
     assert err <= att_tol(w), f"max abs err {err:.3g}"
 
 
@@ -269,4 +278,5 @@ def test_single_layer_dense_sampled(aba, single):
     items = sample_items(w, 6, seed=3)
     ref = oracle.attend_full(q, k, v, w.seq_len, items=items, scale=p.softmax_scale)
     err = np.abs(gpu_rows(dense, items) - ref).max()
+    print(f"[single] attend_full: {len(items)} query blocks, max abs err {err:.3g}")
     assert err <= att_tol(w), f"max abs err {err:.3g}"
