@@ -157,6 +157,214 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T *__restrict__ q, in
     if (tid < C) w_out[(long)row * C + tid] = (float)((double)count[tid] / (double)n);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs: both halves of a Lloyd round are small contractions and run on
+// bf16 MFMA (32x32x16).
+//   assignment  dots^T = C_split X^T.  Query rows are exact in bf16; every fp32
+//               centroid c is split into three bf16 parts hi + mid + lo (each
+//               the rounding of the remainder of the previous ones), which
+//               carry its 24-bit mantissa, so each product is exact and the
+//               dot product has fp32 accuracy.  Accumulator rows are 8p + m
+//               (part p of cluster m), so a lane holds all three parts of four
+//               clusters for its query and adds them locally; the argmin needs
+//               one exchange between the two lane halves.
+//   update      sums = onehot^T X with X^T staged once per block in LDS; new
+//               centroids are sums / counts (counts from wavefront ballots).
+// One workgroup of 4 wavefronts per (b, h, query block); wavefront w owns
+// queries [32w, 32w + 32) in the assignment and dims [32w, 32w + 32) in the
+// update.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <int D>
+__global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__restrict__ q, int N, int N_pad, int NB,
+                                                          int C, int T_iters, float *__restrict__ cent_out,
+                                                          float *__restrict__ w_out)
+{
+    constexpr int KS = D / 16;          // k-steps over the head dimension
+    constexpr int DCH = D / 8;          // 16-byte chunks per row of D bf16
+    __shared__ uint4 xt_s[D * 16];      // X^T: row d holds 128 queries (16 chunks), chunk swizzle c ^ (d & 15)
+    __shared__ uint4 cs_s[32 * DCH];    // split centroids: row 8p + m, chunk swizzle c ^ (row & (DCH - 1))
+    __shared__ float cent[kMaxClusters][D];
+    __shared__ __align__(16) uint8_t asg[kBlock];
+    __shared__ int cnt_part[4][kMaxClusters];
+    __shared__ float cnorm[kMaxClusters];
+
+    const int row = blockIdx.x;                           // (b*H + h) * NB + query block
+    const int qb = row % NB;
+    const long bh = row / NB;
+    const int n = min(kBlock, N - qb * kBlock);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, half = lane >> 5;
+    const uint16_t *src = q + (bh * N_pad + (long)qb * kBlock) * D;
+
+    // this wavefront's 32 queries as B fragments of the assignment product
+    const int my_q = wave * 32 + l32;
+    const bool qv = my_q < n;
+    bf16x8 xf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (qv) raw = *reinterpret_cast<const uint4 *>(src + (long)my_q * D + 16 * ks + 8 * half);
+        xf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+
+    // X^T into LDS: thread (c, quad) moves queries 4quad..4quad+3 of dims 8c..8c+7
+    uint2 *xt2 = reinterpret_cast<uint2 *>(xt_s);
+#pragma unroll
+    for (int pass = 0; pass < DCH / 8; ++pass) {
+        const int c = tid % DCH, quad = tid / DCH + pass * (256 / DCH);
+        uint4 rows[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int qq = 4 * quad + rr;
+            rows[rr] = make_uint4(0, 0, 0, 0);
+            if (qq < n) rows[rr] = *reinterpret_cast<const uint4 *>(src + (long)qq * D + 8 * c);
+        }
+        const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&rows[0]);
+        const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&rows[1]);
+        const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&rows[2]);
+        const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&rows[3]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                const int d = 8 * c + 2 * p + hl;
+                const uint32_t a = hl ? ((r0[p] >> 16) | (r1[p] & 0xFFFF0000u)) : ((r0[p] & 0xFFFFu) | (r1[p] << 16));
+                const uint32_t b = hl ? ((r2[p] >> 16) | (r3[p] & 0xFFFF0000u)) : ((r2[p] & 0xFFFFu) | (r3[p] << 16));
+                xt2[d * 32 + (((quad >> 1) ^ (d & 15)) << 1) + (quad & 1)] = make_uint2(a, b);
+            }
+        }
+    }
+
+    // strided initial centroids; clusters >= C stay zero and are never chosen
+    for (int i = tid; i < kMaxClusters * D; i += 256) {
+        const int m = i / D, d = i % D;
+        cent[m][d] = m < C ? bf16_bits_to_f32(src[(long)((long)m * n / C) * D + d]) : 0.f;
+    }
+    for (int i = tid; i < 8 * DCH; i += 256) cs_s[(24 + i / DCH) * DCH + i % DCH] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    // split centroids into three bf16 parts and refresh |c|^2 (threads (m, chunk))
+    auto refresh = [&]() {
+        if (tid < kMaxClusters * DCH) {
+            const int m = tid / DCH, c = tid % DCH;
+            uint32_t hi[4], mid[4], lo[4];
+            float nrm = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                float x0 = cent[m][8 * c + e], x1 = cent[m][8 * c + e + 1];
+                nrm = fmaf(x0, x0, nrm);
+                nrm = fmaf(x1, x1, nrm);
+                const uint16_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+                const float r0 = x0 - bf16_bits_to_f32(h0), r1 = x1 - bf16_bits_to_f32(h1);
+                const uint16_t m0 = f32_to_bf16_bits(r0), m1 = f32_to_bf16_bits(r1);
+                const uint16_t l0 = f32_to_bf16_bits(r0 - bf16_bits_to_f32(m0));
+                const uint16_t l1 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m1));
+                hi[e / 2] = h0 | ((uint32_t)h1 << 16);
+                mid[e / 2] = m0 | ((uint32_t)m1 << 16);
+                lo[e / 2] = l0 | ((uint32_t)l1 << 16);
+            }
+#pragma unroll
+            for (int pp = 0; pp < 3; ++pp) {
+                const int r = 8 * pp + m;
+                const uint32_t *src4 = pp == 0 ? hi : (pp == 1 ? mid : lo);
+                cs_s[r * DCH + (c ^ (r & (DCH - 1)))] = make_uint4(src4[0], src4[1], src4[2], src4[3]);
+            }
+            // reduce |c_m|^2 over the DCH consecutive lanes of cluster m
+#pragma unroll
+            for (int o = 1; o < DCH; o <<= 1) nrm += __shfl_xor(nrm, o, 64);
+            if (c == 0) cnorm[m] = nrm;
+        }
+    };
+    refresh();
+    __syncthreads();
+
+    const int rounds = T_iters > 0 ? T_iters : 1;
+    for (int it = 0; it < rounds; ++it) {
+        // ---- assignment: dots^T = C_split X^T for this wavefront's 32 queries
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint4 a = cs_s[l32 * DCH + ((2 * ks + half) ^ (l32 & (DCH - 1)))];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), xf[ks], acc, 0, 0, 0);
+        }
+        // lane half h holds clusters 4h .. 4h+3: accumulator row 8p + m is r = 4p + (m & 3)
+        float bd = INFINITY;
+        int bm = 4 * half;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = 4 * half + j;
+            const float dot = acc[j] + acc[4 + j] + acc[8 + j];
+            const float dist = m < C ? fmaf(-2.f, dot, cnorm[m]) : INFINITY;
+            if (dist < bd) {
+                bd = dist;
+                bm = m;
+            }
+        }
+        const float od = __shfl_xor(bd, 32, 64);
+        const int om = __shfl_xor(bm, 32, 64);
+        if (od < bd || (od == bd && om < bm)) {
+            bd = od;
+            bm = om;
+        }
+        if (half == 0) asg[my_q] = qv ? (uint8_t)bm : (uint8_t)0xFF;
+#pragma unroll
+        for (int m = 0; m < kMaxClusters; ++m) {
+            const unsigned long long b = __ballot(qv && half == 0 && bm == m);
+            if (lane == 0) cnt_part[wave][m] = __popcll(b);
+        }
+        __syncthreads();
+        if (T_iters == 0) break;   // weights of the initial centroids only
+
+        // ---- update: sums = onehot^T X, wavefront w owns dims [32w, 32w + 32)
+        if (wave < D / 32) {
+            floatx16 sum;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[r] = 0.f;
+            const int d = wave * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < kBlock / 16; ++ks) {
+                const uint2 ab = *reinterpret_cast<const uint2 *>(&asg[16 * ks + 8 * half]);
+                bf16x8 oh;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t byte = ((e < 4 ? ab.x : ab.y) >> (8 * (e & 3))) & 0xFFu;
+                    oh[e] = (byte == (uint32_t)l32) ? (__bf16)1.0f : (__bf16)0.0f;
+                }
+                const uint4 b = xt_s[d * 16 + ((2 * ks + half) ^ (d & 15))];
+                sum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oh, __builtin_bit_cast(bf16x8, b), sum, 0, 0, 0);
+            }
+            // lane holds the sums of clusters 4half .. 4half+3 for dim d
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * half + r;
+                const int cn = cnt_part[0][m] + cnt_part[1][m] + cnt_part[2][m] + cnt_part[3][m];
+                if (m < C && cn > 0) cent[m][d] = sum[r] / (float)cn;
+            }
+        }
+        __syncthreads();
+        refresh();
+        __syncthreads();
+    }
+
+    float *co = cent_out + (long)row * C * D;
+    for (int i = tid; i < C * D; i += 256) co[i] = cent[i / D][i % D];
+    if (tid < C) {
+        const int cn = cnt_part[0][tid] + cnt_part[1][tid] + cnt_part[2][tid] + cnt_part[3][tid];
+        w_out[(long)row * C + tid] = (float)((double)cn / (double)n);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_kmeans(const void *q, int dtype, int B, int H, int N, int N_pad, int D, int NB, int C, int T,
@@ -164,9 +372,9 @@ hipError_t launch_kmeans(const void *q, int dtype, int B, int H, int N, int N_pa
 {
     const dim3 grid((unsigned)((long)B * H * NB)), block(256);
     if (dtype == kBF16 && D == 128)
-        kmeans_kernel<uint16_t, 128><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight);
+        kmeans_mfma_kernel<128><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight);
     else if (dtype == kBF16 && D == 64)
-        kmeans_kernel<uint16_t, 64><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight);
+        kmeans_mfma_kernel<64><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight);
     else if (dtype == kF32 && D == 64)
         kmeans_kernel<float, 64><<<grid, block, 0, s>>>((const float *)q, N, N_pad, NB, C, T, cent, weight);
     else

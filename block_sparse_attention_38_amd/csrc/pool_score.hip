@@ -8,8 +8,8 @@
 //        HBM with 16-byte loads and writes the fp32 mean of its valid rows.
 //        HBM-bound: 128 * D * elem bytes read per block.
 // score: one workgroup per (b, h, query block).  Logits l_mj = s * c_m . kbar_j
-//        for all key blocks are kept in LDS, then a per-centroid softmax over j
-//        and the weighted sum over centroids give one row of scores.
+//        for all key blocks stay in registers, then a per-centroid softmax over
+//        j and the weighted sum over centroids give one row of scores.
 #include "aba_internal.h"
 
 namespace aba {
@@ -53,73 +53,100 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ k, int 
 }
 
 // ---------------------------------------------------------------------------
-// Block scores
+// Block scores.  Thread j owns key blocks j, j + 256, ...: it streams its pooled
+// key rows and takes the query block's centroids as wavefront-uniform values
+// (scalar loads), so the 8 x NB x D contraction is plain FMAs with no LDS
+// traffic.  Per-centroid max and normaliser over the key blocks are two
+// workgroup reductions; the logits never leave registers.
 // ---------------------------------------------------------------------------
-constexpr int kTileRows = 32;
-
 template <int D>
 __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ cent, const float *__restrict__ weight,
                                                     const float *__restrict__ kbar, int NB, int C, float scale,
                                                     float *__restrict__ scores)
 {
-    __shared__ float4 c_s[kMaxClusters][D / 4];
-    __shared__ float4 k_s[kTileRows][D / 4 + 1];   // +1 float4 per row: conflict-free column reads
-    __shared__ float logit[kMaxClusters][kMaxBlocks];
-    __shared__ float w_s[kMaxClusters], mx_s[kMaxClusters], iz_s[kMaxClusters];
+    constexpr int JPT = kMaxBlocks / 256;     // key blocks per thread at most
+    __shared__ float red[2][4][kMaxClusters];
 
-    const int row = blockIdx.x;                    // (b*H + h) * NB + query block
+    const int row = blockIdx.x;               // (b*H + h) * NB + query block
     const long bh = row / NB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float *c = cent + (long)row * C * D;
+    const float *kb = kbar + bh * NB * D;
 
-    for (int i = tid; i < C * D / 4; i += 256)
-        c_s[i / (D / 4)][i % (D / 4)] = reinterpret_cast<const float4 *>(cent + (long)row * C * D)[i];
-    if (tid < C) w_s[tid] = weight[(long)row * C + tid];
-
-    const float4 *kb = reinterpret_cast<const float4 *>(kbar + bh * NB * D);
-    const int jl = tid % kTileRows, m = tid / kTileRows;     // 8 clusters x 32 key blocks per pass
-    for (int j0 = 0; j0 < NB; j0 += kTileRows) {
-        __syncthreads();
-        for (int i = tid; i < kTileRows * D / 4; i += 256) {
-            const int r = i / (D / 4), cc = i % (D / 4);
-            k_s[r][cc] = (j0 + r < NB) ? kb[(long)(j0 + r) * (D / 4) + cc] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        __syncthreads();
-        if (m < C && j0 + jl < NB) {
-            float dot = 0.f;
-#pragma unroll 8
-            for (int cc = 0; cc < D / 4; ++cc) {
-                const float4 a = c_s[m][cc], b = k_s[jl][cc];
-                dot = fmaf(a.x, b.x, dot);
-                dot = fmaf(a.y, b.y, dot);
-                dot = fmaf(a.z, b.z, dot);
-                dot = fmaf(a.w, b.w, dot);
+    float lg[JPT][kMaxClusters];
+#pragma unroll
+    for (int t = 0; t < JPT; ++t) {
+        const int j = tid + 256 * t;
+        float acc[kMaxClusters];
+#pragma unroll
+        for (int m = 0; m < kMaxClusters; ++m) acc[m] = 0.f;
+        if (j < NB) {
+            const float4 *kr = reinterpret_cast<const float4 *>(kb + (long)j * D);
+#pragma unroll 4
+            for (int d4 = 0; d4 < D / 4; ++d4) {
+                const float4 x = kr[d4];
+#pragma unroll
+                for (int m = 0; m < kMaxClusters; ++m) {
+                    if (m < C) {
+                        const float4 cc = reinterpret_cast<const float4 *>(c + m * D)[d4];
+                        float a = acc[m];
+                        a = fmaf(cc.x, x.x, a);
+                        a = fmaf(cc.y, x.y, a);
+                        a = fmaf(cc.z, x.z, a);
+                        a = fmaf(cc.w, x.w, a);
+                        acc[m] = a;
+                    }
+                }
             }
-            logit[m][j0 + jl] = scale * dot;
         }
+#pragma unroll
+        for (int m = 0; m < kMaxClusters; ++m) lg[t][m] = (j < NB && m < C) ? scale * acc[m] : -INFINITY;
     }
-    __syncthreads();
 
-    // Per-centroid softmax statistics over the key blocks: wave w handles
-    // clusters w and w + 4.
-    for (int mm = wave; mm < C; mm += 4) {
-        float mx = -INFINITY;
-        for (int j = lane; j < NB; j += 64) mx = fmaxf(mx, logit[mm][j]);
-        mx = wave_max(mx);
-        float z = 0.f;
-        for (int j = lane; j < NB; j += 64) z += __expf(logit[mm][j] - mx);
-        z = wave_sum(z);
-        if (lane == 0) {
-            mx_s[mm] = mx;
-            iz_s[mm] = 1.f / z;
-        }
+    // per-centroid max over key blocks
+    float mx[kMaxClusters];
+#pragma unroll
+    for (int m = 0; m < kMaxClusters; ++m) {
+        float v = lg[0][m];
+#pragma unroll
+        for (int t = 1; t < JPT; ++t) v = fmaxf(v, lg[t][m]);
+        v = wave_max(v);
+        if (lane == 0) red[0][wave][m] = v;
     }
     __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kMaxClusters; ++m)
+        mx[m] = fmaxf(fmaxf(red[0][0][m], red[0][1][m]), fmaxf(red[0][2][m], red[0][3][m]));
+
+    // exponentials and per-centroid normalisers
+#pragma unroll
+    for (int m = 0; m < kMaxClusters; ++m) {
+        float v = 0.f;
+#pragma unroll
+        for (int t = 0; t < JPT; ++t) {
+            lg[t][m] = (m < C) ? __expf(lg[t][m] - mx[m]) : 0.f;
+            v += lg[t][m];
+        }
+        v = wave_sum(v);
+        if (lane == 0) red[1][wave][m] = v;
+    }
+    __syncthreads();
+    float coef[kMaxClusters];
+#pragma unroll
+    for (int m = 0; m < kMaxClusters; ++m)
+        coef[m] = (m < C) ? weight[(long)row * C + m] / (red[1][0][m] + red[1][1][m] + red[1][2][m] + red[1][3][m])
+                          : 0.f;
 
     float *out = scores + (long)row * NB;
-    for (int j = tid; j < NB; j += 256) {
-        float s = 0.f;
-        for (int mm = 0; mm < C; ++mm) s += w_s[mm] * (__expf(logit[mm][j] - mx_s[mm]) * iz_s[mm]);
-        out[j] = s;
+#pragma unroll
+    for (int t = 0; t < JPT; ++t) {
+        const int j = tid + 256 * t;
+        if (j < NB) {
+            float s = 0.f;
+#pragma unroll
+            for (int m = 0; m < kMaxClusters; ++m) s = fmaf(coef[m], lg[t][m], s);
+            out[j] = s;
+        }
     }
 }
 
