@@ -169,7 +169,12 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T *__restrict__ q, in
 //               clusters for its query and adds them locally; the argmin needs
 //               one exchange between the two lane halves.
 //   update      sums = onehot^T X with X^T staged once per block in LDS; new
-//               centroids are sums / counts (counts from wavefront ballots).
+//               centroids are sums / counts (counts from wavefront ballots);
+//               the lanes that form a centroid element also write its three
+//               bf16 parts and its share of |c|^2, so a round has two barriers.
+// A round whose assignment equals the previous round's leaves every later
+// round unchanged bit for bit (same rows, same sums), so the loop stops there:
+// the result is exactly that of all T rounds.
 // One workgroup of 4 wavefronts per (b, h, query block); wavefront w owns
 // queries [32w, 32w + 32) in the assignment and dims [32w, 32w + 32) in the
 // update.
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
     __shared__ float cent[kMaxClusters][D];
     __shared__ __align__(16) uint8_t asg[kBlock];
     __shared__ int cnt_part[4][kMaxClusters];
-    __shared__ float cnorm[kMaxClusters];
+    __shared__ float cn_part[4][kMaxClusters];   // per-wavefront shares of |c_m|^2
 
     const int row = blockIdx.x;                           // (b*H + h) * NB + query block
     const int qb = row % NB;
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
     // strided initial centroids; clusters >= C stay zero and are never chosen
     for (int i = tid; i < kMaxClusters * D; i += 256) {
         const int m = i / D, d = i % D;
-        cent[m][d] = m < C ? bf16_bits_to_f32(src[(long)((long)m * n / C) * D + d]) : 0.f;
+        cent[m][d] = m < C ? bf16_bits_to_f32(src[(m * n / C) * D + d]) : 0.f;
     }
     for (int i = tid; i < 8 * DCH; i += 256) cs_s[(24 + i / DCH) * DCH + i % DCH] = make_uint4(0, 0, 0, 0);
     __syncthreads();
@@ -281,13 +286,18 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
             // reduce |c_m|^2 over the DCH consecutive lanes of cluster m
 #pragma unroll
             for (int o = 1; o < DCH; o <<= 1) nrm += __shfl_xor(nrm, o, 64);
-            if (c == 0) cnorm[m] = nrm;
+            if (c == 0) {
+                cn_part[0][m] = nrm;
+                cn_part[1][m] = cn_part[2][m] = cn_part[3][m] = 0.f;
+            }
         }
     };
     refresh();
     __syncthreads();
+    uint16_t *cs16 = reinterpret_cast<uint16_t *>(cs_s);
 
     const int rounds = T_iters > 0 ? T_iters : 1;
+    int prev = -1;
     for (int it = 0; it < rounds; ++it) {
         // ---- assignment: dots^T = C_split X^T for this wavefront's 32 queries
         floatx16 acc;
@@ -305,7 +315,8 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
         for (int j = 0; j < 4; ++j) {
             const int m = 4 * half + j;
             const float dot = acc[j] + acc[4 + j] + acc[8 + j];
-            const float dist = m < C ? fmaf(-2.f, dot, cnorm[m]) : INFINITY;
+            const float cn2 = cn_part[0][m] + cn_part[1][m] + cn_part[2][m] + cn_part[3][m];
+            const float dist = m < C ? fmaf(-2.f, dot, cn2) : INFINITY;
             if (dist < bd) {
                 bd = dist;
                 bm = m;
@@ -323,8 +334,10 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
             const unsigned long long b = __ballot(qv && half == 0 && bm == m);
             if (lane == 0) cnt_part[wave][m] = __popcll(b);
         }
-        __syncthreads();
-        if (T_iters == 0) break;   // weights of the initial centroids only
+        const int changed = (half == 0 && qv && bm != prev) ? 1 : 0;
+        prev = bm;
+        const int any_changed = __syncthreads_or(changed);
+        if (T_iters == 0 || !any_changed) break;   // initial-centroid weights, or converged
 
         // ---- update: sums = onehot^T X, wavefront w owns dims [32w, 32w + 32)
         if (wave < D / 32) {
@@ -345,15 +358,38 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
                 sum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oh, __builtin_bit_cast(bf16x8, b), sum, 0, 0, 0);
             }
             // lane holds the sums of clusters 4half .. 4half+3 for dim d
+            float sq[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = 4 * half + r;
                 const int cn = cnt_part[0][m] + cnt_part[1][m] + cnt_part[2][m] + cnt_part[3][m];
-                if (m < C && cn > 0) cent[m][d] = sum[r] / (float)cn;
+                float cv = cent[m][d];
+                if (m < C && cn > 0) {
+                    cv = sum[r] / (float)cn;
+                    cent[m][d] = cv;
+                    const uint16_t hb = f32_to_bf16_bits(cv);
+                    const float r1 = cv - bf16_bits_to_f32(hb);
+                    const uint16_t mb = f32_to_bf16_bits(r1);
+                    const uint16_t lb = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mb));
+#pragma unroll
+                    for (int pp = 0; pp < 3; ++pp) {
+                        const int rr = 8 * pp + m;
+                        cs16[(rr * DCH + ((d >> 3) ^ (rr & (DCH - 1)))) * 8 + (d & 7)] = pp == 0 ? hb : (pp == 1 ? mb : lb);
+                    }
+                }
+                sq[r] = cv * cv;
+            }
+            // this wavefront's share of |c_m|^2: sum over its 32 dims (lanes of one half)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) sq[r] += __shfl_xor(sq[r], o, 64);
+            }
+            if (l32 == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) cn_part[wave][4 * half + r] = sq[r];
             }
         }
-        __syncthreads();
-        refresh();
         __syncthreads();
     }
 

@@ -54,9 +54,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ k, int 
 
 // ---------------------------------------------------------------------------
 // Block scores.  Thread j owns key blocks j, j + 256, ...: it streams its pooled
-// key rows and takes the query block's centroids as wavefront-uniform values
-// (scalar loads), so the 8 x NB x D contraction is plain FMAs with no LDS
-// traffic.  Per-centroid max and normaliser over the key blocks are two
+// key rows from L1/L2 and reads the query block's centroids from LDS as
+// broadcasts (every lane the same address), so the 8 x NB x D contraction is
+// plain FMAs.  Per-centroid max and normaliser over the key blocks are two
 // workgroup reductions; the logits never leave registers.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -65,13 +65,19 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ ce
                                                     float *__restrict__ scores)
 {
     constexpr int JPT = kMaxBlocks / 256;     // key blocks per thread at most
+    __shared__ float4 c_s[kMaxClusters][D / 4];
     __shared__ float red[2][4][kMaxClusters];
 
     const int row = blockIdx.x;               // (b*H + h) * NB + query block
     const long bh = row / NB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float *c = cent + (long)row * C * D;
     const float *kb = kbar + bh * NB * D;
+
+    // centroids of this query block; rows >= C are zero (their logits are dropped)
+    const float4 *c4 = reinterpret_cast<const float4 *>(cent + (long)row * C * D);
+    for (int i = tid; i < kMaxClusters * D / 4; i += 256)
+        c_s[i / (D / 4)][i % (D / 4)] = (i / (D / 4) < C) ? c4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
 
     float lg[JPT][kMaxClusters];
 #pragma unroll
@@ -87,15 +93,13 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ ce
                 const float4 x = kr[d4];
 #pragma unroll
                 for (int m = 0; m < kMaxClusters; ++m) {
-                    if (m < C) {
-                        const float4 cc = reinterpret_cast<const float4 *>(c + m * D)[d4];
-                        float a = acc[m];
-                        a = fmaf(cc.x, x.x, a);
-                        a = fmaf(cc.y, x.y, a);
-                        a = fmaf(cc.z, x.z, a);
-                        a = fmaf(cc.w, x.w, a);
-                        acc[m] = a;
-                    }
+                    const float4 cc = c_s[m][d4];
+                    float a = acc[m];
+                    a = fmaf(cc.x, x.x, a);
+                    a = fmaf(cc.y, x.y, a);
+                    a = fmaf(cc.z, x.z, a);
+                    a = fmaf(cc.w, x.w, a);
+                    acc[m] = a;
                 }
             }
         }
