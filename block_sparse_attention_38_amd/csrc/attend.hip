@@ -22,9 +22,10 @@
 //   O^T += V^T P^T   32x32x16 bf16 MFMA, P^T straight from the S^T accumulators
 // Computing the transposed products makes every lane own one query column, so
 // row statistics need a single cross-half exchange and the rescale of O is a
-// per-lane scalar multiply.  K sits in LDS row-major with a 16-byte XOR swizzle;
-// V is transposed on its way into LDS (key-contiguous, 8-byte XOR swizzle) so
-// that the PV operand is two 8-byte reads.
+// per-lane scalar multiply.  K sits in LDS row-major; V is transposed on its
+// way into LDS (key-contiguous) so that the PV operand is two 8-byte reads.
+// Both use padded rows, which keeps the reads free of bank conflicts and every
+// LDS address a per-lane base plus an immediate offset.
 //
 // fp32 path: a plain VALU kernel (pairs of lanes per query row) for fp32
 // inputs with head_dim 64.
@@ -49,78 +50,84 @@ constexpr int kSub = 64;
 // by more than this many powers of two (exp2 values then stay below 2^8).
 constexpr float kRescaleSlack = 8.f;
 
-// K sub-tile: 64 rows x D bf16 in 16-byte chunks, chunk c of row r stored at
-// r * (D/8) + (c ^ swz(r)); the swizzle spreads the 16 rows that one
-// 16-lane phase of a 128-bit read touches over distinct banks.
-template <int D> __device__ __forceinline__ int k_slot(int r, int c)
-{
-    constexpr int kChunks = D / 8;
-    if constexpr (kChunks == 16)
-        return r * 16 + (c ^ (r & 15));
-    else
-        return r * 8 + (c ^ ((r >> 1) & 7));   // 128-byte rows: row parity already splits the banks
-}
-// V^T sub-tile: D rows (dims) x 64 keys in 8-byte slots of 4 keys (16 slots,
-// 128 bytes per row); slot s of row d stored at d * 16 + (s ^ ((d >> 1) & 15)),
-// so that the 32 rows one 8-byte read phase touches hit distinct banks.
-__device__ __forceinline__ int vt_slot(int d, int s) { return d * 16 + (s ^ ((d >> 1) & 15)); }
+// LDS layout of one stage.  Rows are padded instead of swizzled, so every LDS
+// address is a per-lane base plus a compile-time offset:
+//   K    64 rows x D bf16, row pitch D*2 + 16 bytes: the 16 rows one 16-lane
+//        phase of a 128-bit read touches start 4 banks apart;
+//   V^T  D rows x 64 keys, row pitch 136 bytes: the 32 rows one phase of a
+//        64-bit read touches cover all 64 banks.
+template <int D> struct Lds {
+    static constexpr int kPitch = D * 2 + 16;
+    static constexpr int vPitch = kSub * 2 + 8;
+    static constexpr int kBytes = kSub * kPitch;
+    static constexpr int vBytes = D * vPitch;
+    static constexpr int stage = kBytes + vBytes;
+};
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 // Global -> register staging of one 64-key sub-tile (each thread holds its
 // share until it is written to LDS after the current sub-tile is computed).
+// Thread (c, r0) moves 16-byte chunk c of K rows r0 + 16i and of V rows
+// 4*r0' .. 4*r0'+3 (keys of one 8-byte V^T slot).
 template <int D> struct Stage {
     static constexpr int kChunks = D / 8;
-    static constexpr int kKLoads = kSub * kChunks / 256;       // 16-byte K chunks per thread
-    static constexpr bool kVAll = (kSub / 4) * kChunks >= 256; // every thread moves one V quad
+    static constexpr int kRowsPerPass = 256 / kChunks;
+    static constexpr int kKLoads = kSub / kRowsPerPass;       // 16-byte K chunks per thread
+    static constexpr bool kVAll = (kSub / 4) >= kRowsPerPass; // every thread moves one V quad
     uint4 k[kKLoads];
     uint4 v[4];
 };
 
+// full: every key of the sub-tile is valid (no bounds checks); otherwise rows
+// >= N and the whole sub-tile when !active read as zero.
 template <int D>
-__device__ __forceinline__ void stage_load(Stage<D> &st, const uint16_t *kh, const uint16_t *vh, int key0, int N,
-                                           int tid, bool active)
+__device__ __forceinline__ void stage_load(Stage<D> &st, const uint16_t *kb, const uint16_t *vb, int valid, bool full,
+                                           int tid)
 {
-    constexpr int kChunks = D / 8;
-    const int c = tid % kChunks;
+    constexpr int kChunks = D / 8, RP = Stage<D>::kRowsPerPass;
+    const int c = tid % kChunks, r0 = tid / kChunks;
+    const uint16_t *kp = kb + r0 * D + 8 * c;
+    const uint16_t *vp = vb + 4 * r0 * D + 8 * c;
+    const bool vq = Stage<D>::kVAll || r0 < kSub / 4;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < Stage<D>::kKLoads; ++i) {
-        const int r = tid / kChunks + i * (256 / kChunks);
-        st.k[i] = make_uint4(0, 0, 0, 0);
-        if (active && key0 + r < N) st.k[i] = *reinterpret_cast<const uint4 *>(kh + (long)(key0 + r) * D + 8 * c);
-    }
-    const int quad = tid / kChunks;   // keys 4*quad .. 4*quad+3
+        for (int i = 0; i < Stage<D>::kKLoads; ++i) st.k[i] = *reinterpret_cast<const uint4 *>(kp + i * RP * D);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int key = key0 + 4 * quad + rr;
-        st.v[rr] = make_uint4(0, 0, 0, 0);
-        if (active && quad < kSub / 4 && key < N)
-            st.v[rr] = *reinterpret_cast<const uint4 *>(vh + (long)key * D + 8 * c);
+        for (int rr = 0; rr < 4; ++rr)
+            st.v[rr] = vq ? *reinterpret_cast<const uint4 *>(vp + rr * D) : make_uint4(0, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < Stage<D>::kKLoads; ++i)
+            st.k[i] = (r0 + i * RP < valid) ? *reinterpret_cast<const uint4 *>(kp + i * RP * D) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            st.v[rr] = (vq && 4 * r0 + rr < valid) ? *reinterpret_cast<const uint4 *>(vp + rr * D) : make_uint4(0, 0, 0, 0);
     }
 }
 
 template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D> &st, uint4 *k_s, uint2 *vt_s, int tid)
+__device__ __forceinline__ void stage_store(const Stage<D> &st, char *stage_base, int tid)
 {
-    constexpr int kChunks = D / 8;
-    const int c = tid % kChunks;
+    using L = Lds<D>;
+    constexpr int kChunks = D / 8, RP = Stage<D>::kRowsPerPass;
+    const int c = tid % kChunks, r0 = tid / kChunks;
+    char *kbase = stage_base + r0 * L::kPitch + 16 * c;
 #pragma unroll
-    for (int i = 0; i < Stage<D>::kKLoads; ++i) {
-        const int r = tid / kChunks + i * (256 / kChunks);
-        k_s[k_slot<D>(r, c)] = st.k[i];
-    }
-    const int quad = tid / kChunks;
-    if (Stage<D>::kVAll || quad < kSub / 4) {
-        const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&st.v[0]);
-        const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&st.v[1]);
-        const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&st.v[2]);
-        const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&st.v[3]);
+    for (int i = 0; i < Stage<D>::kKLoads; ++i) *reinterpret_cast<uint4 *>(kbase + i * RP * L::kPitch) = st.k[i];
+    if (Stage<D>::kVAll || r0 < kSub / 4) {
+        // V^T rows 8c .. 8c+7, slot r0 (keys 4r0 .. 4r0+3)
+        char *vbase = stage_base + L::kBytes + 8 * c * L::vPitch + 8 * r0;
+        const uint32_t *a = reinterpret_cast<const uint32_t *>(&st.v[0]);
+        const uint32_t *b = reinterpret_cast<const uint32_t *>(&st.v[1]);
+        const uint32_t *e = reinterpret_cast<const uint32_t *>(&st.v[2]);
+        const uint32_t *f = reinterpret_cast<const uint32_t *>(&st.v[3]);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int d = 8 * c + 2 * p;
-            vt_s[vt_slot(d, quad)] = make_uint2(pack_lo(r0[p], r1[p]), pack_lo(r2[p], r3[p]));
-            vt_s[vt_slot(d + 1, quad)] = make_uint2(pack_hi(r0[p], r1[p]), pack_hi(r2[p], r3[p]));
+            *reinterpret_cast<uint2 *>(vbase + (2 * p) * L::vPitch) = make_uint2(perm_lo(a[p], b[p]), perm_lo(e[p], f[p]));
+            *reinterpret_cast<uint2 *>(vbase + (2 * p + 1) * L::vPitch) =
+                make_uint2(perm_hi(a[p], b[p]), perm_hi(e[p], f[p]));
         }
     }
 }
@@ -141,18 +148,26 @@ __device__ __forceinline__ Entry list_entry(const int32_t *lrow, const float *wr
     return Entry{j, __log2f(wj)};
 }
 
+template <int D>
+__device__ __forceinline__ void load_subtile(Stage<D> &st, const uint16_t *kh, const uint16_t *vh, Entry en, int half_idx,
+                                             int N, int tid)
+{
+    const int key0 = en.j * kBlock + kSub * half_idx;
+    const int valid = (en.j < 0) ? 0 : min(kSub, N - key0);
+    stage_load<D>(st, kh + (long)key0 * D, vh + (long)key0 * D, valid, valid == kSub, tid);
+}
+
 template <int D, bool full>
 __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
     uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap, float scale_log2)
 {
-    constexpr int kChunks = D / 8;     // 16-byte chunks per K row
+    using L = Lds<D>;
     constexpr int KS = D / 16;         // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;         // 32-row tiles of O^T
     constexpr int KT = kSub / 32;      // 32-key tiles per sub-tile
-    __shared__ uint4 k_s[2][kSub * kChunks];
-    __shared__ uint2 vt_s[2][D * kSub / 4];
+    __shared__ __align__(16) char lds[2 * L::stage];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
@@ -180,6 +195,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
+    const floatx16 zero16 = {};
 
     int n_list = NB;
     const int32_t *lrow = nullptr;
@@ -192,22 +208,26 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     }
     const int n_sub = 2 * n_list;   // sub-tile u = half (u & 1) of list entry u >> 1
 
+    // per-lane LDS read bases (constant offsets are added per instruction)
+    const int k_rd = l32 * L::kPitch + 16 * half;
+    const int v_rd = L::kBytes + l32 * L::vPitch + 8 * half;
+
     Stage<D> st;
     Entry cur{-1, 0.f};
     if (n_sub > 0) {
         cur = list_entry<full>(lrow, wrow, 0, NB);
-        stage_load<D>(st, kh, vh, cur.j * kBlock, N, tid, cur.j >= 0);
-        stage_store<D>(st, k_s[0], vt_s[0], tid);
+        load_subtile<D>(st, kh, vh, cur, 0, N, tid);
+        stage_store<D>(st, lds, tid);
     }
     __syncthreads();
 
     for (int u = 0; u < n_sub; ++u) {
-        const int buf = u & 1;
+        char *cur_stage = lds + (u & 1) * L::stage;
         // prefetch the next sub-tile into registers; it lands while this one is computed
         Entry nxt = cur;
         if (u + 1 < n_sub) {
-            if ((u & 1) == 1) nxt = list_entry<full>(lrow, wrow, (u + 1) >> 1, NB);
-            stage_load<D>(st, kh, vh, nxt.j * kBlock + kSub * ((u + 1) & 1), N, tid, nxt.j >= 0);
+            if (u & 1) nxt = list_entry<full>(lrow, wrow, (u + 1) >> 1, NB);
+            load_subtile<D>(st, kh, vh, nxt, (u + 1) & 1, N, tid);
         }
 
         const int key0 = cur.j * kBlock + kSub * (u & 1);
@@ -217,13 +237,11 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
             floatx16 s[KT];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-                const int krow = kt * 32 + l32;
+                const char *kr = cur_stage + k_rd + kt * 32 * L::kPitch;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const uint4 a = k_s[buf][k_slot<D>(krow, 2 * ks + half)];
-                    s[kt] = mfma32(__builtin_bit_cast(bf16x8, a), qf[ks], s[kt]);
+                    const uint4 a = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
+                    s[kt] = mfma32(__builtin_bit_cast(bf16x8, a), qf[ks], ks == 0 ? zero16 : s[kt]);
                 }
             }
             if (key0 + kSub > N) {   // ragged end of the sequence: mask padding keys
@@ -266,24 +284,24 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
 
             // O^T += V^T P^T.  MFMA (kt, sub) contracts the 16 keys held in
             // accumulator rows [8sub, 8sub+8) of tile kt: for lane half h,
-            // element e is key 32kt + 16sub + 8(e/4) + 4h + e%4.
+            // element e is key 32kt + 16sub + 8(e/4) + 4h + e%4, i.e. V^T slots
+            // 8kt + 4sub + h and 8kt + 4sub + h + 2.
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int d = dt * 32 + l32;
+                const char *vr = cur_stage + v_rd + dt * 32 * L::vPitch;
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                     for (int sub = 0; sub < 2; ++sub) {
-                        const int slot = 8 * kt + 4 * sub + half;
-                        const uint2 a0 = vt_s[buf][vt_slot(d, slot)];
-                        const uint2 a1 = vt_s[buf][vt_slot(d, slot + 2)];
+                        const uint2 a0 = *reinterpret_cast<const uint2 *>(vr + 8 * (8 * kt + 4 * sub));
+                        const uint2 a1 = *reinterpret_cast<const uint2 *>(vr + 8 * (8 * kt + 4 * sub + 2));
                         const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
                         o[dt] = mfma32(__builtin_bit_cast(bf16x8, a), pb[kt][sub], o[dt]);
                     }
             }
         }
 
-        if (u + 1 < n_sub) stage_store<D>(st, k_s[buf ^ 1], vt_s[buf ^ 1], tid);
+        if (u + 1 < n_sub) stage_store<D>(st, lds + ((u + 1) & 1) * L::stage, tid);
         cur = nxt;
         __syncthreads();
     }
