@@ -49,86 +49,72 @@ constexpr int kSub = 64;
 // Lazy rescaling: the running max only moves when a sub-tile's max exceeds it
 // by more than this many powers of two (exp2 values then stay below 2^8).
 constexpr float kRescaleSlack = 8.f;
+// Two wavefronts per workgroup, 64 query rows each (two 32-row MFMA tiles).
+constexpr int kThreads = 128;
+constexpr int QT = 2;
 
-// LDS layout of one stage.  Rows are padded instead of swizzled, so every LDS
-// address is a per-lane base plus a compile-time offset:
-//   K    64 rows x D bf16, row pitch D*2 + 16 bytes: the 16 rows one 16-lane
-//        phase of a 128-bit read touches start 4 banks apart;
-//   V^T  D rows x 64 keys, row pitch 136 bytes: the 32 rows one phase of a
-//        64-bit read touches cover all 64 banks.
+// LDS layout of one stage: K and V sub-tiles of 64 rows x D bf16, unpadded
+// (one direct global->LDS load fills four whole rows), with XOR swizzles of the
+// 16-byte chunks chosen per tensor:
+//   K  chunk c of row r at c ^ (r % 16): the 16 rows one 16-lane phase of a
+//      128-bit read touches hit 16 different chunks;
+//   V  chunk c of row r at c ^ 4(r % 4): the four rows x 64 bytes that 32 lanes
+//      of a transposing 64-bit read touch fall on distinct banks.
 template <int D> struct Lds {
-    static constexpr int kPitch = D * 2 + 16;
-    static constexpr int vPitch = kSub * 2 + 8;
-    static constexpr int kBytes = kSub * kPitch;
-    static constexpr int vBytes = D * vPitch;
+    static constexpr int pitch = D * 2;
+    static constexpr int chunks = D / 8;
+    static constexpr int kBytes = kSub * pitch;
+    static constexpr int vBytes = kSub * pitch;
     static constexpr int stage = kBytes + vBytes;
 };
+template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Lds<D>::chunks - 1); }
+template <int D> __device__ __forceinline__ int v_swz(int r) { return (4 * (r & 3)) & (Lds<D>::chunks - 1); }
 
-__device__ __forceinline__ uint32_t perm_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t perm_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void glb_void;
 
-// Global -> register staging of one 64-key sub-tile (each thread holds its
-// share until it is written to LDS after the current sub-tile is computed).
-// Thread (c, r0) moves 16-byte chunk c of K rows r0 + 16i and of V rows
-// 4*r0' .. 4*r0'+3 (keys of one 8-byte V^T slot).
-template <int D> struct Stage {
-    static constexpr int kChunks = D / 8;
-    static constexpr int kRowsPerPass = 256 / kChunks;
-    static constexpr int kKLoads = kSub / kRowsPerPass;       // 16-byte K chunks per thread
-    static constexpr bool kVAll = (kSub / 4) >= kRowsPerPass; // every thread moves one V quad
-    uint4 k[kKLoads];
-    uint4 v[4];
-};
-
-// full: every key of the sub-tile is valid (no bounds checks); otherwise rows
-// >= N and the whole sub-tile when !active read as zero.
-template <int D>
-__device__ __forceinline__ void stage_load(Stage<D> &st, const uint16_t *kb, const uint16_t *vb, int valid, bool full,
-                                           int tid)
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte chunks addressed by
+// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4: if lane L addresses row kb + L/4,
+// columns c0 + 4(L % 4) .. +3 of a row-major 16-bit matrix, lane i receives
+// column c0 + i at rows kb .. kb+3.
+__device__ __forceinline__ uint2 lds_read_tr16(const char *p)
 {
-    constexpr int kChunks = D / 8, RP = Stage<D>::kRowsPerPass;
-    const int c = tid % kChunks, r0 = tid / kChunks;
-    const uint16_t *kp = kb + r0 * D + 8 * c;
-    const uint16_t *vp = vb + 4 * r0 * D + 8 * c;
-    const bool vq = Stage<D>::kVAll || r0 < kSub / 4;
-    if (full) {
-#pragma unroll
-        for (int i = 0; i < Stage<D>::kKLoads; ++i) st.k[i] = *reinterpret_cast<const uint4 *>(kp + i * RP * D);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            st.v[rr] = vq ? *reinterpret_cast<const uint4 *>(vp + rr * D) : make_uint4(0, 0, 0, 0);
-    } else {
-#pragma unroll
-        for (int i = 0; i < Stage<D>::kKLoads; ++i)
-            st.k[i] = (r0 + i * RP < valid) ? *reinterpret_cast<const uint4 *>(kp + i * RP * D) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            st.v[rr] = (vq && 4 * r0 + rr < valid) ? *reinterpret_cast<const uint4 *>(vp + rr * D) : make_uint4(0, 0, 0, 0);
-    }
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p)));
 }
 
+// Direct global -> LDS copy of 16 bytes per lane; lane L's bytes land at
+// dst + 16 L (dst is wavefront-uniform).
+__device__ __forceinline__ void load_lds16(const uint16_t *src, char *dst)
+{
+    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)dst, 16, 0, 0);
+}
+
+// Issue the direct loads of one 64-key sub-tile of K and V (rows key0 ..
+// key0 + 63) into an LDS stage.  Wavefront w fills rows [32w, 32w + 32) of
+// both tensors: eight loads of four rows each per tensor.  Rows past the last
+// valid one are read from that row instead (finite values; those keys are
+// masked and their probabilities are zero).  Needs a vmcnt wait and a barrier
+// before the stage is read.
 template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D> &st, char *stage_base, int tid)
+__device__ __forceinline__ void stage_issue(const uint16_t *kh, const uint16_t *vh, int key0, int valid, char *stage,
+                                            int wave, int lane)
 {
     using L = Lds<D>;
-    constexpr int kChunks = D / 8, RP = Stage<D>::kRowsPerPass;
-    const int c = tid % kChunks, r0 = tid / kChunks;
-    char *kbase = stage_base + r0 * L::kPitch + 16 * c;
+    constexpr int rows_per_load = 1024 / L::pitch;   // 4 (D=128) or 8 (D=64)
+    constexpr int loads = 32 / rows_per_load;
+    const int lr = lane / L::chunks, pc = lane % L::chunks;   // row within the load, physical chunk
 #pragma unroll
-    for (int i = 0; i < Stage<D>::kKLoads; ++i) *reinterpret_cast<uint4 *>(kbase + i * RP * L::kPitch) = st.k[i];
-    if (Stage<D>::kVAll || r0 < kSub / 4) {
-        // V^T rows 8c .. 8c+7, slot r0 (keys 4r0 .. 4r0+3)
-        char *vbase = stage_base + L::kBytes + 8 * c * L::vPitch + 8 * r0;
-        const uint32_t *a = reinterpret_cast<const uint32_t *>(&st.v[0]);
-        const uint32_t *b = reinterpret_cast<const uint32_t *>(&st.v[1]);
-        const uint32_t *e = reinterpret_cast<const uint32_t *>(&st.v[2]);
-        const uint32_t *f = reinterpret_cast<const uint32_t *>(&st.v[3]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            *reinterpret_cast<uint2 *>(vbase + (2 * p) * L::vPitch) = make_uint2(perm_lo(a[p], b[p]), perm_lo(e[p], f[p]));
-            *reinterpret_cast<uint2 *>(vbase + (2 * p + 1) * L::vPitch) =
-                make_uint2(perm_hi(a[p], b[p]), perm_hi(e[p], f[p]));
-        }
+    for (int t = 0; t < loads; ++t) {
+        const int r = 32 * wave + rows_per_load * t + lr;
+        const int rs = r < valid ? r : valid - 1;
+        const uint16_t *ks = kh + (long)(key0 + rs) * D + 8 * (pc ^ k_swz<D>(r));
+        const uint16_t *vs = vh + (long)(key0 + rs) * D + 8 * (pc ^ v_swz<D>(r));
+        char *kd = stage + (32 * wave + rows_per_load * t) * L::pitch;
+        load_lds16(ks, kd);
+        load_lds16(vs, kd + L::kBytes);
     }
 }
 
@@ -148,17 +134,8 @@ __device__ __forceinline__ Entry list_entry(const int32_t *lrow, const float *wr
     return Entry{j, __log2f(wj)};
 }
 
-template <int D>
-__device__ __forceinline__ void load_subtile(Stage<D> &st, const uint16_t *kh, const uint16_t *vh, Entry en, int half_idx,
-                                             int N, int tid)
-{
-    const int key0 = en.j * kBlock + kSub * half_idx;
-    const int valid = (en.j < 0) ? 0 : min(kSub, N - key0);
-    stage_load<D>(st, kh + (long)key0 * D, vh + (long)key0 * D, valid, valid == kSub, tid);
-}
-
 template <int D, bool full>
-__global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void attend_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
     uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap, float scale_log2)
@@ -170,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     __shared__ __align__(16) char lds[2 * L::stage];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, half = lane >> 5;
+    const int l32 = lane & 31, half = lane >> 5, grp = lane >> 4, i16 = lane & 15;
     const int blk = xcd_contiguous_id(blockIdx.x, gridDim.x);   // (b*H + h) * NB + query block
     const int qb = blk % NB;
     const long bh = blk / NB;
@@ -178,23 +155,33 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     const uint16_t *kh = k + bh * N_pad * D;
     const uint16_t *vh = v + bh * N_pad * D;
 
-    // this lane's query row; padding rows read as zero
-    const int qrow = qb * kBlock + wave * 32 + l32;
-    const bool qvalid = qrow < N;
-    bf16x8 qf[KS];
+    // this lane's two query rows (one per 32-row tile); padding rows read as zero
+    int qrow[QT];
+    bool qvalid[QT];
+    bf16x8 qf[QT][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (qvalid) raw = *reinterpret_cast<const uint4 *>(qh + (long)qrow * D + 16 * ks + 8 * half);
-        qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    for (int qt = 0; qt < QT; ++qt) {
+        qrow[qt] = qb * kBlock + wave * 64 + qt * 32 + l32;
+        qvalid[qt] = qrow[qt] < N;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 raw = make_uint4(0, 0, 0, 0);
+            if (qvalid[qt]) raw = *reinterpret_cast<const uint4 *>(qh + (long)qrow[qt] * D + 16 * ks + 8 * half);
+            qf[qt][ks] = __builtin_bit_cast(bf16x8, raw);
+        }
     }
 
-    floatx16 o[DT];
+    floatx16 o[QT][DT];
+    float m_run[QT], l_run[QT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int qt = 0; qt < QT; ++qt) {
+        m_run[qt] = -INFINITY;
+        l_run[qt] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[qt][dt][r] = 0.f;
+    }
     const floatx16 zero16 = {};
 
     int n_list = NB;
@@ -208,119 +195,175 @@ __global__ __launch_bounds__(256, 2) void attend_bf16_kernel(
     }
     const int n_sub = 2 * n_list;   // sub-tile u = half (u & 1) of list entry u >> 1
 
-    // per-lane LDS read bases (constant offsets are added per instruction)
-    const int k_rd = l32 * L::kPitch + 16 * half;
-    const int v_rd = L::kBytes + l32 * L::vPitch + 8 * half;
+    // Per-lane LDS read offsets (compile-time row offsets are added in the loops).
+    // K: row 32kt + l32, logical chunk 2ks + half; row % 16 == l32 % 16.
+    int k_rd[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_rd[ks] = l32 * L::pitch + 16 * ((2 * ks + half) ^ k_swz<D>(l32));
+    // V (transposing reads): lane group grp addresses row kb + i16/4 (kb a
+    // multiple of 4) at dims 32dt + 16(grp & 1) + 4(i16 % 4), with kb = 32kt +
+    // 16sub + 4half (+8 for the second read), so lane (l32, half) receives dim
+    // 32dt + l32 at the keys its P^T operand holds.
+    int v_rd[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const int rr = 4 * half + (i16 >> 2);
+        const int c = 4 * dt + 2 * (grp & 1) + ((i16 & 3) >> 1);
+        v_rd[dt] = L::kBytes + rr * L::pitch + 16 * (c ^ v_swz<D>(rr)) + 8 * (i16 & 1);
+    }
 
-    Stage<D> st;
     Entry cur{-1, 0.f};
     if (n_sub > 0) {
         cur = list_entry<full>(lrow, wrow, 0, NB);
-        load_subtile<D>(st, kh, vh, cur, 0, N, tid);
-        stage_store<D>(st, lds, tid);
+        if (cur.j >= 0)
+            stage_issue<D>(kh, vh, cur.j * kBlock, min(kSub, N - cur.j * kBlock), lds, wave, lane);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int u = 0; u < n_sub; ++u) {
-        char *cur_stage = lds + (u & 1) * L::stage;
-        // prefetch the next sub-tile into registers; it lands while this one is computed
-        Entry nxt = cur;
-        if (u + 1 < n_sub) {
-            if (u & 1) nxt = list_entry<full>(lrow, wrow, (u + 1) >> 1, NB);
-            load_subtile<D>(st, kh, vh, nxt, (u + 1) & 1, N, tid);
-        }
-
-        const int key0 = cur.j * kBlock + kSub * (u & 1);
-        if (cur.j >= 0 && key0 < N) {   // uniform over the workgroup
-            // S^T = K Q^T: tile kt holds keys [32kt, 32kt+32) of the sub-tile x this
-            // wave's 32 queries; lane (l32, half) holds key 32kt + 8(r/4) + 4half + r%4.
-            floatx16 s[KT];
+    // Per sub-tile: S^T = K Q^T for both query tiles; s[qt][kt] holds keys
+    // [32kt, 32kt+32) of the sub-tile, lane (l32, half) key 32kt + 8(r/4) + 4half + r%4.
+    floatx16 s[QT][KT];
+    float m_tile[QT];
+    auto scores = [&](const char *stage, int key0) {
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                const char *kr = cur_stage + k_rd + kt * 32 * L::kPitch;
+        for (int kt = 0; kt < KT; ++kt) {
+            const char *kr = stage + kt * 32 * L::pitch;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const uint4 a = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
-                    s[kt] = mfma32(__builtin_bit_cast(bf16x8, a), qf[ks], ks == 0 ? zero16 : s[kt]);
-                }
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kr + k_rd[ks]));
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(a, qf[qt][ks], ks == 0 ? zero16 : s[qt][kt]);
             }
-            if (key0 + kSub > N) {   // ragged end of the sequence: mask padding keys
+        }
+        if (key0 + kSub > N) {   // ragged end of the sequence: mask padding keys
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        if (key0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= N) s[kt][r] = -INFINITY;
-            }
-
-            // online softmax in the exp2 domain; the block weight is a logit shift
+                        if (key0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= N) s[qt][kt][r] = -INFINITY;
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qt][kt][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_tile = fmaf(mx, scale_log2, cur.lw);
-            if (__ballot(m_tile > m_run + kRescaleSlack) != 0) {   // wave-uniform
-                const float m_new = fmaxf(m_run, m_tile);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
+            m_tile[qt] = fmaf(mx, scale_log2, cur.lw);   // block weight enters as a logit shift
+        }
+    };
+    // Probabilities against the running max, then O^T += V^T P^T.  MFMA (kt, sub)
+    // contracts the 16 keys held in accumulator rows [8sub, 8sub+8) of tile kt:
+    // for lane half h, element e is key 32kt + 16sub + 8(e/4) + 4h + e%4,
+    // fetched by two transposing reads at rows 32kt + 16sub + 4h (+8).
+    auto accumulate = [&](const char *stage) {
+        bf16x8 pb[QT][KT][2];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            }
-            const float bias = cur.lw - m_run;
-
-            bf16x8 pb[KT][2];
+        for (int qt = 0; qt < QT; ++qt) {
+            const float bias = cur.lw - m_run[qt];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, bias));
-                    l_run += p;
-                    pb[kt][r >> 3][r & 7] = (__bf16)p;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][kt][r], scale_log2, bias));
+                    l_run[qt] += p;
+                    pb[qt][kt][r >> 3][r & 7] = (__bf16)p;
                 }
-
-            // O^T += V^T P^T.  MFMA (kt, sub) contracts the 16 keys held in
-            // accumulator rows [8sub, 8sub+8) of tile kt: for lane half h,
-            // element e is key 32kt + 16sub + 8(e/4) + 4h + e%4, i.e. V^T slots
-            // 8kt + 4sub + h and 8kt + 4sub + h + 2.
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const char *vr = cur_stage + v_rd + dt * 32 * L::vPitch;
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                    for (int sub = 0; sub < 2; ++sub) {
-                        const uint2 a0 = *reinterpret_cast<const uint2 *>(vr + 8 * (8 * kt + 4 * sub));
-                        const uint2 a1 = *reinterpret_cast<const uint2 *>(vr + 8 * (8 * kt + 4 * sub + 2));
-                        const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
-                        o[dt] = mfma32(__builtin_bit_cast(bf16x8, a), pb[kt][sub], o[dt]);
-                    }
-            }
         }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int sub = 0; sub < 2; ++sub) {
+                    const char *vr = stage + v_rd[dt] + (32 * kt + 16 * sub) * L::pitch;
+                    const uint2 a0 = lds_read_tr16(vr);
+                    const uint2 a1 = lds_read_tr16(vr + 8 * L::pitch);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+#pragma unroll
+                    for (int qt = 0; qt < QT; ++qt) o[qt][dt] = mfma32(a, pb[qt][kt][sub], o[qt][dt]);
+                }
+    };
+    // Issue the direct loads of sub-tile u + 1 into the other stage.
+    auto prefetch = [&](int u, Entry &nxt) {
+        nxt = cur;
+        if (u + 1 < n_sub) {
+            if (u & 1) nxt = list_entry<full>(lrow, wrow, (u + 1) >> 1, NB);
+            const int nkey0 = nxt.j * kBlock + kSub * ((u + 1) & 1);
+            if (nxt.j >= 0 && nkey0 < N)
+                stage_issue<D>(kh, vh, nkey0, min(kSub, N - nkey0), lds + ((u + 1) & 1) * L::stage, wave, lane);
+        }
+    };
 
-        if (u + 1 < n_sub) stage_store<D>(st, lds + ((u + 1) & 1) * L::stage, tid);
+    // The running max only moves when a sub-tile's max exceeds it by more than
+    // the slack (always on the first sub-tile).  Such sub-tiles leave the hot
+    // loop for the rescale below, so inside the hot loop the output
+    // accumulators are touched by MFMAs only.
+    int u = 0;
+    while (u < n_sub) {
+        bool grow = false;
+        Entry nxt;
+        for (; u < n_sub; ++u) {
+            const char *stage = lds + (u & 1) * L::stage;
+            prefetch(u, nxt);
+            const int key0 = cur.j * kBlock + kSub * (u & 1);
+            if (cur.j >= 0 && key0 < N) {   // uniform over the workgroup
+                scores(stage, key0);
+                const bool g0 = m_tile[0] > m_run[0] + kRescaleSlack, g1 = m_tile[1] > m_run[1] + kRescaleSlack;
+                if (__ballot(g0 || g1) != 0) {
+                    grow = true;
+                    break;
+                }
+                accumulate(stage);
+            }
+            cur = nxt;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        if (!grow) break;
+        // rescale (rare): sub-tile u's scores are in s, its successor is in flight
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            const float m_new = fmaxf(m_run[qt], m_tile[qt]);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+            m_run[qt] = m_new;
+            l_run[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[qt][dt][r] *= alpha;
+        }
+        accumulate(lds + (u & 1) * L::stage);
         cur = nxt;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        ++u;
     }
 
     // normalise and store: lane holds dims dt*32 + 8(r/4) + 4half + r%4 of its query
-    l_run += __shfl_xor(l_run, 32, 64);
-    const float inv = (l_run > 0.f && qvalid) ? 1.f / l_run : 0.f;
-    uint16_t *orow = out + (bh * N_pad + qrow) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int qt = 0; qt < QT; ++qt) {
+        const float lsum = l_run[qt] + __shfl_xor(l_run[qt], 32, 64);
+        const float inv = (lsum > 0.f && qvalid[qt]) ? 1.f / lsum : 0.f;
+        uint16_t *orow = out + (bh * N_pad + qrow[qt]) * D;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d = dt * 32 + 8 * g + 4 * half;
-            __bf16 b0 = (__bf16)(o[dt][4 * g + 0] * inv), b1 = (__bf16)(o[dt][4 * g + 1] * inv);
-            __bf16 b2 = (__bf16)(o[dt][4 * g + 2] * inv), b3 = (__bf16)(o[dt][4 * g + 3] * inv);
-            const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-            const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-            *reinterpret_cast<uint2 *>(orow + d) = make_uint2(lo, hi);
-        }
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = dt * 32 + 8 * g + 4 * half;
+                __bf16 b0 = (__bf16)(o[qt][dt][4 * g + 0] * inv), b1 = (__bf16)(o[qt][dt][4 * g + 1] * inv);
+                __bf16 b2 = (__bf16)(o[qt][dt][4 * g + 2] * inv), b3 = (__bf16)(o[qt][dt][4 * g + 3] * inv);
+                const uint32_t lo =
+                    (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+                const uint32_t hi =
+                    (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+                *reinterpret_cast<uint2 *>(orow + d) = make_uint2(lo, hi);
+            }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -426,11 +469,11 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
     const dim3 grid((unsigned)((long)B * H * NB)), block(256);
     const float sl2 = scale * kLog2e;
     if (dtype == kBF16 && D == 128)
-        attend_bf16_kernel<128, full><<<grid, block, 0, s>>>((const uint16_t *)q, (const uint16_t *)k,
+        attend_bf16_kernel<128, full><<<grid, dim3(kThreads), 0, s>>>((const uint16_t *)q, (const uint16_t *)k,
                                                             (const uint16_t *)v, idx, cnt, w, (uint16_t *)out, N, N_pad,
                                                             NB, cap, sl2);
     else if (dtype == kBF16 && D == 64)
-        attend_bf16_kernel<64, full><<<grid, block, 0, s>>>((const uint16_t *)q, (const uint16_t *)k,
+        attend_bf16_kernel<64, full><<<grid, dim3(kThreads), 0, s>>>((const uint16_t *)q, (const uint16_t *)k,
                                                            (const uint16_t *)v, idx, cnt, w, (uint16_t *)out, N, N_pad,
                                                            NB, cap, sl2);
     else if (dtype == kF32 && D == 64)
