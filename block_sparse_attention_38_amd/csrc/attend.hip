@@ -94,27 +94,63 @@ __device__ __forceinline__ void load_lds16(const uint16_t *src, char *dst)
 
 // Issue the direct loads of one 64-key sub-tile of K and V (rows key0 ..
 // key0 + 63) into an LDS stage.  Wavefront w fills rows [32w, 32w + 32) of
-// both tensors: eight loads of four rows each per tensor.  Rows past the last
-// valid one are read from that row instead (finite values; those keys are
+// both tensors with loads of 1024 bytes (four rows at D = 128).  The source
+// byte offset of every lane is precomputed (DmaOffsets), so a full sub-tile is
+// scalar base + per-lane offset only.  On the ragged last block, rows past the
+// last valid one are read from that row instead (finite values; those keys are
 // masked and their probabilities are zero).  Needs a vmcnt wait and a barrier
 // before the stage is read.
+template <int D> struct DmaOffsets {
+    static constexpr int rows_per_load = 1024 / (D * 2);   // 4 (D=128) or 8 (D=64)
+    static constexpr int loads = 32 / rows_per_load;
+    static constexpr int kPeriod = 16 / rows_per_load;     // loads after which the K swizzle repeats
+    int k[kPeriod];
+    int v;
+};
+
 template <int D>
-__device__ __forceinline__ void stage_issue(const uint16_t *kh, const uint16_t *vh, int key0, int valid, char *stage,
-                                            int wave, int lane)
+__device__ __forceinline__ DmaOffsets<D> dma_offsets(int wave, int lane)
 {
     using L = Lds<D>;
-    constexpr int rows_per_load = 1024 / L::pitch;   // 4 (D=128) or 8 (D=64)
-    constexpr int loads = 32 / rows_per_load;
-    const int lr = lane / L::chunks, pc = lane % L::chunks;   // row within the load, physical chunk
+    DmaOffsets<D> off;
+    const int lr = lane / L::chunks, pc = lane % L::chunks;
 #pragma unroll
-    for (int t = 0; t < loads; ++t) {
-        const int r = 32 * wave + rows_per_load * t + lr;
-        const int rs = r < valid ? r : valid - 1;
-        const uint16_t *ks = kh + (long)(key0 + rs) * D + 8 * (pc ^ k_swz<D>(r));
-        const uint16_t *vs = vh + (long)(key0 + rs) * D + 8 * (pc ^ v_swz<D>(r));
-        char *kd = stage + (32 * wave + rows_per_load * t) * L::pitch;
-        load_lds16(ks, kd);
-        load_lds16(vs, kd + L::kBytes);
+    for (int t = 0; t < DmaOffsets<D>::kPeriod; ++t) {
+        const int r = 32 * wave + DmaOffsets<D>::rows_per_load * t + lr;
+        off.k[t] = r * L::pitch + 16 * (pc ^ k_swz<D>(r));
+    }
+    const int r0 = 32 * wave + lr;
+    off.v = r0 * L::pitch + 16 * (pc ^ v_swz<D>(r0));
+    return off;
+}
+
+template <int D>
+__device__ __forceinline__ void stage_issue(const uint16_t *kh, const uint16_t *vh, int key0, int valid, char *stage,
+                                            int wave, int lane, const DmaOffsets<D> &off)
+{
+    using L = Lds<D>;
+    using O = DmaOffsets<D>;
+    const char *kb = reinterpret_cast<const char *>(kh + (long)key0 * D);
+    const char *vb = reinterpret_cast<const char *>(vh + (long)key0 * D);
+    char *kd = stage + 32 * wave * L::pitch;
+    if (valid >= kSub) {
+#pragma unroll
+        for (int t = 0; t < O::loads; ++t) {
+            const int step = O::rows_per_load * t * L::pitch;   // whole rows: the V swizzle is unchanged
+            load_lds16(reinterpret_cast<const uint16_t *>(kb + (off.k[t % O::kPeriod] + (t / O::kPeriod) * 16 * L::pitch)),
+                       kd + step);
+            load_lds16(reinterpret_cast<const uint16_t *>(vb + off.v + step), kd + L::kBytes + step);
+        }
+    } else {
+        const int lr = lane / L::chunks, pc = lane % L::chunks;
+#pragma unroll
+        for (int t = 0; t < O::loads; ++t) {
+            const int r = 32 * wave + O::rows_per_load * t + lr;
+            const int rs = r < valid ? r : valid - 1;
+            load_lds16(kh + (long)(key0 + rs) * D + 8 * (pc ^ k_swz<D>(r)), kd + O::rows_per_load * t * L::pitch);
+            load_lds16(vh + (long)(key0 + rs) * D + 8 * (pc ^ v_swz<D>(r)),
+                       kd + L::kBytes + O::rows_per_load * t * L::pitch);
+        }
     }
 }
 
@@ -212,11 +248,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         v_rd[dt] = L::kBytes + rr * L::pitch + 16 * (c ^ v_swz<D>(rr)) + 8 * (i16 & 1);
     }
 
+    const DmaOffsets<D> dma = dma_offsets<D>(wave, lane);
     Entry cur{-1, 0.f};
     if (n_sub > 0) {
         cur = list_entry<full>(lrow, wrow, 0, NB);
         if (cur.j >= 0)
-            stage_issue<D>(kh, vh, cur.j * kBlock, min(kSub, N - cur.j * kBlock), lds, wave, lane);
+            stage_issue<D>(kh, vh, cur.j * kBlock, min(kSub, N - cur.j * kBlock), lds, wave, lane, dma);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -261,9 +298,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // for lane half h, element e is key 32kt + 16sub + 8(e/4) + 4h + e%4,
     // fetched by two transposing reads at rows 32kt + 16sub + 4h (+8).
     auto accumulate = [&](const char *stage) {
-        bf16x8 pb[QT][KT][2];
+        // query tile 0's PV MFMAs are independent of tile 1's softmax, so the
+        // two can be co-issued
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
+            bf16x8 pb[KT][2];
             const float bias = cur.lw - m_run[qt];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
@@ -271,22 +310,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 for (int r = 0; r < 16; ++r) {
                     const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][kt][r], scale_log2, bias));
                     l_run[qt] += p;
-                    pb[qt][kt][r >> 3][r & 7] = (__bf16)p;
+                    pb[kt][r >> 3][r & 7] = (__bf16)p;
                 }
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub) {
-                    const char *vr = stage + v_rd[dt] + (32 * kt + 16 * sub) * L::pitch;
-                    const uint2 a0 = lds_read_tr16(vr);
-                    const uint2 a1 = lds_read_tr16(vr + 8 * L::pitch);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+                for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                    for (int qt = 0; qt < QT; ++qt) o[qt][dt] = mfma32(a, pb[qt][kt][sub], o[qt][dt]);
-                }
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const char *vr = stage + v_rd[dt] + (32 * kt + 16 * sub) * L::pitch;
+                        const uint2 a0 = lds_read_tr16(vr);
+                        const uint2 a1 = lds_read_tr16(vr + 8 * L::pitch);
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+                        o[qt][dt] = mfma32(a, pb[kt][sub], o[qt][dt]);
+                    }
+        }
     };
     // Issue the direct loads of sub-tile u + 1 into the other stage.
     auto prefetch = [&](int u, Entry &nxt) {
@@ -295,7 +333,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             if (u & 1) nxt = list_entry<full>(lrow, wrow, (u + 1) >> 1, NB);
             const int nkey0 = nxt.j * kBlock + kSub * ((u + 1) & 1);
             if (nxt.j >= 0 && nkey0 < N)
-                stage_issue<D>(kh, vh, nkey0, min(kSub, N - nkey0), lds + ((u + 1) & 1) * L::stage, wave, lane);
+                stage_issue<D>(kh, vh, nkey0, min(kSub, N - nkey0), lds + ((u + 1) & 1) * L::stage, wave, lane, dma);
         }
     };
 
