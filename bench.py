@@ -188,7 +188,7 @@ def main():
         aba.sample(p, scores, args.seed, out=lists)
         if ev is not None:
             ev[2].record(stream)
-        aba.attend(p, qd, kd, vd, *lists, out=out)
+        aba.attend(p, qd, kd, vd, *lists, out=out, ws=ws)
         if ev is not None:
             ev[3].record(stream)
 
@@ -218,12 +218,12 @@ def main():
 
     dense_ms = None
     if not args.no_dense:
-        aba.attend_full(p, qd, kd, vd, out=out)
+        aba.attend_full(p, qd, kd, vd, out=out, ws=ws)
         torch.cuda.synchronize()
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         d0.record(stream)
         for _ in range(args.dense_reps):
-            aba.attend_full(p, qd, kd, vd, out=out)
+            aba.attend_full(p, qd, kd, vd, out=out, ws=ws)
         d1.record(stream)
         torch.cuda.synchronize()
         dense_ms = d0.elapsed_time(d1) / args.dense_reps

@@ -69,8 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.aba_plan.argtypes = [PP, i32, i32, i32, i32, i32, i32, i32, i32, f32]
     lib.aba_score.argtypes = [PP, P, P, P, P, P, P, P, P]
     lib.aba_sample.argtypes = [PP, P, u64, P, P, P, P]
-    lib.aba_attend.argtypes = [PP, P, P, P, P, P, P, P, P]
-    lib.aba_attend_full.argtypes = [PP, P, P, P, P, P]
+    lib.aba_attend.argtypes = [PP, P, P, P, P, P, P, P, P, P]
+    lib.aba_attend_full.argtypes = [PP, P, P, P, P, P, P]
     for name in ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full"):
         getattr(lib, name).restype = ctypes.c_int
     lib.aba_last_error.argtypes = []
@@ -135,7 +135,16 @@ def _qkv_shape(p: Plan):
 
 
 def workspace(p: Plan, device) -> torch.Tensor:
+    """Device scratch of p.workspace_bytes; one buffer serves every call ordered on a stream."""
     return torch.empty(max(int(p.workspace_bytes), 1), dtype=torch.uint8, device=device)
+
+
+def _ws(p: Plan, ws, device) -> torch.Tensor:
+    if ws is None:
+        return workspace(p, device)
+    if ws.device != device or ws.numel() * ws.element_size() < int(p.workspace_bytes) or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous {int(p.workspace_bytes)}-byte buffer on {device}")
+    return ws
 
 
 def score(p: Plan, q: torch.Tensor, k: torch.Tensor, *, return_parts: bool = False, out: torch.Tensor | None = None,
@@ -154,8 +163,8 @@ def score(p: Plan, q: torch.Tensor, k: torch.Tensor, *, return_parts: bool = Fal
         cent = torch.empty(B, H, NB, C, D, dtype=torch.float32, device=dev)
         wgt = torch.empty(B, H, NB, C, dtype=torch.float32, device=dev)
         kbar = torch.empty(B, H, NB, D, dtype=torch.float32, device=dev)
-    elif ws is None:
-        ws = workspace(p, dev)
+    else:
+        ws = _ws(p, ws, dev)
     _check(load_library().aba_score(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(out), _ptr(cent), _ptr(wgt),
                                     _ptr(kbar), _ptr(ws), _stream()))
     return (out, cent, wgt, kbar) if return_parts else out
@@ -179,7 +188,7 @@ def sample(p: Plan, scores: torch.Tensor, seed: int, *, out=None):
     return idx, cnt, w
 
 
-def attend(p: Plan, q, k, v, idx, cnt, w, *, out=None) -> torch.Tensor:
+def attend(p: Plan, q, k, v, idx, cnt, w, *, out=None, ws=None) -> torch.Tensor:
     """aba_attend: HT-weighted block-sparse attention, [B,H,N_pad,D] in the plan's dtype."""
     dev = q.device
     shp = _qkv_shape(p)
@@ -192,12 +201,13 @@ def attend(p: Plan, q, k, v, idx, cnt, w, *, out=None) -> torch.Tensor:
     if out is None:
         out = torch.empty(shp, dtype=p.torch_dtype, device=dev)
     _need(out, "out", shp, p.torch_dtype, dev)
+    ws = _ws(p, ws, dev)
     _check(load_library().aba_attend(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(cnt), _ptr(w),
-                                     _ptr(out), _stream()))
+                                     _ptr(out), _ptr(ws), _stream()))
     return out
 
 
-def attend_full(p: Plan, q, k, v, *, out=None) -> torch.Tensor:
+def attend_full(p: Plan, q, k, v, *, out=None, ws=None) -> torch.Tensor:
     """aba_attend_full: dense softmax attention, [B,H,N_pad,D] in the plan's dtype."""
     dev = q.device
     shp = _qkv_shape(p)
@@ -206,15 +216,18 @@ def attend_full(p: Plan, q, k, v, *, out=None) -> torch.Tensor:
     if out is None:
         out = torch.empty(shp, dtype=p.torch_dtype, device=dev)
     _need(out, "out", shp, p.torch_dtype, dev)
-    _check(load_library().aba_attend_full(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream()))
+    ws = _ws(p, ws, dev)
+    _check(load_library().aba_attend_full(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
+                                          _stream()))
     return out
 
 
-def layer(p: Plan, q, k, v, seed: int):
+def layer(p: Plan, q, k, v, seed: int, *, ws=None):
     """One pass of the whole hot path: score -> sample -> attend."""
-    s = score(p, q, k)
+    ws = _ws(p, ws, q.device)
+    s = score(p, q, k, ws=ws)
     idx, cnt, w = sample(p, s, seed)
-    return attend(p, q, k, v, idx, cnt, w), (s, idx, cnt, w)
+    return attend(p, q, k, v, idx, cnt, w, ws=ws), (s, idx, cnt, w)
 
 
 def version() -> str:

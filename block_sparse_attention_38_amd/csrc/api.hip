@@ -35,8 +35,12 @@ aba_status hip_status(hipError_t e, const char *what)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// One workspace serves every call, each using it from offset 0 and only for
+// the duration of the call: aba_score keeps centroids, weights and pooled keys
+// there when the caller does not ask for them, aba_attend and aba_attend_full
+// the V^T staging copy of v.
 struct Workspace {
-    size_t cent, weight, kbar, total;
+    size_t cent, weight, kbar, score_total, attend_total, total;
 };
 
 Workspace workspace_layout(const aba_plan_t &p)
@@ -46,8 +50,18 @@ Workspace workspace_layout(const aba_plan_t &p)
     w.cent = 0;
     w.weight = align256(rows * p.n_clusters * p.head_dim * sizeof(float));
     w.kbar = w.weight + align256(rows * p.n_clusters * sizeof(float));
-    w.total = w.kbar + align256(rows * p.head_dim * sizeof(float));
+    w.score_total = w.kbar + align256(rows * p.head_dim * sizeof(float));
+    w.attend_total = align256(aba::attend_workspace_bytes(p.dtype, p.batch, p.heads, p.seq_pad, p.head_dim));
+    w.total = w.score_total > w.attend_total ? w.score_total : w.attend_total;
     return w;
+}
+
+aba_status check_attend_workspace(const aba_plan_t *p, const void *workspace)
+{
+    if (!workspace && workspace_layout(*p).attend_total > 0)
+        return fail(ABA_E_INVALID, "workspace of %llu bytes is required for bf16 attention",
+                    (unsigned long long)p->workspace_bytes);
+    return ABA_OK;
 }
 
 // A plan must be exactly what aba_plan produces for its own fields.
@@ -151,28 +165,33 @@ aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, i
 }
 
 aba_status aba_attend(const aba_plan_t *p, const void *q, const void *k, const void *v, const int32_t *idx,
-                      const int32_t *cnt, const float *w, void *out, hipStream_t stream)
+                      const int32_t *cnt, const float *w, void *out, void *workspace, hipStream_t stream)
 {
     g_last_error.clear();
     aba_status st = check_plan(p);
     if (st != ABA_OK) return st;
     if (!q || !k || !v || !idx || !cnt || !w || !out)
         return fail(ABA_E_INVALID, "q, k, v, idx, cnt, w and out must be non-NULL");
+    st = check_attend_workspace(p, workspace);
+    if (st != ABA_OK) return st;
     return hip_status(aba::launch_attend(q, k, v, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad, p->head_dim,
-                                         p->n_blocks, p->softmax_scale, idx, cnt, w, p->list_cap, false, out, stream),
+                                         p->n_blocks, p->softmax_scale, idx, cnt, w, p->list_cap, false, workspace, out,
+                                         stream),
                       "attend launch");
 }
 
 aba_status aba_attend_full(const aba_plan_t *p, const void *q, const void *k, const void *v, void *out,
-                           hipStream_t stream)
+                           void *workspace, hipStream_t stream)
 {
     g_last_error.clear();
     aba_status st = check_plan(p);
     if (st != ABA_OK) return st;
     if (!q || !k || !v || !out) return fail(ABA_E_INVALID, "q, k, v and out must be non-NULL");
+    st = check_attend_workspace(p, workspace);
+    if (st != ABA_OK) return st;
     return hip_status(aba::launch_attend(q, k, v, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad, p->head_dim,
-                                         p->n_blocks, p->softmax_scale, nullptr, nullptr, nullptr, p->list_cap, true, out,
-                                         stream),
+                                         p->n_blocks, p->softmax_scale, nullptr, nullptr, nullptr, p->list_cap, true,
+                                         workspace, out, stream),
                       "attend_full launch");
 }
 

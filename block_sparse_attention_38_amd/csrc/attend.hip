@@ -9,23 +9,28 @@
 // with no permutation and no copies (third paragraph).  The dense path is the
 // same kernel over every key block with unit weights.
 //
-// bf16 path (the hot path): one workgroup of 4 wavefronts per (b, h, query
-// block), two workgroups per CU; wavefront w owns query rows [32w, 32w + 32).
-// Each kept key block is streamed as two 64-key sub-tiles through a
-// double-buffered LDS stage: the next sub-tile's global loads are issued into
-// registers before the current one is computed and written to the other LDS
-// buffer afterwards, so one barrier per sub-tile remains.  Per sub-tile:
+// bf16 path (the hot path), two kernels:
+//   vt_kernel     writes V once per call as 64-key V^T tiles (see "V^T
+//                 staging" below), so that the PV operand is one 16-byte LDS
+//                 read (a transposing read of row-major V runs at half the
+//                 LDS rate on gfx950);
+//   attend_bf16   one workgroup of 4 wavefronts per (b, h, query block), two
+//                 workgroups per CU (two wavefronts per SIMD); wavefront w owns
+//                 query rows [32w, 32w + 32).  A kept key block is two 64-key
+//                 sub-tiles, each copied by buffer->LDS direct loads into one of
+//                 two LDS stages while the other stage is computed; one barrier
+//                 per sub-tile.  Per sub-tile:
 //   S^T = K Q^T      32x32x16 bf16 MFMA, K from LDS, Q fragments in registers
 //   online softmax   in the exp2 domain; the block's log2(w_j) is added to its
 //                    logits, so the weight enters numerator and normaliser; the
 //                    running max moves only when it grows by more than 2^8
 //   O^T += V^T P^T   32x32x16 bf16 MFMA, P^T straight from the S^T accumulators
 // Computing the transposed products makes every lane own one query column, so
-// row statistics need a single cross-half exchange and the rescale of O is a
-// per-lane scalar multiply.  K sits in LDS row-major; V is transposed on its
-// way into LDS (key-contiguous) so that the PV operand is two 8-byte reads.
-// Both use padded rows, which keeps the reads free of bank conflicts and every
-// LDS address a per-lane base plus an immediate offset.
+// row statistics need a single cross-half exchange (v_permlane32_swap) and the
+// rescale of O is a per-lane scalar multiply.  LDS fragment reads are issued
+// four MFMAs ahead of their use, and the second key tile's exponentials are
+// interleaved with the first tile's PV MFMAs (transcendentals overlap matrix
+// work on gfx950, plain VALU arithmetic largely does not).
 //
 // fp32 path: a plain VALU kernel (pairs of lanes per query row) for fp32
 // inputs with head_dim 64.
@@ -35,6 +40,7 @@ namespace aba {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -49,108 +55,147 @@ constexpr int kSub = 64;
 // Lazy rescaling: the running max only moves when a sub-tile's max exceeds it
 // by more than this many powers of two (exp2 values then stay below 2^8).
 constexpr float kRescaleSlack = 8.f;
-// Two wavefronts per workgroup, 64 query rows each (two 32-row MFMA tiles).
-constexpr int kThreads = 128;
-constexpr int QT = 2;
+// A workgroup covers one 128-row query block with four wavefronts of 32 rows
+// (one 32x32 MFMA tile of queries each); two workgroups share a CU, so every
+// SIMD runs two wavefronts.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 
-// LDS layout of one stage: K and V sub-tiles of 64 rows x D bf16, unpadded
-// (one direct global->LDS load fills four whole rows), with XOR swizzles of the
-// 16-byte chunks chosen per tensor:
-//   K  chunk c of row r at c ^ (r % 16): the 16 rows one 16-lane phase of a
-//      128-bit read touches hit 16 different chunks;
-//   V  chunk c of row r at c ^ 4(r % 4): the four rows x 64 bytes that 32 lanes
-//      of a transposing 64-bit read touch fall on distinct banks.
+// ---------------------------------------------------------------------------
+// V^T staging.  The PV product contracts over keys, so its MFMA operand wants
+// each lane's 8 keys of one head dimension contiguous.  A pre-pass writes V
+// once per call as, for every (b, h) and 64-key sub-tile s, a [D][64] bf16
+// tile whose row d holds v[64s + .][d] with key order vt_key(): inside each
+// group of 16 keys, positions 4..7 and 8..11 are exchanged.  Lane half h of
+// an MFMA then finds its keys 8(e/4) + 4h + e%4 (e = 0..7, the order in which
+// the S^T accumulators hand over P^T) at positions 8h .. 8h+7: one 16-byte
+// LDS read.  Keys >= N are written as zero.  The tiles occupy the same
+// B*H*N_pad*D elements as v.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+template <int D>
+__global__ __launch_bounds__(256) void vt_kernel(const uint16_t *__restrict__ v, int N, int N_pad,
+                                                 uint16_t *__restrict__ vt)
+{
+    constexpr int kRow = D + 2;                 // odd word stride: the column reads spread over banks
+    constexpr int kChunks = kSub * D / 8;       // 16-byte chunks per tile
+    __shared__ uint32_t tile[kSub * kRow / 2];
+    const int tiles = N_pad / kSub;
+    const int s = blockIdx.x % tiles;
+    const long bh = blockIdx.x / tiles;
+    const uint16_t *src = v + (bh * N_pad + (long)kSub * s) * D;
+    const int valid = N - kSub * s;
+    for (int i = threadIdx.x; i < kChunks; i += 256) {
+        const int r = i / (D / 8), c = i % (D / 8);
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (r < valid) x = *reinterpret_cast<const uint4 *>(src + (long)r * D + 8 * c);
+        uint32_t *t = tile + (r * kRow + 8 * c) / 2;
+        t[0] = x.x;
+        t[1] = x.y;
+        t[2] = x.z;
+        t[3] = x.w;
+    }
+    __syncthreads();
+    const uint16_t *t16 = reinterpret_cast<const uint16_t *>(tile);
+    uint4 *dst = reinterpret_cast<uint4 *>(vt + (bh * N_pad + (long)kSub * s) * D);
+    for (int i = threadIdx.x; i < kChunks; i += 256) {
+        const int d = i / (kSub / 8), c = i % (kSub / 8);   // row d, positions 8c .. 8c+7
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const int k0 = 16 * (c >> 1) + vt_key(8 * (c & 1) + e);
+            const int k1 = 16 * (c >> 1) + vt_key(8 * (c & 1) + e + 1);
+            w[e / 2] = (uint32_t)t16[k0 * kRow + d] | ((uint32_t)t16[k1 * kRow + d] << 16);
+        }
+        dst[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// LDS layout of one stage, unpadded (one direct global->LDS load fills whole
+// rows), with XOR swizzles of the 16-byte chunks:
+//   K   [64 keys][D]:  chunk c of row r at c ^ (r % 16), so the 16 rows one
+//       16-lane phase of a 128-bit read touches hit 16 different chunks;
+//   V^T [D][64 keys]:  chunk c of row r at c ^ ((r / 2) % 8); with 128-byte
+//       rows, 16 consecutive rows then cover every bank once.
 template <int D> struct Lds {
-    static constexpr int pitch = D * 2;
+    static constexpr int pitch = D * 2;        // K row bytes
     static constexpr int chunks = D / 8;
     static constexpr int kBytes = kSub * pitch;
-    static constexpr int vBytes = kSub * pitch;
+    static constexpr int vPitch = kSub * 2;    // V^T row bytes
+    static constexpr int vBytes = D * vPitch;
     static constexpr int stage = kBytes + vBytes;
 };
 template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Lds<D>::chunks - 1); }
-template <int D> __device__ __forceinline__ int v_swz(int r) { return (4 * (r & 3)) & (Lds<D>::chunks - 1); }
+__device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void glb_void;
 
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
-// lanes, lane i receives element (i % 4) of the 8-byte chunks addressed by
-// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4: if lane L addresses row kb + L/4,
-// columns c0 + 4(L % 4) .. +3 of a row-major 16-bit matrix, lane i receives
-// column c0 + i at rows kb .. kb+3.
-__device__ __forceinline__ uint2 lds_read_tr16(const char *p)
+// Buffer resource over one (b, h) slice of a [.., N_pad, D] bf16 tensor: the
+// loads below address it by byte offset and the hardware range check returns
+// zeros past its end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t *base, int bytes)
 {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p)));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, bytes, 0x00020000);
 }
 
-// Direct global -> LDS copy of 16 bytes per lane; lane L's bytes land at
-// dst + 16 L (dst is wavefront-uniform).
-__device__ __forceinline__ void load_lds16(const uint16_t *src, char *dst)
+// Direct copy of 16 bytes per lane from a buffer into LDS: lane L's bytes land
+// at dst + 16 L (dst is wavefront-uniform).  The buffer form (rather than the
+// global one) lets the compiler keep counting LDS reads exactly while these
+// copies are in flight.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, int voff, int soff, char *dst)
 {
-    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)dst, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, soff, 0, 0);
 }
 
-// Issue the direct loads of one 64-key sub-tile of K and V (rows key0 ..
-// key0 + 63) into an LDS stage.  Wavefront w fills rows [32w, 32w + 32) of
-// both tensors with loads of 1024 bytes (four rows at D = 128).  The source
-// byte offset of every lane is precomputed (DmaOffsets), so a full sub-tile is
-// scalar base + per-lane offset only.  On the ragged last block, rows past the
-// last valid one are read from that row instead (finite values; those keys are
-// masked and their probabilities are zero).  Needs a vmcnt wait and a barrier
-// before the stage is read.
-template <int D> struct DmaOffsets {
-    static constexpr int rows_per_load = 1024 / (D * 2);   // 4 (D=128) or 8 (D=64)
-    static constexpr int loads = 32 / rows_per_load;
-    static constexpr int kPeriod = 16 / rows_per_load;     // loads after which the K swizzle repeats
-    int k[kPeriod];
-    int v;
+// Direct loads of one 64-key sub-tile (K rows key0 .. key0+63 and the matching
+// V^T tile) into an LDS stage.  Every load moves 1024 bytes: whole K rows (4
+// at D = 128) or 8 V^T rows.  Wavefront w fills its share of both; the
+// per-lane byte offsets inside a sub-tile are precomputed, the sub-tile's own
+// offset is a scalar.  Rows of K past N are read as they are (they lie inside
+// the padded sequence) and masked after the product.  Needs a vmcnt wait and a
+// barrier before the stage is read.
+template <int D> struct Dma {
+    static constexpr int loads = Lds<D>::kBytes / 1024 / kWaves;   // per tensor and wavefront
+    static constexpr int k_rows = 1024 / Lds<D>::pitch;             // K rows per load
+    static constexpr int k_period = 16 / k_rows;                    // loads per K swizzle period
+    int k[k_period];
+    int v[2];                                                       // V^T swizzle period: 2 loads
 };
 
 template <int D>
-__device__ __forceinline__ DmaOffsets<D> dma_offsets(int wave, int lane)
+__device__ __forceinline__ Dma<D> dma_offsets(int wave, int lane)
 {
     using L = Lds<D>;
-    DmaOffsets<D> off;
-    const int lr = lane / L::chunks, pc = lane % L::chunks;
+    using O = Dma<D>;
+    O off;
+    const int k0 = O::loads * O::k_rows * wave, v0 = O::loads * 8 * wave;
 #pragma unroll
-    for (int t = 0; t < DmaOffsets<D>::kPeriod; ++t) {
-        const int r = 32 * wave + DmaOffsets<D>::rows_per_load * t + lr;
+    for (int t = 0; t < O::k_period; ++t) {
+        const int r = k0 + O::k_rows * t + lane / L::chunks, pc = lane % L::chunks;
         off.k[t] = r * L::pitch + 16 * (pc ^ k_swz<D>(r));
     }
-    const int r0 = 32 * wave + lr;
-    off.v = r0 * L::pitch + 16 * (pc ^ v_swz<D>(r0));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int r = v0 + 8 * t + lane / 8, pc = lane % 8;
+        off.v[t] = r * L::vPitch + 16 * (pc ^ vt_swz(r));
+    }
     return off;
 }
 
 template <int D>
-__device__ __forceinline__ void stage_issue(const uint16_t *kh, const uint16_t *vh, int key0, int valid, char *stage,
-                                            int wave, int lane, const DmaOffsets<D> &off)
+__device__ __forceinline__ void stage_issue(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int key0, char *stage,
+                                            int wave, const Dma<D> &off)
 {
     using L = Lds<D>;
-    using O = DmaOffsets<D>;
-    const char *kb = reinterpret_cast<const char *>(kh + (long)key0 * D);
-    const char *vb = reinterpret_cast<const char *>(vh + (long)key0 * D);
-    char *kd = stage + 32 * wave * L::pitch;
-    if (valid >= kSub) {
+    using O = Dma<D>;
+    const int base = key0 * D * 2;   // byte offset of the sub-tile in both K and V^T
+    char *kd = stage + O::loads * 1024 * wave;
+    char *vd = stage + L::kBytes + O::loads * 1024 * wave;
 #pragma unroll
-        for (int t = 0; t < O::loads; ++t) {
-            const int step = O::rows_per_load * t * L::pitch;   // whole rows: the V swizzle is unchanged
-            load_lds16(reinterpret_cast<const uint16_t *>(kb + (off.k[t % O::kPeriod] + (t / O::kPeriod) * 16 * L::pitch)),
-                       kd + step);
-            load_lds16(reinterpret_cast<const uint16_t *>(vb + off.v + step), kd + L::kBytes + step);
-        }
-    } else {
-        const int lr = lane / L::chunks, pc = lane % L::chunks;
-#pragma unroll
-        for (int t = 0; t < O::loads; ++t) {
-            const int r = 32 * wave + O::rows_per_load * t + lr;
-            const int rs = r < valid ? r : valid - 1;
-            load_lds16(kh + (long)(key0 + rs) * D + 8 * (pc ^ k_swz<D>(r)), kd + O::rows_per_load * t * L::pitch);
-            load_lds16(vh + (long)(key0 + rs) * D + 8 * (pc ^ v_swz<D>(r)),
-                       kd + L::kBytes + O::rows_per_load * t * L::pitch);
-        }
+    for (int t = 0; t < O::loads; ++t) {
+        load_lds16(rk, off.k[t % O::k_period], base + (t / O::k_period) * 16 * L::pitch, kd + 1024 * t);
+        load_lds16(rv, off.v[t % 2], base + (t / 2) * 16 * L::vPitch, vd + 1024 * t);
     }
 }
 
@@ -170,54 +215,57 @@ __device__ __forceinline__ Entry list_entry(const int32_t *lrow, const float *wr
     return Entry{j, __log2f(wj)};
 }
 
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_fmaxf(a, b); }
+
+// Maximum of x over the lane pair (l, l ^ 32), in every lane.
+__device__ __forceinline__ float half_pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int D, bool full>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void attend_bf16_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
     uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap, float scale_log2)
 {
     using L = Lds<D>;
-    constexpr int KS = D / 16;         // k-steps of S^T = K Q^T
+    constexpr int KS = D / 16;         // k-steps of S^T = K Q^T per 32-key tile
     constexpr int DT = D / 32;         // 32-row tiles of O^T
     constexpr int KT = kSub / 32;      // 32-key tiles per sub-tile
+    constexpr int NK = KT * KS;        // K fragments (QK MFMAs) per sub-tile
+    constexpr int NV = KT * 2 * DT;    // V^T fragments (PV MFMAs) per sub-tile
+    constexpr int PF = 4;              // LDS fragment reads kept in flight ahead of their MFMA
     __shared__ __align__(16) char lds[2 * L::stage];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, half = lane >> 5, grp = lane >> 4, i16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, half = lane >> 5;
     const int blk = xcd_contiguous_id(blockIdx.x, gridDim.x);   // (b*H + h) * NB + query block
     const int qb = blk % NB;
     const long bh = blk / NB;
     const uint16_t *qh = q + bh * N_pad * D;
-    const uint16_t *kh = k + bh * N_pad * D;
-    const uint16_t *vh = v + bh * N_pad * D;
+    const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + bh * N_pad * D, N_pad * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc(vt + bh * N_pad * D, N_pad * D * 2);
 
-    // this lane's two query rows (one per 32-row tile); padding rows read as zero
-    int qrow[QT];
-    bool qvalid[QT];
-    bf16x8 qf[QT][KS];
+    // this lane's query row (the MFMA column l32 of wavefront's tile); padding rows read as zero
+    const int qrow = qb * kBlock + 32 * wave + l32;
+    const bool qvalid = qrow < N;
+    bf16x8 qf[KS];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        qrow[qt] = qb * kBlock + wave * 64 + qt * 32 + l32;
-        qvalid[qt] = qrow[qt] < N;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 raw = make_uint4(0, 0, 0, 0);
-            if (qvalid[qt]) raw = *reinterpret_cast<const uint4 *>(qh + (long)qrow[qt] * D + 16 * ks + 8 * half);
-            qf[qt][ks] = __builtin_bit_cast(bf16x8, raw);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (qvalid) raw = *reinterpret_cast<const uint4 *>(qh + (long)qrow * D + 16 * ks + 8 * half);
+        qf[ks] = __builtin_bit_cast(bf16x8, raw);
     }
 
-    floatx16 o[QT][DT];
-    float m_run[QT], l_run[QT];
+    floatx16 o[DT];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        m_run[qt] = -INFINITY;
-        l_run[qt] = 0.f;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qt][dt][r] = 0.f;
-    }
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m_run = -INFINITY, l_run0 = 0.f, l_run1 = 0.f;
     const floatx16 zero16 = {};
 
     int n_list = NB;
@@ -229,179 +277,172 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         lrow = idx + (long)blk * cap;
         wrow = w + (long)blk * cap;
     }
-    const int n_sub = 2 * n_list;   // sub-tile u = half (u & 1) of list entry u >> 1
 
-    // Per-lane LDS read offsets (compile-time row offsets are added in the loops).
-    // K: row 32kt + l32, logical chunk 2ks + half; row % 16 == l32 % 16.
+    // Per-lane LDS read offsets; tile offsets are immediates.
+    // K fragment i = (kt, ks): row 32kt + l32, logical chunk 2ks + half (row % 16 == l32 % 16).
     int k_rd[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) k_rd[ks] = l32 * L::pitch + 16 * ((2 * ks + half) ^ k_swz<D>(l32));
-    // V (transposing reads): lane group grp addresses row kb + i16/4 (kb a
-    // multiple of 4) at dims 32dt + 16(grp & 1) + 4(i16 % 4), with kb = 32kt +
-    // 16sub + 4half (+8 for the second read), so lane (l32, half) receives dim
-    // 32dt + l32 at the keys its P^T operand holds.
-    int v_rd[DT];
+    // V^T fragment i = (kt, sub, dt): row 32dt + l32 (the dimension), logical chunk
+    // 4kt + 2sub + half, i.e. positions 32kt + 16sub + 8half .. +7; (row / 2) % 8 ==
+    // (l32 / 2) % 8, so the tile row 32dt is an immediate offset.
+    int v_rd[KT * 2];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        const int rr = 4 * half + (i16 >> 2);
-        const int c = 4 * dt + 2 * (grp & 1) + ((i16 & 3) >> 1);
-        v_rd[dt] = L::kBytes + rr * L::pitch + 16 * (c ^ v_swz<D>(rr)) + 8 * (i16 & 1);
-    }
+    for (int i = 0; i < KT * 2; ++i) v_rd[i] = L::kBytes + l32 * L::vPitch + 16 * ((2 * i + half) ^ vt_swz(l32));
+    auto k_frag = [&](const char *st, int i) {
+        return __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const uint4 *>(st + k_rd[i % KS] + (i / KS) * 32 * L::pitch));
+    };
+    auto v_frag = [&](const char *st, int i) {
+        return __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const uint4 *>(st + v_rd[i / DT] + (i % DT) * 32 * L::vPitch));
+    };
 
-    const DmaOffsets<D> dma = dma_offsets<D>(wave, lane);
-    Entry cur{-1, 0.f};
-    if (n_sub > 0) {
-        cur = list_entry<full>(lrow, wrow, 0, NB);
-        if (cur.j >= 0)
-            stage_issue<D>(kh, vh, cur.j * kBlock, min(kSub, N - cur.j * kBlock), lds, wave, lane, dma);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    const Dma<D> dma = dma_offsets<D>(wave, lane);
+    char *const stage0 = lds, *const stage1 = lds + L::stage;
 
-    // Per sub-tile: S^T = K Q^T for both query tiles; s[qt][kt] holds keys
-    // [32kt, 32kt+32) of the sub-tile, lane (l32, half) key 32kt + 8(r/4) + 4half + r%4.
-    floatx16 s[QT][KT];
-    float m_tile[QT];
-    auto scores = [&](const char *stage, int key0) {
+    // One 64-key sub-tile held in LDS stage st (a compile-time offset, so every
+    // LDS read address is a per-lane base plus an immediate); lw = log2 w_j.
+    auto tile = [&](const char *st, int key0, float lw) {
+        // S^T = K Q^T: s[kt] holds keys [32kt, 32kt+32) of the sub-tile; lane
+        // (l32, half) element r is key 32kt + 8(r/4) + 4half + r%4 of query l32.
+        floatx16 s[KT];
+        bf16x8 kf[PF];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            const char *kr = stage + kt * 32 * L::pitch;
+        for (int i = 0; i < PF; ++i) kf[i] = k_frag(st, i);
+        // each read is issued PF MFMAs ahead of its use; the scheduling
+        // fences keep the compiler from pulling reads back next to their use
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kr + k_rd[ks]));
-#pragma unroll
-                for (int qt = 0; qt < QT; ++qt) s[qt][kt] = mfma32(a, qf[qt][ks], ks == 0 ? zero16 : s[qt][kt]);
-            }
+        for (int i = 0; i < NK; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int kt = i / KS, ks = i % KS;
+            s[kt] = mfma32(kf[i % PF], qf[ks], ks == 0 ? zero16 : s[kt]);
+            if (i + PF < NK) kf[i % PF] = k_frag(st, i + PF);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // the PV operands are read while the softmax runs
+        bf16x8 vf[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) vf[i] = v_frag(st, i);
+
         if (key0 + kSub > N) {   // ragged end of the sequence: mask padding keys
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (key0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= N) s[qt][kt][r] = -INFINITY;
-        }
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-            float mx = -INFINITY;
-#pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qt][kt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            m_tile[qt] = fmaf(mx, scale_log2, cur.lw);   // block weight enters as a logit shift
+                for (int r = 0; r < 16; ++r)
+                    if (key0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= N) s[kt][r] = -INFINITY;
         }
-    };
-    // Probabilities against the running max, then O^T += V^T P^T.  MFMA (kt, sub)
-    // contracts the 16 keys held in accumulator rows [8sub, 8sub+8) of tile kt:
-    // for lane half h, element e is key 32kt + 16sub + 8(e/4) + 4h + e%4,
-    // fetched by two transposing reads at rows 32kt + 16sub + 4h (+8).
-    auto accumulate = [&](const char *stage) {
-        // query tile 0's PV MFMAs are independent of tile 1's softmax, so the
-        // two can be co-issued
+        float mx = s[0][0];
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-            bf16x8 pb[KT][2];
-            const float bias = cur.lw - m_run[qt];
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][kt][r], scale_log2, bias));
-                    l_run[qt] += p;
-                    pb[kt][r >> 3][r & 7] = (__bf16)p;
-                }
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const char *vr = stage + v_rd[dt] + (32 * kt + 16 * sub) * L::pitch;
-                        const uint2 a0 = lds_read_tr16(vr);
-                        const uint2 a1 = lds_read_tr16(vr + 8 * L::pitch);
-                        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
-                        o[qt][dt] = mfma32(a, pb[kt][sub], o[qt][dt]);
-                    }
-        }
-    };
-    // Issue the direct loads of sub-tile u + 1 into the other stage.
-    auto prefetch = [&](int u, Entry &nxt) {
-        nxt = cur;
-        if (u + 1 < n_sub) {
-            if (u & 1) nxt = list_entry<full>(lrow, wrow, (u + 1) >> 1, NB);
-            const int nkey0 = nxt.j * kBlock + kSub * ((u + 1) & 1);
-            if (nxt.j >= 0 && nkey0 < N)
-                stage_issue<D>(kh, vh, nkey0, min(kSub, N - nkey0), lds + ((u + 1) & 1) * L::stage, wave, lane, dma);
-        }
-    };
-
-    // The running max only moves when a sub-tile's max exceeds it by more than
-    // the slack (always on the first sub-tile).  Such sub-tiles leave the hot
-    // loop for the rescale below, so inside the hot loop the output
-    // accumulators are touched by MFMAs only.
-    int u = 0;
-    while (u < n_sub) {
-        bool grow = false;
-        Entry nxt;
-        for (; u < n_sub; ++u) {
-            const char *stage = lds + (u & 1) * L::stage;
-            prefetch(u, nxt);
-            const int key0 = cur.j * kBlock + kSub * (u & 1);
-            if (cur.j >= 0 && key0 < N) {   // uniform over the workgroup
-                scores(stage, key0);
-                const bool g0 = m_tile[0] > m_run[0] + kRescaleSlack, g1 = m_tile[1] > m_run[1] + kRescaleSlack;
-                if (__ballot(g0 || g1) != 0) {
-                    grow = true;
-                    break;
-                }
-                accumulate(stage);
-            }
-            cur = nxt;
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-        }
-        if (!grow) break;
-        // rescale (rare): sub-tile u's scores are in s, its successor is in flight
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-            const float m_new = fmaxf(m_run[qt], m_tile[qt]);
-            const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
-            m_run[qt] = m_new;
-            l_run[qt] *= alpha;
+            for (int r = 0; r < 16; ++r)
+                if (kt | r) mx = max2(mx, s[kt][r]);
+        // block weight enters as a logit shift
+        const float m_tile = fmaf(half_pair_max(mx), scale_log2, lw);
+        // lazy rescale: the running max moves only when the tile's max
+        // exceeds it by more than the slack (always on the first tile)
+        if (__ballot(m_tile > m_run + kRescaleSlack) != 0) {
+            asm volatile("s_nop 0");   // keeps this a branch rather than selects
+            const float m_new = max2(m_run, m_tile);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run0 *= alpha;
+            l_run1 *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[qt][dt][r] *= alpha;
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
-        accumulate(lds + (u & 1) * L::stage);
+        // P^T in bf16 straight from the accumulators; the row sum adds the
+        // same rounded probabilities that enter the PV product
+        const float bias = lw - m_run;
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+        bf16x8 pb[KT][2];
+        auto prob = [&](int kt, int r) {
+            pb[kt][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, bias));
+        };
+        auto row_sum = [&](int kt) {
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int h2 = 0; h2 < 4; ++h2) {
+                    const bf16x2 pair = {pb[kt][sub][2 * h2], pb[kt][sub][2 * h2 + 1]};
+                    if (h2 & 1) l_run1 = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run1, false);
+                    else        l_run0 = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run0, false);
+                }
+        };
+#pragma unroll
+        for (int r = 0; r < 16; ++r) prob(0, r);
+        row_sum(0);
+        // O^T += V^T P^T: MFMA (kt, sub, dt) contracts the 16 keys held in
+        // accumulator rows [8sub, 8sub+8) of S^T tile kt against V^T rows
+        // [32dt, 32dt+32); for lane half h, element e is key 32kt + 16sub +
+        // 8(e/4) + 4h + e%4, stored at positions 32kt + 16sub + 8h + e.
+        // Tile 1's probabilities are computed between tile 0's MFMAs.
+        constexpr int per = 16 / (NV / 2);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int ksub = i / DT, dt = i % DT;
+            o[dt] = mfma32(vf[i % PF], pb[ksub >> 1][ksub & 1], o[dt]);
+            if (i + PF < NV) vf[i % PF] = v_frag(st, i + PF);
+            if (i < NV / 2) {
+#pragma unroll
+                for (int e = 0; e < per; ++e) prob(1, per * i + e);
+            }
+            if (i == NV / 2 - 1) row_sum(1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // List entry e: its first half (keys 128j .. 128j+63) sits in stage 0, its
+    // second half in stage 1.  While one half is computed the next half's
+    // direct loads fill the other stage; one barrier per half.
+    Entry cur{-1, 0.f};
+    if (n_list > 0) {
+        cur = list_entry<full>(lrow, wrow, 0, NB);
+        if (cur.j >= 0) stage_issue<D>(rk, rv, cur.j * kBlock, stage0, wave, dma);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int e = 0; e < n_list; ++e) {   // every branch below is uniform over the workgroup
+        const int key_lo = cur.j * kBlock, key_hi = key_lo + kSub;
+        const bool hi = cur.j >= 0 && key_hi < N;   // the second half holds valid keys
+        if (hi) stage_issue<D>(rk, rv, key_hi, stage1, wave, dma);
+        if (cur.j >= 0) tile(stage0, key_lo, cur.lw);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        Entry nxt{-1, 0.f};
+        if (e + 1 < n_list) {
+            nxt = list_entry<full>(lrow, wrow, e + 1, NB);
+            if (nxt.j >= 0) stage_issue<D>(rk, rv, nxt.j * kBlock, stage0, wave, dma);
+        }
+        if (hi) tile(stage1, key_hi, cur.lw);
         cur = nxt;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        ++u;
     }
 
     // normalise and store: lane holds dims dt*32 + 8(r/4) + 4half + r%4 of its query
+    const float l_lane = l_run0 + l_run1;
+    const auto lr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
+    const float lsum = __uint_as_float(lr[0]) + __uint_as_float(lr[1]);
+    const float inv = (lsum > 0.f && qvalid) ? 1.f / lsum : 0.f;
+    uint16_t *orow = out + (bh * N_pad + qrow) * D;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        const float lsum = l_run[qt] + __shfl_xor(l_run[qt], 32, 64);
-        const float inv = (lsum > 0.f && qvalid[qt]) ? 1.f / lsum : 0.f;
-        uint16_t *orow = out + (bh * N_pad + qrow[qt]) * D;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = dt * 32 + 8 * g + 4 * half;
-                __bf16 b0 = (__bf16)(o[qt][dt][4 * g + 0] * inv), b1 = (__bf16)(o[qt][dt][4 * g + 1] * inv);
-                __bf16 b2 = (__bf16)(o[qt][dt][4 * g + 2] * inv), b3 = (__bf16)(o[qt][dt][4 * g + 3] * inv);
-                const uint32_t lo =
-                    (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-                const uint32_t hi =
-                    (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-                *reinterpret_cast<uint2 *>(orow + d) = make_uint2(lo, hi);
-            }
-    }
+        for (int g = 0; g < 4; ++g) {
+            const int d = dt * 32 + 8 * g + 4 * half;
+            __bf16 b0 = (__bf16)(o[dt][4 * g + 0] * inv), b1 = (__bf16)(o[dt][4 * g + 1] * inv);
+            __bf16 b2 = (__bf16)(o[dt][4 * g + 2] * inv), b3 = (__bf16)(o[dt][4 * g + 3] * inv);
+            const uint32_t lo =
+                (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+            const uint32_t hi =
+                (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+            *reinterpret_cast<uint2 *>(orow + d) = make_uint2(lo, hi);
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -502,32 +543,42 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const float *__restrict
 template <bool full>
 hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad,
                            int D, int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap,
-                           void *out, hipStream_t s)
+                           void *vt_ws, void *out, hipStream_t s)
 {
     const dim3 grid((unsigned)((long)B * H * NB)), block(256);
     const float sl2 = scale * kLog2e;
-    if (dtype == kBF16 && D == 128)
-        attend_bf16_kernel<128, full><<<grid, dim3(kThreads), 0, s>>>((const uint16_t *)q, (const uint16_t *)k,
-                                                            (const uint16_t *)v, idx, cnt, w, (uint16_t *)out, N, N_pad,
-                                                            NB, cap, sl2);
-    else if (dtype == kBF16 && D == 64)
-        attend_bf16_kernel<64, full><<<grid, dim3(kThreads), 0, s>>>((const uint16_t *)q, (const uint16_t *)k,
-                                                           (const uint16_t *)v, idx, cnt, w, (uint16_t *)out, N, N_pad,
-                                                           NB, cap, sl2);
-    else if (dtype == kF32 && D == 64)
+    if (dtype == kBF16 && (D == 128 || D == 64)) {
+        const dim3 vt_grid((unsigned)((long)B * H * (N_pad / kSub)));
+        uint16_t *vt = static_cast<uint16_t *>(vt_ws);
+        if (D == 128) {
+            vt_kernel<128><<<vt_grid, block, 0, s>>>((const uint16_t *)v, N, N_pad, vt);
+            attend_bf16_kernel<128, full><<<grid, dim3(kThreads), 0, s>>>(
+                (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, (uint16_t *)out, N, N_pad, NB, cap, sl2);
+        } else {
+            vt_kernel<64><<<vt_grid, block, 0, s>>>((const uint16_t *)v, N, N_pad, vt);
+            attend_bf16_kernel<64, full><<<grid, dim3(kThreads), 0, s>>>(
+                (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, (uint16_t *)out, N, N_pad, NB, cap, sl2);
+        }
+    } else if (dtype == kF32 && D == 64) {
         attend_f32_kernel<64, full><<<grid, block, 0, s>>>((const float *)q, (const float *)k, (const float *)v, idx,
                                                           cnt, w, (float *)out, N, N_pad, NB, cap, sl2);
-    else
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_attend(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad, int D,
                          int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap, bool full,
-                         void *out, hipStream_t s)
+                         void *vt_ws, void *out, hipStream_t s)
 {
-    return full ? launch_attend_t<true>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, out, s)
-                : launch_attend_t<false>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, out, s);
+    return full ? launch_attend_t<true>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, vt_ws, out, s)
+                : launch_attend_t<false>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, vt_ws, out, s);
+}
+
+size_t attend_workspace_bytes(int dtype, int B, int H, int N_pad, int D)
+{
+    return dtype == kBF16 ? (size_t)B * H * N_pad * D * sizeof(uint16_t) : 0;
 }
 
 }  // namespace aba

@@ -22,7 +22,6 @@ namespace {
 // lanes on consecutive rows start on different banks.
 template <typename T, int D> constexpr int row_stride() { return D + 16 / (int)sizeof(T); }
 
-__device__ __forceinline__ float to_f32(uint16_t bits) { return __uint_as_float((uint32_t)bits << 16); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
 template <typename T, int D>

@@ -82,8 +82,11 @@ typedef struct aba_plan {
     int32_t dtype;          /* aba_dtype of q, k, v, out */
     float softmax_scale;    /* s, 1/sqrt(D) unless given */
     int32_t reserved;
-    uint64_t workspace_bytes; /* device scratch aba_score needs when the optional
-                                 outputs are NULL */
+    uint64_t workspace_bytes; /* device scratch for aba_score (when its optional
+                                 outputs are NULL), aba_attend and aba_attend_full;
+                                 every call uses it from offset 0 and only while it
+                                 runs, so one buffer serves all calls ordered on a
+                                 stream (calls that overlap in time need their own) */
 } aba_plan_t;
 
 /* Fill *p for a layer of `batch` x `heads` sequences of `seq_len` valid tokens.
@@ -140,16 +143,19 @@ aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, i
  * i.e. softmax attention with the logits of block j shifted by ln w_j; keys
  * >= N are masked.  List entries outside [0, NB) are skipped; cnt is clamped
  * to [0, list_cap]; a query block with nothing to attend gets zeros.
- *   q, k, v : [B,H,N_pad,D];  idx, cnt, w : as produced by aba_sample
- *   out     : out, [B,H,N_pad,D] in the plan's dtype */
+ *   q, k, v   : [B,H,N_pad,D];  idx, cnt, w : as produced by aba_sample
+ *   out       : out, [B,H,N_pad,D] in the plan's dtype
+ *   workspace : at least p->workspace_bytes of device memory; required for
+ *               ABA_BF16 (it holds a transposed copy of v), may be NULL for
+ *               ABA_F32.  NULL where required -> ABA_E_INVALID. */
 aba_status aba_attend(const aba_plan_t *p, const void *q, const void *k, const void *v, const int32_t *idx,
-                      const int32_t *cnt, const float *w, void *out, hipStream_t stream);
+                      const int32_t *cnt, const float *w, void *out, void *workspace, hipStream_t stream);
 
 /* Dense softmax attention softmax(s q k^T) v over all valid keys, non-causal
- * (the full-attention reference of "Как мерили и что вышло").  Same layout and
- * output convention as aba_attend. */
+ * (the full-attention reference of "Как мерили и что вышло").  Same layout,
+ * workspace rule and output convention as aba_attend. */
 aba_status aba_attend_full(const aba_plan_t *p, const void *q, const void *k, const void *v, void *out,
-                           hipStream_t stream);
+                           void *workspace, hipStream_t stream);
 
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * pointer stays valid until the thread's next aba_* call. */

@@ -51,6 +51,7 @@ def test_plan_fills_the_layer_sizes(aba):
     assert abs(p.softmax_scale - 128 ** -0.5) < 1e-7
     rows = 12 * 256
     assert p.workspace_bytes >= 4 * rows * (8 * 128 + 8 + 128)
+    assert p.workspace_bytes >= 12 * 32768 * 128 * 2          # the transposed copy of v
     p = aba.plan(1, 24, 118800, 128, "bf16", 8, 10, 74)
     assert (p.n_blocks, p.seq_pad) == (929, 118912)
     p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 2, softmax_scale=0.5)
@@ -82,10 +83,20 @@ def test_entry_points_reject_null_pointers_before_launch(aba):
     nul = None
     assert lib.aba_score(pp, nul, nul, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
     assert lib.aba_sample(pp, nul, 1, nul, nul, nul, nul) == aba.ABA_E_INVALID
-    assert lib.aba_attend(pp, nul, nul, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
-    assert lib.aba_attend_full(pp, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
+    assert lib.aba_attend(pp, nul, nul, nul, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
+    assert lib.aba_attend_full(pp, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
     assert b"NULL" in lib.aba_last_error()
-    assert lib.aba_attend_full(None, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
+    assert lib.aba_attend_full(None, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
+
+
+def test_bf16_attention_requires_a_workspace(aba):
+    lib = aba.load_library()
+    p = aba.plan(1, 2, 1024, 128, "bf16", 8, 10, 2)
+    fake = ctypes.c_void_p(1)
+    assert lib.aba_attend(ctypes.byref(p.raw), fake, fake, fake, fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
+    assert b"workspace" in lib.aba_last_error()
+    assert lib.aba_attend_full(ctypes.byref(p.raw), fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
+    assert b"workspace" in lib.aba_last_error()
 
 
 def test_tampered_plan_is_rejected(aba):
@@ -93,7 +104,7 @@ def test_tampered_plan_is_rejected(aba):
     p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 2)
     p.raw.n_blocks = 9          # not what aba_plan computes for 1024 tokens
     fake = ctypes.c_void_p(1)
-    assert lib.aba_attend_full(ctypes.byref(p.raw), fake, fake, fake, fake, None) == aba.ABA_E_INVALID
+    assert lib.aba_attend_full(ctypes.byref(p.raw), fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
     assert b"inconsistent" in lib.aba_last_error()
 
 
