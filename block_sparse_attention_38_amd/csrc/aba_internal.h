@@ -26,8 +26,8 @@ hipError_t launch_sample(const float *scores, int B, int H, int NB, int K, uint6
                          int32_t *cnt, float *w, hipStream_t s);
 hipError_t launch_attend(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad, int D,
                          int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap, bool full,
-                         void *vt_ws, void *out, hipStream_t s);
-// Device bytes launch_attend needs at vt_ws (the V^T staging copy; 0 for fp32).
+                         void *ws, void *out, hipStream_t s);
+// Device bytes launch_attend needs at ws (the V^T copy and the work order; 0 for fp32).
 size_t attend_workspace_bytes(int dtype, int B, int H, int N_pad, int D);
 
 // ---------------------------------------------------------------------------

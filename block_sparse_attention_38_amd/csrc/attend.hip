@@ -36,6 +36,8 @@
 // inputs with head_dim 64.
 #include "aba_internal.h"
 
+#include <type_traits>
+
 namespace aba {
 namespace {
 
@@ -118,43 +120,57 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t *__restrict__ v,
 //       16-lane phase of a 128-bit read touches hit 16 different chunks;
 //   V^T [D][64 keys]:  chunk c of row r at c ^ ((r / 2) % 8); with 128-byte
 //       rows, 16 consecutive rows then cover every bank once.
+// Three K slots and two V^T slots: K sub-tiles are loaded two sub-tiles
+// ahead of their use and V^T tiles one and a half (the PV product comes after
+// the softmax), which hides the latency of key blocks gathered from beyond the
+// L2.  80 KB at D = 128, so two workgroups fill the 160 KB of a CU.
 template <int D> struct Lds {
     static constexpr int pitch = D * 2;        // K row bytes
     static constexpr int chunks = D / 8;
     static constexpr int kBytes = kSub * pitch;
     static constexpr int vPitch = kSub * 2;    // V^T row bytes
     static constexpr int vBytes = D * vPitch;
-    static constexpr int stage = kBytes + vBytes;
+    static constexpr int kSlots = 3, vSlots = 2;
+    static constexpr int bytes = kSlots * kBytes + vSlots * vBytes;
 };
 template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Lds<D>::chunks - 1); }
 __device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Buffer resource over one (b, h) slice of a [.., N_pad, D] bf16 tensor: the
-// loads below address it by byte offset and the hardware range check returns
-// zeros past its end.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t *base, int bytes)
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over one (b, h) slice of a [.., N_pad, D] bf16 tensor
+// (base, stride 0, size in bytes, raw dword access): the loads below address
+// it by byte offset, and the hardware range check returns zeros past its end.
+__device__ __forceinline__ int4v head_rsrc(const uint16_t *base, int bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, bytes, 0x00020000);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return int4v{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)), bytes, 0x00020000};
 }
 
 // Direct copy of 16 bytes per lane from a buffer into LDS: lane L's bytes land
-// at dst + 16 L (dst is wavefront-uniform).  The buffer form (rather than the
-// global one) lets the compiler keep counting LDS reads exactly while these
-// copies are in flight.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, int voff, int soff, char *dst)
+// at dst + 16 L (dst is wavefront-uniform; M0 holds its LDS address).  Issued
+// as inline assembly: the compiler then does not track these LDS writes, and
+// would otherwise wait for every copy in flight before each LDS read it cannot
+// prove disjoint from them.  Ordering is explicit instead: a slot is read only
+// after wait_loads_and_sync has covered the copies into it, and is refilled
+// only after the barrier that follows its last read.
+__device__ __forceinline__ void load_lds16(int4v rs, int voff, int soff, char *dst)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, soff, 0, 0);
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)dst);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
+                 : "memory");
 }
 
-// Direct loads of one 64-key sub-tile (K rows key0 .. key0+63 and the matching
-// V^T tile) into an LDS stage.  Every load moves 1024 bytes: whole K rows (4
-// at D = 128) or 8 V^T rows.  Wavefront w fills its share of both; the
-// per-lane byte offsets inside a sub-tile are precomputed, the sub-tile's own
-// offset is a scalar.  Rows of K past N are read as they are (they lie inside
-// the padded sequence) and masked after the product.  Needs a vmcnt wait and a
-// barrier before the stage is read.
+// Direct loads of one 64-key sub-tile: K rows key0 .. key0+63 into a K slot,
+// the matching V^T tile into a V slot.  Every load moves 1024 bytes: whole K
+// rows (4 at D = 128) or 8 V^T rows.  The per-lane byte offsets inside a
+// sub-tile are precomputed, the sub-tile's own offset is a scalar.  Rows of K
+// past N are read as they are (they lie inside the padded sequence) and
+// masked after the product.  A slot is read only after a vmcnt wait and a
+// barrier.
 template <int D> struct Dma {
     static constexpr int loads = Lds<D>::kBytes / 1024 / kWaves;   // per tensor and wavefront
     static constexpr int k_rows = 1024 / Lds<D>::pitch;             // K rows per load
@@ -183,20 +199,39 @@ __device__ __forceinline__ Dma<D> dma_offsets(int wave, int lane)
     return off;
 }
 
+// Issue the direct loads of K rows key0 .. key0+63 into a K slot, or of the
+// matching V^T tile into a V slot (wavefront w fills its share of either).
 template <int D>
-__device__ __forceinline__ void stage_issue(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int key0, char *stage,
-                                            int wave, const Dma<D> &off)
+__device__ __forceinline__ void issue_k(int4v rk, int key0, char *slot, int wave, const Dma<D> &off)
 {
     using L = Lds<D>;
     using O = Dma<D>;
-    const int base = key0 * D * 2;   // byte offset of the sub-tile in both K and V^T
-    char *kd = stage + O::loads * 1024 * wave;
-    char *vd = stage + L::kBytes + O::loads * 1024 * wave;
+    const int base = key0 * D * 2;
+    char *dst = slot + O::loads * 1024 * wave;
 #pragma unroll
-    for (int t = 0; t < O::loads; ++t) {
-        load_lds16(rk, off.k[t % O::k_period], base + (t / O::k_period) * 16 * L::pitch, kd + 1024 * t);
-        load_lds16(rv, off.v[t % 2], base + (t / 2) * 16 * L::vPitch, vd + 1024 * t);
-    }
+    for (int t = 0; t < O::loads; ++t)
+        load_lds16(rk, off.k[t % O::k_period], base + (t / O::k_period) * 16 * L::pitch, dst + 1024 * t);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_v(int4v rv, int key0, char *slot, int wave, const Dma<D> &off)
+{
+    using L = Lds<D>;
+    using O = Dma<D>;
+    const int base = key0 * D * 2;   // a V^T tile sits where its keys' rows of v do
+    char *dst = slot + O::loads * 1024 * wave;
+#pragma unroll
+    for (int t = 0; t < O::loads; ++t) load_lds16(rv, off.v[t % 2], base + (t / 2) * 16 * L::vPitch, dst + 1024 * t);
+}
+
+// Wait until at most n of this wavefront's direct loads are in flight (they
+// complete in issue order), then meet the other wavefronts: their loads up to
+// the same point are then in LDS as well.  A bare s_barrier: the workgroup
+// fence of __syncthreads would also wait for the loads that are meant to stay
+// in flight.  Every LDS read before the barrier has been consumed by then.
+template <int n> __device__ __forceinline__ void wait_loads_and_sync()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
 }
 
 // One list entry: key block j with log2 weight lw; j < 0 marks an entry to skip.
@@ -215,6 +250,95 @@ __device__ __forceinline__ Entry list_entry(const int32_t *lrow, const float *wr
     return Entry{j, __log2f(wj)};
 }
 
+// ---------------------------------------------------------------------------
+// Work order.  The hardware hands workgroup i to XCD i % 8 and each XCD starts
+// its workgroups in increasing i; xcd_contiguous_id turns that into one
+// contiguous range of query blocks per XCD.  A query block's cost is its kept
+// count, which varies several-fold between blocks, so every range is
+// reordered by decreasing count (longest first), which keeps the tail of the
+// launch short.  One workgroup per XCD range: an LDS histogram of the counts,
+// a scan over the counts from high to low, and an atomic scatter.  The order
+// inside one count is arbitrary; results do not depend on it (each query
+// block is computed by one workgroup, independently of the others).
+// ---------------------------------------------------------------------------
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ cnt, int G, int cap,
+                                                             int32_t *__restrict__ order)
+{
+    __shared__ int bins[kMaxBlocks + 1];
+    __shared__ int part[kOrderThreads / 64];
+    constexpr int kXcds = 8;
+    const int x = blockIdx.x, per = G / kXcds, extra = G % kXcds;
+    const int start = x * per + (x < extra ? x : extra), n = per + (x < extra ? 1 : 0);
+    const int nb = cap + 1, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto key = [&](int i) {   // count rank: 0 for the largest possible count
+        const int c = cnt[start + i];
+        return cap - (c < 0 ? 0 : (c > cap ? cap : c));
+    };
+    for (int b = tid; b < nb; b += kOrderThreads) bins[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kOrderThreads) atomicAdd(&bins[key(i)], 1);
+    __syncthreads();
+    // exclusive scan of bins[0 .. nb): each thread owns a run of consecutive bins
+    constexpr int kRun = (kMaxBlocks + 1 + kOrderThreads - 1) / kOrderThreads;
+    int run[kRun], sum = 0;
+#pragma unroll
+    for (int r = 0; r < kRun; ++r) {
+        const int b = tid * kRun + r;
+        run[r] = b < nb ? bins[b] : 0;
+        sum += run[r];
+    }
+    int incl = sum;   // inclusive scan of the per-thread sums: wavefront, then across wavefronts
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) part[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int v = 0; v < wave; ++v) base += part[v];
+    int off = base + incl - sum;
+#pragma unroll
+    for (int r = 0; r < kRun; ++r) {
+        const int b = tid * kRun + r;
+        if (b < nb) bins[b] = off;
+        off += run[r];
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kOrderThreads) order[start + atomicAdd(&bins[key(i)], 1)] = start + i;
+}
+
+// The list of a sparse row is read 64 entries at a time into lane-distributed
+// registers (lane i: entry 64m + i, already validated and turned into log2 w),
+// and an entry is taken with v_readlane: no memory access per entry, so no
+// scalar load shares the LDS wait counter with the fragment reads.
+struct Window {
+    int j;
+    float lw;
+};
+
+template <bool full>
+__device__ __forceinline__ Window load_window(const int32_t *lrow, const float *wrow, int m, int n_list, int NB, int lane)
+{
+    const int e = 64 * m + lane;
+    Window win{-1, 0.f};
+    if (!full && e < n_list) {
+        const Entry en = list_entry<false>(lrow, wrow, e, NB);
+        win.j = en.j;
+        win.lw = en.lw;
+    }
+    return win;
+}
+
+template <bool full> __device__ __forceinline__ Entry window_entry(const Window &win, int e)
+{
+    if (full) return Entry{e, 0.f};
+    return Entry{__builtin_amdgcn_readlane(win.j, e & 63),
+                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(win.lw), e & 63))};
+}
+
 __device__ __forceinline__ float max2(float a, float b) { return __builtin_fmaxf(a, b); }
 
 // Maximum of x over the lane pair (l, l ^ 32), in every lane.
@@ -228,7 +352,8 @@ template <int D, bool full>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
-    uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap, float scale_log2)
+    const int32_t *__restrict__ order, uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap,
+    float scale_log2)
 {
     using L = Lds<D>;
     constexpr int KS = D / 16;         // k-steps of S^T = K Q^T per 32-key tile
@@ -237,17 +362,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int NK = KT * KS;        // K fragments (QK MFMAs) per sub-tile
     constexpr int NV = KT * 2 * DT;    // V^T fragments (PV MFMAs) per sub-tile
     constexpr int PF = 4;              // LDS fragment reads kept in flight ahead of their MFMA
-    __shared__ __align__(16) char lds[2 * L::stage];
+    // every slot is a separate LDS object, so that the compiler can tell the
+    // slot being read from the slots whose direct loads are still in flight
+    __shared__ __align__(16) char ks0[L::kBytes], ks1[L::kBytes], ks2[L::kBytes];
+    __shared__ __align__(16) char vs0[L::vBytes], vs1[L::vBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, half = lane >> 5;
-    const int blk = xcd_contiguous_id(blockIdx.x, gridDim.x);   // (b*H + h) * NB + query block
+    // (b*H + h) * NB + query block; sparse lists run longest first within each XCD
+    const int slot = xcd_contiguous_id(blockIdx.x, gridDim.x);
+    const int blk = full ? slot : order[slot];
     const int qb = blk % NB;
     const long bh = blk / NB;
     const uint16_t *qh = q + bh * N_pad * D;
-    const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + bh * N_pad * D, N_pad * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = head_rsrc(vt + bh * N_pad * D, N_pad * D * 2);
+    const int4v rk = head_rsrc(k + bh * N_pad * D, N_pad * D * 2);
+    const int4v rv = head_rsrc(vt + bh * N_pad * D, N_pad * D * 2);
 
     // this lane's query row (the MFMA column l32 of wavefront's tile); padding rows read as zero
     const int qrow = qb * kBlock + 32 * wave + l32;
@@ -288,28 +418,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // (l32 / 2) % 8, so the tile row 32dt is an immediate offset.
     int v_rd[KT * 2];
 #pragma unroll
-    for (int i = 0; i < KT * 2; ++i) v_rd[i] = L::kBytes + l32 * L::vPitch + 16 * ((2 * i + half) ^ vt_swz(l32));
-    auto k_frag = [&](const char *st, int i) {
+    for (int i = 0; i < KT * 2; ++i) v_rd[i] = l32 * L::vPitch + 16 * ((2 * i + half) ^ vt_swz(l32));
+    auto k_frag = [&](const char *st, int i) __attribute__((always_inline)) {
         return __builtin_bit_cast(bf16x8,
                                   *reinterpret_cast<const uint4 *>(st + k_rd[i % KS] + (i / KS) * 32 * L::pitch));
     };
-    auto v_frag = [&](const char *st, int i) {
+    auto v_frag = [&](const char *st, int i) __attribute__((always_inline)) {
         return __builtin_bit_cast(bf16x8,
                                   *reinterpret_cast<const uint4 *>(st + v_rd[i / DT] + (i % DT) * 32 * L::vPitch));
     };
 
     const Dma<D> dma = dma_offsets<D>(wave, lane);
-    char *const stage0 = lds, *const stage1 = lds + L::stage;
 
-    // One 64-key sub-tile held in LDS stage st (a compile-time offset, so every
-    // LDS read address is a per-lane base plus an immediate); lw = log2 w_j.
-    auto tile = [&](const char *st, int key0, float lw) {
+    // One 64-key sub-tile held in K slot kst and V slot vst (compile-time
+    // offsets, so every LDS read address is a per-lane base plus an
+    // immediate); lw = log2 w_j.
+    auto tile = [&](const char *kst, const char *vst, int key0, float lw) __attribute__((always_inline)) {
         // S^T = K Q^T: s[kt] holds keys [32kt, 32kt+32) of the sub-tile; lane
         // (l32, half) element r is key 32kt + 8(r/4) + 4half + r%4 of query l32.
         floatx16 s[KT];
         bf16x8 kf[PF];
 #pragma unroll
-        for (int i = 0; i < PF; ++i) kf[i] = k_frag(st, i);
+        for (int i = 0; i < PF; ++i) kf[i] = k_frag(kst, i);
         // each read is issued PF MFMAs ahead of its use; the scheduling
         // fences keep the compiler from pulling reads back next to their use
 #pragma unroll
@@ -317,13 +447,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             __builtin_amdgcn_sched_barrier(0);
             const int kt = i / KS, ks = i % KS;
             s[kt] = mfma32(kf[i % PF], qf[ks], ks == 0 ? zero16 : s[kt]);
-            if (i + PF < NK) kf[i % PF] = k_frag(st, i + PF);
+            if (i + PF < NK) kf[i % PF] = k_frag(kst, i + PF);
         }
         __builtin_amdgcn_sched_barrier(0);
         // the PV operands are read while the softmax runs
         bf16x8 vf[PF];
 #pragma unroll
-        for (int i = 0; i < PF; ++i) vf[i] = v_frag(st, i);
+        for (int i = 0; i < PF; ++i) vf[i] = v_frag(vst, i);
 
         if (key0 + kSub > N) {   // ragged end of the sequence: mask padding keys
 #pragma unroll
@@ -359,10 +489,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const float bias = lw - m_run;
         const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
         bf16x8 pb[KT][2];
-        auto prob = [&](int kt, int r) {
+        auto prob = [&](int kt, int r) __attribute__((always_inline)) {
             pb[kt][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, bias));
         };
-        auto row_sum = [&](int kt) {
+        auto row_sum = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -386,7 +516,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             __builtin_amdgcn_sched_barrier(0);
             const int ksub = i / DT, dt = i % DT;
             o[dt] = mfma32(vf[i % PF], pb[ksub >> 1][ksub & 1], o[dt]);
-            if (i + PF < NV) vf[i % PF] = v_frag(st, i + PF);
+            if (i + PF < NV) vf[i % PF] = v_frag(vst, i + PF);
             if (i < NV / 2) {
 #pragma unroll
                 for (int e = 0; e < per; ++e) prob(1, per * i + e);
@@ -396,32 +526,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // List entry e: its first half (keys 128j .. 128j+63) sits in stage 0, its
-    // second half in stage 1.  While one half is computed the next half's
-    // direct loads fill the other stage; one barrier per half.
-    Entry cur{-1, 0.f};
-    if (n_list > 0) {
-        cur = list_entry<full>(lrow, wrow, 0, NB);
-        if (cur.j >= 0) stage_issue<D>(rk, rv, cur.j * kBlock, stage0, wave, dma);
+    // Sub-tile u is half u % 2 of list entry u / 2; its K sits in K slot u % 3,
+    // its V^T in V slot u % 2.  Iteration u issues V^T(u + 1) and then K(u + 2),
+    // computes u, and waits for all but the K(u + 2) loads: K(u + 1) and
+    // V^T(u + 1) are then in LDS.  The entry loop is unrolled three times, so
+    // every slot is a compile-time offset.  Branches are uniform over the
+    // workgroup; invalid entries and sub-tiles past N load and compute nothing.
+    constexpr int KL = Dma<D>::loads;
+    auto kptr = [&](int sl) __attribute__((always_inline)) { return sl == 0 ? ks0 : (sl == 1 ? ks1 : ks2); };
+    auto vptr = [&](int sl) __attribute__((always_inline)) { return sl == 0 ? vs0 : vs1; };
+    const Entry none{-1, 0.f};
+    Window win = load_window<full>(lrow, wrow, 0, n_list, NB, lane);
+    Entry ce = n_list > 0 ? window_entry<full>(win, 0) : none;
+    Entry ne = n_list > 1 ? window_entry<full>(win, 1) : none;
+    auto hi_valid = [&](const Entry &en) __attribute__((always_inline)) { return en.j >= 0 && en.j * kBlock + kSub < N; };
+    if (ce.j >= 0) {
+        issue_k<D>(rk, ce.j * kBlock, kptr(0), wave, dma);
+        issue_v<D>(rv, ce.j * kBlock, vptr(0), wave, dma);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int e = 0; e < n_list; ++e) {   // every branch below is uniform over the workgroup
-        const int key_lo = cur.j * kBlock, key_hi = key_lo + kSub;
-        const bool hi = cur.j >= 0 && key_hi < N;   // the second half holds valid keys
-        if (hi) stage_issue<D>(rk, rv, key_hi, stage1, wave, dma);
-        if (cur.j >= 0) tile(stage0, key_lo, cur.lw);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        Entry nxt{-1, 0.f};
-        if (e + 1 < n_list) {
-            nxt = list_entry<full>(lrow, wrow, e + 1, NB);
-            if (nxt.j >= 0) stage_issue<D>(rk, rv, nxt.j * kBlock, stage0, wave, dma);
-        }
-        if (hi) tile(stage1, key_hi, cur.lw);
-        cur = nxt;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+    if (hi_valid(ce)) issue_k<D>(rk, ce.j * kBlock + kSub, kptr(1), wave, dma);
+    // settle the Q loads here, once, rather than before every tile of the loop
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    if (hi_valid(ce)) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
+    auto step = [&](auto e3c, int e) __attribute__((always_inline)) {
+        constexpr int E3 = decltype(e3c)::value;             // e % 3
+        constexpr int k0 = (2 * E3) % 3, k1 = (2 * E3 + 1) % 3;   // K slots of this entry's halves
+        const int e2 = e + 2;
+        if (!full && e2 < n_list && (e2 & 63) == 0) win = load_window<full>(lrow, wrow, e2 >> 6, n_list, NB, lane);
+        const Entry nn = e2 < n_list ? window_entry<full>(win, e2) : none;
+        const bool ce_hi = hi_valid(ce), ne_ok = ne.j >= 0, ne_hi = hi_valid(ne);
+        // first half: V^T of the second half, K of the next entry's first half
+        if (ce_hi) issue_v<D>(rv, ce.j * kBlock + kSub, vptr(1), wave, dma);
+        if (ne_ok) issue_k<D>(rk, ne.j * kBlock, kptr((2 * E3 + 2) % 3), wave, dma);
+        if (ce.j >= 0) tile(kptr(k0), vptr(0), ce.j * kBlock, ce.lw);
+        if (ne_ok) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
+        // second half: V^T of the next entry's first half, K of its second half
+        if (ne_ok) issue_v<D>(rv, ne.j * kBlock, vptr(0), wave, dma);
+        if (ne_hi) issue_k<D>(rk, ne.j * kBlock + kSub, kptr((2 * E3 + 3) % 3), wave, dma);
+        if (ce_hi) tile(kptr(k1), vptr(1), ce.j * kBlock + kSub, ce.lw);
+        if (ne_hi) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
+        ce = ne;
+        ne = nn;
+    };
+    for (int e = 0; e < n_list; e += 3) {
+        step(std::integral_constant<int, 0>{}, e);
+        if (e + 1 >= n_list) break;
+        step(std::integral_constant<int, 1>{}, e + 1);
+        if (e + 2 >= n_list) break;
+        step(std::integral_constant<int, 2>{}, e + 2);
     }
 
     // normalise and store: lane holds dims dt*32 + 8(r/4) + 4half + r%4 of its query
@@ -540,24 +693,33 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const float *__restrict
 
 }  // namespace
 
+// V^T copy, then the work order (sparse lists only), in the workspace.
+size_t vt_bytes(int B, int H, int N_pad, int D) { return ((size_t)B * H * N_pad * D * sizeof(uint16_t) + 255) & ~(size_t)255; }
+
 template <bool full>
 hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad,
                            int D, int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap,
-                           void *vt_ws, void *out, hipStream_t s)
+                           void *ws, void *out, hipStream_t s)
 {
-    const dim3 grid((unsigned)((long)B * H * NB)), block(256);
+    const int G = B * H * NB;
+    const dim3 grid((unsigned)G), block(256);
     const float sl2 = scale * kLog2e;
     if (dtype == kBF16 && (D == 128 || D == 64)) {
         const dim3 vt_grid((unsigned)((long)B * H * (N_pad / kSub)));
-        uint16_t *vt = static_cast<uint16_t *>(vt_ws);
+        uint16_t *vt = static_cast<uint16_t *>(ws);
+        int32_t *order = nullptr;
+        if (!full) {
+            order = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + vt_bytes(B, H, N_pad, D));
+            order_kernel<<<dim3(8), dim3(kOrderThreads), 0, s>>>(cnt, G, cap, order);
+        }
         if (D == 128) {
             vt_kernel<128><<<vt_grid, block, 0, s>>>((const uint16_t *)v, N, N_pad, vt);
             attend_bf16_kernel<128, full><<<grid, dim3(kThreads), 0, s>>>(
-                (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, (uint16_t *)out, N, N_pad, NB, cap, sl2);
+                (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, order, (uint16_t *)out, N, N_pad, NB, cap, sl2);
         } else {
             vt_kernel<64><<<vt_grid, block, 0, s>>>((const uint16_t *)v, N, N_pad, vt);
             attend_bf16_kernel<64, full><<<grid, dim3(kThreads), 0, s>>>(
-                (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, (uint16_t *)out, N, N_pad, NB, cap, sl2);
+                (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, order, (uint16_t *)out, N, N_pad, NB, cap, sl2);
         }
     } else if (dtype == kF32 && D == 64) {
         attend_f32_kernel<64, full><<<grid, block, 0, s>>>((const float *)q, (const float *)k, (const float *)v, idx,
@@ -570,15 +732,16 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
 
 hipError_t launch_attend(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad, int D,
                          int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap, bool full,
-                         void *vt_ws, void *out, hipStream_t s)
+                         void *ws, void *out, hipStream_t s)
 {
-    return full ? launch_attend_t<true>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, vt_ws, out, s)
-                : launch_attend_t<false>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, vt_ws, out, s);
+    return full ? launch_attend_t<true>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, ws, out, s)
+                : launch_attend_t<false>(q, k, v, dtype, B, H, N, N_pad, D, NB, scale, idx, cnt, w, cap, ws, out, s);
 }
 
 size_t attend_workspace_bytes(int dtype, int B, int H, int N_pad, int D)
 {
-    return dtype == kBF16 ? (size_t)B * H * N_pad * D * sizeof(uint16_t) : 0;
+    if (dtype != kBF16) return 0;
+    return vt_bytes(B, H, N_pad, D) + (size_t)B * H * (N_pad / kBlock) * sizeof(int32_t);
 }
 
 }  // namespace aba
