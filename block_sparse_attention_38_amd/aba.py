@@ -11,6 +11,7 @@ Steps (AB-Attention page, section "Три приёма AB-Attention"):
     sample(plan, scores, seed)     SIP sampling plan (idx, cnt, w) -> aba_sample
     attend(plan, q, k, v, ...)     HT-weighted block-sparse attn   -> aba_attend
     attend_full(plan, q, k, v)     dense attention                 -> aba_attend_full
+    block_mass(plan, q, k, items)  attention mass per key block    -> aba_block_mass (diagnostic)
 """
 from __future__ import annotations
 
@@ -50,7 +51,8 @@ class PlanStruct(ctypes.Structure):
     ]
 
 
-EXPORTS = ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full", "aba_last_error", "aba_version")
+EXPORTS = ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full", "aba_block_mass", "aba_last_error",
+           "aba_version")
 
 _lib = None
 
@@ -71,7 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.aba_sample.argtypes = [PP, P, u64, P, P, P, P]
     lib.aba_attend.argtypes = [PP, P, P, P, P, P, P, P, P, P]
     lib.aba_attend_full.argtypes = [PP, P, P, P, P, P, P]
-    for name in ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full"):
+    lib.aba_block_mass.argtypes = [PP, P, P, P, ctypes.c_int32, P, P]
+    for name in ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full", "aba_block_mass"):
         getattr(lib, name).restype = ctypes.c_int
     lib.aba_last_error.argtypes = []
     lib.aba_last_error.restype = ctypes.c_char_p
@@ -220,6 +223,19 @@ def attend_full(p: Plan, q, k, v, *, out=None, ws=None) -> torch.Tensor:
     _check(load_library().aba_attend_full(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
                                           _stream()))
     return out
+
+
+def block_mass(p: Plan, q, k, items) -> torch.Tensor:
+    """aba_block_mass: dense attention mass per key block for the listed (b, h, query block)
+    items, float32 [n_items, NB]; each row sums to one."""
+    dev = q.device
+    _need(q, "q", _qkv_shape(p), p.torch_dtype, dev)
+    _need(k, "k", _qkv_shape(p), p.torch_dtype, dev)
+    it = torch.as_tensor(items, dtype=torch.int32).reshape(-1, 3).contiguous().to(dev)
+    mass = torch.empty(it.shape[0], p.n_blocks, dtype=torch.float32, device=dev)
+    _check(load_library().aba_block_mass(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(it), it.shape[0], _ptr(mass),
+                                         _stream()))
+    return mass
 
 
 def layer(p: Plan, q, k, v, seed: int, *, ws=None):

@@ -27,6 +27,8 @@ hipError_t launch_sample(const float *scores, int B, int H, int NB, int K, uint6
 hipError_t launch_attend(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad, int D,
                          int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap, bool full,
                          void *ws, void *out, hipStream_t s);
+hipError_t launch_block_mass(const void *q, const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB,
+                             float scale, const int32_t *items, int n_items, float *mass, hipStream_t s);
 // Device bytes launch_attend needs at ws (the V^T copy and the work order; 0 for fp32).
 size_t attend_workspace_bytes(int dtype, int B, int H, int N_pad, int D);
 

@@ -195,6 +195,21 @@ aba_status aba_attend_full(const aba_plan_t *p, const void *q, const void *k, co
                       "attend_full launch");
 }
 
+aba_status aba_block_mass(const aba_plan_t *p, const void *q, const void *k, const int32_t *items, int32_t n_items,
+                          float *mass, hipStream_t stream)
+{
+    g_last_error.clear();
+    aba_status st = check_plan(p);
+    if (st != ABA_OK) return st;
+    if (p->dtype != ABA_BF16) return fail(ABA_E_UNSUPPORTED, "aba_block_mass takes bf16 inputs");
+    if (n_items < 0) return fail(ABA_E_INVALID, "n_items must be >= 0");
+    if (n_items == 0) return ABA_OK;
+    if (!q || !k || !items || !mass) return fail(ABA_E_INVALID, "q, k, items and mass must be non-NULL");
+    return hip_status(aba::launch_block_mass(q, k, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad, p->head_dim,
+                                             p->n_blocks, p->softmax_scale, items, n_items, mass, stream),
+                      "block_mass launch");
+}
+
 const char *aba_last_error(void) { return g_last_error.c_str(); }
 
 const char *aba_version(void) { return "aba 0.1.0 (gfx950)"; }

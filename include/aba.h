@@ -157,6 +157,22 @@ aba_status aba_attend(const aba_plan_t *p, const void *q, const void *k, const v
 aba_status aba_attend_full(const aba_plan_t *p, const void *q, const void *k, const void *v, void *out,
                            void *workspace, hipStream_t stream);
 
+/* Dense attention mass per key block, for judging a block selection (IBCS
+ * paragraph and the opening of "Три приёма AB-Attention": the share of the
+ * attention a selection keeps).  For each listed query block b' with n valid
+ * query rows:
+ *     mass[item][j] = (1/n) sum_i sum_{t in key block j, t < N} softmax_t(s q_i . k_t)
+ * so each row sums to one; its K largest entries sum to the ideal top-K mass.
+ * ABA_BF16 only (ABA_E_UNSUPPORTED otherwise).  A diagnostic, off the attention
+ * path: it costs two dense QK^T passes per listed query block.
+ *   q, k    : [B,H,N_pad,D]
+ *   items   : device int32 [n_items][3] of (b, h, query block); an item outside
+ *             the layer yields a row of zeros
+ *   n_items : >= 0 (0 launches nothing)
+ *   mass    : out, device float32 [n_items][NB] */
+aba_status aba_block_mass(const aba_plan_t *p, const void *q, const void *k, const int32_t *items, int32_t n_items,
+                          float *mass, hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * pointer stays valid until the thread's next aba_* call. */
 const char *aba_last_error(void);

@@ -89,6 +89,17 @@ def test_entry_points_reject_null_pointers_before_launch(aba):
     assert lib.aba_attend_full(None, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
 
 
+def test_block_mass_checks_dtype_and_pointers(aba):
+    lib = aba.load_library()
+    fake = ctypes.c_void_p(1)
+    p32 = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 2)
+    assert lib.aba_block_mass(ctypes.byref(p32.raw), fake, fake, fake, 1, fake, None) == aba.ABA_E_UNSUPPORTED
+    p = aba.plan(1, 2, 1024, 128, "bf16", 8, 10, 2)
+    assert lib.aba_block_mass(ctypes.byref(p.raw), fake, fake, None, 1, fake, None) == aba.ABA_E_INVALID
+    assert lib.aba_block_mass(ctypes.byref(p.raw), fake, fake, fake, -1, fake, None) == aba.ABA_E_INVALID
+    assert lib.aba_block_mass(ctypes.byref(p.raw), None, None, None, 0, None, None) == aba.ABA_OK   # nothing to do
+
+
 def test_bf16_attention_requires_a_workspace(aba):
     lib = aba.load_library()
     p = aba.plan(1, 2, 1024, 128, "bf16", 8, 10, 2)
