@@ -9,10 +9,14 @@ inputs resident in HBM:
     aba_attend (block-sparse flash attention with inverse-inclusion weights)
 
 The workload is the 32K-token single video DiT layer (batch 1, 12 heads,
-head_dim 128, bf16, 21x30x52 latent grid, 10% key-block density).  ``value`` is
-the effective (dense-equivalent) throughput 4*B*H*N^2*D / step time.  Printed as
-one JSON line, with the roofline of the dominant kernel (aba_attend, measured
-with HIP events on the stream it runs on) and the CPU oracle timed on a bounded
+head_dim 128, bf16, 21x30x52 latent grid, 10% key-block density); the steps
+cycle through three seeded input sets so that no step finds its q and k in the
+MALL.  ``value`` is the effective (dense-equivalent) throughput 4*B*H*N^2*D /
+step time.  Printed as one JSON line, with the roofline of the dominant call
+(aba_attend, measured with HIP events on the stream it runs on), untimed
+selection diagnostics (dense attention mass kept by the ideal, IBCS, mean-pool
+and sampled selections on sampled query blocks, and the attention error of the
+sampled lists against hard top-K lists), and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload single_layer]
@@ -136,6 +140,66 @@ def cpu_baseline(w, p, q, k, v, seed: int, target_s: float):
     }
 
 
+def selection_diagnostics(w, p, qkv, lists, ws, n_blocks: int):
+    """How much dense attention mass the selections keep, on sampled query blocks
+    (dense mass per key block from aba_block_mass), and the attention error of the
+    sampled lists against hard top-K lists of the same scores (outputs of
+    aba_attend against aba_attend_full).  Untimed."""
+    qd, kd, vd = qkv
+    (scores, (idx, cnt, wt)) = lists
+    B, H, NB, K = p.batch, p.heads, p.n_blocks, p.budget
+    rng = np.random.default_rng(5)
+    items = sorted({(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(NB))) for _ in range(4 * n_blocks)})
+    items = items[:max(n_blocks, 32)]
+    mass = aba.block_mass(p, qd, kd, items).double().cpu().numpy()                 # [n, NB]
+    it = np.array(items)
+    ideal = np.sort(mass, axis=1)[:, ::-1][:, :K].sum(axis=1)
+
+    def top_k_mass(sc):
+        top = np.argsort(-sc[it[:, 0], it[:, 1], it[:, 2]], axis=1, kind="stable")[:, :K]
+        return np.take_along_axis(mass, top, axis=1).sum(axis=1)
+
+    ibcs = top_k_mass(scores.double().cpu().numpy())
+    p1 = aba.plan(B, H, w.seq_len, w.head_dim, w.dtype, 1, p.kmeans_iters, K)      # one cluster: mean-pool scorer
+    meanpool = top_k_mass(aba.score(p1, qd, kd, ws=aba.workspace(p1, qd.device)).double().cpu().numpy())
+    idx_h, cnt_h, wt_h = (x.cpu().numpy() for x in (idx, cnt, wt))
+    kept, ht = [], []
+    for r, (b, h, qb) in enumerate(items):
+        c = int(cnt_h[b, h, qb])
+        sel = idx_h[b, h, qb, :c]
+        kept.append(mass[r, sel].sum())
+        ht.append((mass[r, sel] * wt_h[b, h, qb, :c]).sum())
+    # hard top-K lists of the same scores, ascending, unit weights
+    top = torch.topk(scores, K, dim=-1).indices.sort(dim=-1).values.to(torch.int32)
+    idx_t = torch.zeros_like(idx)
+    idx_t[..., :K] = top
+    cnt_t = torch.full_like(cnt, K)
+    wt_t = torch.ones_like(wt)
+    dense = aba.attend_full(p, qd, kd, vd, ws=ws)
+    o_sip = aba.attend(p, qd, kd, vd, idx, cnt, wt, ws=ws)
+    o_top = aba.attend(p, qd, kd, vd, idx_t, cnt_t, wt_t, ws=ws)
+    torch.cuda.synchronize()
+
+    def rel_err(o):
+        e = []
+        for b, h, qb in items:
+            n = min(128, w.seq_len - 128 * qb)
+            ref = dense[b, h, 128 * qb:128 * qb + n].float()
+            e.append(((o[b, h, 128 * qb:128 * qb + n].float() - ref).norm() / ref.norm()).item())
+        return float(np.mean(e))
+
+    return {
+        "query_blocks": len(items),
+        "ideal_topk_mass": float(ideal.mean()),
+        "ibcs_topk_mass": float(ibcs.mean()),
+        "meanpool_topk_mass": float(meanpool.mean()),
+        "recall_gap": {"ibcs": float((ideal - ibcs).mean()), "meanpool": float((ideal - meanpool).mean())},
+        "sip_kept_mass": float(np.mean(kept)),
+        "sip_ht_weighted_mass": float(np.mean(ht)),
+        "attention_rel_err_vs_dense": {"sip": rel_err(o_sip), "hard_topk": rel_err(o_top)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +212,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--input-sets", type=int, default=3, help="input sets the steps cycle through")
+    ap.add_argument("--no-diagnostics", action="store_true")
+    ap.add_argument("--diag-blocks", type=int, default=32, help="sampled query blocks for the selection diagnostics")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -164,10 +231,12 @@ def main():
     density = w.densities[0] if args.density is None else args.density
     dev = torch.device("cuda:0")
     log(f"[bench] workload {w.name}: {w.description}; density {density}")
+    # Several input sets, used in turn: one set's q and k (201 MB at the single
+    # layer) would otherwise stay in the 256 MB MALL from one step to the next.
     t0 = time.perf_counter()
-    q, k, v = synth.make_inputs(w, seed=1001)
-    qd, kd, vd = (x.to(dev) for x in (q, k, v))
-    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+    host_sets = [synth.make_inputs(w, seed=1001 + 10 * i) for i in range(args.input_sets)]
+    sets = [tuple(x.to(dev) for x in hs) for hs in host_sets]
+    log(f"[bench] {len(sets)} input sets ready in {time.perf_counter() - t0:.1f} s")
 
     p = aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, CLUSTERS, KMEANS_ITERS, w.budget(density))
     B, H, NB, cap, D = p.batch, p.heads, p.n_blocks, p.list_cap, p.head_dim
@@ -176,32 +245,34 @@ def main():
     lists = (torch.empty(B, H, NB, cap, dtype=torch.int32, device=dev),
              torch.empty(B, H, NB, dtype=torch.int32, device=dev),
              torch.empty(B, H, NB, cap, dtype=torch.float32, device=dev))
-    out = torch.empty_like(qd)
+    out = torch.empty_like(sets[0][0])
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(i, ev=None):
+        qd, kd, vd = sets[i % len(sets)]
+        seed = args.seed + i % len(sets)
         if ev is not None:
             ev[0].record(stream)
         aba.score(p, qd, kd, out=scores, ws=ws)
         if ev is not None:
             ev[1].record(stream)
-        aba.sample(p, scores, args.seed, out=lists)
+        aba.sample(p, scores, seed, out=lists)
         if ev is not None:
             ev[2].record(stream)
         aba.attend(p, qd, kd, vd, *lists, out=out, ws=ws)
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for s in range(args.steps):
-        step(evs[s])
+    for i in range(args.steps):
+        step(i, evs[i])
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
@@ -211,13 +282,23 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (score {score_ms:.3f}, sample {sample_ms:.3f}, "
         f"attend {attend_ms:.3f})")
 
-    idx, cnt, wt = (x.cpu().numpy() for x in lists)
-    kflops = kept_flops(p, cnt, idx)
+    # kept work per call, averaged over the input sets the steps cycle through
+    kflops_sets, dens_sets, set_lists = [], [], []
+    for i in range(len(sets)):
+        qd, kd, vd = sets[i]
+        s_i = aba.score(p, qd, kd, ws=ws)
+        l_i = aba.sample(p, s_i, args.seed + i)
+        idx, cnt, wt = (x.cpu().numpy() for x in l_i)
+        kflops_sets.append(kept_flops(p, cnt, idx))
+        dens_sets.append(float(cnt.mean() / NB))
+        set_lists.append((s_i, l_i))
+    kflops = float(np.mean(kflops_sets))
     dense_flops = w.dense_flops
-    realised_density = float(cnt.mean() / NB)
+    realised_density = float(np.mean(dens_sets))
 
     dense_ms = None
     if not args.no_dense:
+        qd, kd, vd = sets[0]
         aba.attend_full(p, qd, kd, vd, out=out, ws=ws)
         torch.cuda.synchronize()
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -228,6 +309,11 @@ def main():
         torch.cuda.synchronize()
         dense_ms = d0.elapsed_time(d1) / args.dense_reps
         log(f"[bench] dense attention: {dense_ms:.3f} ms")
+
+    diagnostics = None
+    if not args.no_diagnostics and w.dtype == "bf16":
+        diagnostics = selection_diagnostics(w, p, sets[0], set_lists[0], ws, args.diag_blocks)
+        log(f"[bench] diagnostics: {json.dumps(diagnostics)}")
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -259,6 +345,7 @@ def main():
             "workload": w.name, "batch": B, "heads": H, "seq_len": w.seq_len, "seq_pad": p.seq_pad,
             "head_dim": D, "grid": list(w.grid), "density": density, "budget_blocks": p.budget,
             "clusters": p.n_clusters, "kmeans_iters": p.kmeans_iters, "block": 128, "seed": args.seed,
+            "input_sets": len(sets),
         },
         "stages_ms": {"score": score_ms, "sample": sample_ms, "attend": attend_ms},
         "dense_attention_ms": dense_ms,
@@ -269,7 +356,9 @@ def main():
         "score_stage_gbs": score_bytes / (score_ms * 1e-3) / 1e9,
         "score_stage_hbm_frac": score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "roofline": {
-            "kernel": "attend_bf16_kernel<128>" if w.dtype == "bf16" else "attend_f32_kernel<64>",
+            # the whole aba_attend call: the V^T copy and the work order are part of it
+            "kernel": ("aba_attend: vt_kernel<128> + order_kernel + attend_bf16_kernel<128,false>"
+                       if w.dtype == "bf16" else "aba_attend: attend_f32_kernel<64,false>"),
             "bound": "mfma",
             "achieved": attend_tflops,
             "peak": PEAK_BF16_TFLOPS,
@@ -277,10 +366,12 @@ def main():
             "frac": attend_tflops / PEAK_BF16_TFLOPS,
             "traffic": traffic_entry(),
         },
+        "diagnostics": diagnostics,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
+        q, k, v = host_sets[0]
         result["cpu_baseline"] = cpu_baseline(w, p, q, k, v, args.seed, args.cpu_seconds)
         log(f"[bench] CPU oracle: {result['cpu_baseline']['value']:.4g} TFLOP/s effective")
     print(json.dumps(result), flush=True)
