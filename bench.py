@@ -200,6 +200,100 @@ def selection_diagnostics(w, p, qkv, lists, ws, n_blocks: int):
     }
 
 
+def run_sweep(args, w):
+    """The denoising sweep: w.steps steps, each with fresh q/k/v (centres drifting
+    per step), each re-running score, sample and attend.  Also timed, on the same
+    inputs: the plan refreshed every args.plan_every steps and reused in between
+    (attend every step), and that schedule with dense attention for the first
+    args.dense_frac of the steps.  One JSON line."""
+    dev = torch.device("cuda:0")
+    steps = w.steps
+    t0 = time.perf_counter()
+    sets = [tuple(x.to(dev) for x in synth.make_inputs(w, seed=1001, step=s)) for s in range(steps)]
+    log(f"[bench] sweep: {steps} steps of inputs ready in {time.perf_counter() - t0:.1f} s")
+    density = w.densities[0] if args.density is None else args.density
+    p = aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, CLUSTERS, KMEANS_ITERS, w.budget(density))
+    B, H, NB, cap = p.batch, p.heads, p.n_blocks, p.list_cap
+    ws = aba.workspace(p, dev)
+    scores = torch.empty(B, H, NB, NB, dtype=torch.float32, device=dev)
+    lists = (torch.empty(B, H, NB, cap, dtype=torch.int32, device=dev),
+             torch.empty(B, H, NB, dtype=torch.int32, device=dev),
+             torch.empty(B, H, NB, cap, dtype=torch.float32, device=dev))
+    out = torch.empty_like(sets[0][0])
+    stream = torch.cuda.current_stream()
+
+    def sweep(plan_every: int, dense_steps: int, record: bool):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for s in range(steps):
+            qd, kd, vd = sets[s]
+            e = evs[s]
+            e[0].record(stream)
+            if s < dense_steps:
+                e[1].record(stream)
+                e[2].record(stream)
+                aba.attend_full(p, qd, kd, vd, out=out, ws=ws)
+            else:
+                if (s - dense_steps) % plan_every == 0:
+                    aba.score(p, qd, kd, out=scores, ws=ws)
+                    e[1].record(stream)
+                    aba.sample(p, scores, args.seed + s, out=lists)
+                else:
+                    e[1].record(stream)
+                e[2].record(stream)
+                aba.attend(p, qd, kd, vd, *lists, out=out, ws=ws)
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        per = [evs[s][0].elapsed_time(evs[s][3]) for s in range(steps)]
+        parts = {"score": float(sum(evs[s][0].elapsed_time(evs[s][1]) for s in range(steps))),
+                 "sample": float(sum(evs[s][1].elapsed_time(evs[s][2]) for s in range(steps))),
+                 "attend": float(sum(evs[s][2].elapsed_time(evs[s][3]) for s in range(steps)))}
+        return per, parts
+
+    for _ in range(max(1, args.warmup // 5)):
+        sweep(1, 0, False)
+    per, parts = sweep(1, 0, True)
+    total = float(sum(per))
+    log(f"[bench] sweep, plan every step: total {total:.2f} ms ({np.mean(per):.3f} ms/step; score {parts['score']:.2f}, "
+        f"sample {parts['sample']:.2f}, attend {parts['attend']:.2f})")
+    per_r, parts_r = sweep(args.plan_every, 0, True)
+    total_r = float(sum(per_r))
+    dense_steps = int(round(args.dense_frac * steps))
+    per_d, parts_d = sweep(args.plan_every, dense_steps, True)
+    total_d = float(sum(per_d))
+    log(f"[bench] sweep, plan every {args.plan_every}: total {total_r:.2f} ms; with {dense_steps} dense steps first: "
+        f"{total_d:.2f} ms")
+    dense_flops = w.dense_flops
+    result = {
+        "metric": METRIC,
+        "value": steps * dense_flops / (total * 1e-3) / 1e12,
+        "unit": "TFLOP/s (effective, dense-equivalent)",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": total / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian-mixture video tokens, fresh per step, centres drifting; no model weights)",
+        "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": w.seq_len, "head_dim": w.head_dim,
+                   "steps": steps, "drift": w.drift, "density": density, "budget_blocks": p.budget},
+        "sweep": {
+            "per_step_ms": per,
+            "total_ms": total,
+            "stages_total_ms": parts,
+            "score_sample_over_attend": (parts["score"] + parts["sample"]) / parts["attend"],
+            "plan_reuse": {"plan_every": args.plan_every, "total_ms": total_r, "stages_total_ms": parts_r,
+                           "speedup": total / total_r},
+            "plan_reuse_dense_first": {"plan_every": args.plan_every, "dense_steps": dense_steps,
+                                        "total_ms": total_d, "per_step_ms": per_d},
+        },
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +307,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--input-sets", type=int, default=3, help="input sets the steps cycle through")
+    ap.add_argument("--plan-every", type=int, default=4, help="sweep: steps between plan refreshes (the page: 4)")
+    ap.add_argument("--dense-frac", type=float, default=0.2,
+                    help="sweep: share of the first steps run dense (the page: 10 of 50)")
     ap.add_argument("--no-diagnostics", action="store_true")
     ap.add_argument("--diag-blocks", type=int, default=32, help="sampled query blocks for the selection diagnostics")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -228,6 +325,9 @@ def main():
         sys.exit(2)
 
     w = ALL[args.workload]
+    if w.steps > 1:
+        run_sweep(args, w)
+        return
     density = w.densities[0] if args.density is None else args.density
     dev = torch.device("cuda:0")
     log(f"[bench] workload {w.name}: {w.description}; density {density}")
