@@ -28,9 +28,10 @@
 // Computing the transposed products makes every lane own one query column, so
 // row statistics need a single cross-half exchange (v_permlane32_swap) and the
 // rescale of O is a per-lane scalar multiply.  LDS fragment reads are issued
-// four MFMAs ahead of their use, and the second key tile's exponentials are
-// interleaved with the first tile's PV MFMAs (transcendentals overlap matrix
-// work on gfx950, plain VALU arithmetic largely does not).
+// four MFMAs ahead of their use, the second key tile's probabilities are
+// computed between the first tile's PV MFMAs, and the wavefront raises its
+// priority while it issues MFMAs, so that the other wavefront of the SIMD
+// fills the softmax gaps rather than competing for the matrix pipe.
 //
 // fp32 path: a plain VALU kernel (pairs of lanes per query row) for fp32
 // inputs with head_dim 64.
@@ -442,6 +443,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int i = 0; i < PF; ++i) kf[i] = k_frag(kst, i);
         // each read is issued PF MFMAs ahead of its use; the scheduling
         // fences keep the compiler from pulling reads back next to their use
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             __builtin_amdgcn_sched_barrier(0);
@@ -450,6 +452,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             if (i + PF < NK) kf[i % PF] = k_frag(kst, i + PF);
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         // the PV operands are read while the softmax runs
         bf16x8 vf[PF];
 #pragma unroll
@@ -484,33 +487,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
-        // P^T in bf16 straight from the accumulators; the row sum adds the
-        // same rounded probabilities that enter the PV product
+        // P^T in bf16 straight from the accumulators; the row sum adds the fp32
+        // probabilities with plain adds (two chains), which overlap the MFMAs
+        // (v_dot2 would run on the matrix pipe and serialise with them)
         const float bias = lw - m_run;
-        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
         bf16x8 pb[KT][2];
         auto prob = [&](int kt, int r) __attribute__((always_inline)) {
-            pb[kt][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, bias));
-        };
-        auto row_sum = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int h2 = 0; h2 < 4; ++h2) {
-                    const bf16x2 pair = {pb[kt][sub][2 * h2], pb[kt][sub][2 * h2 + 1]};
-                    if (h2 & 1) l_run1 = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run1, false);
-                    else        l_run0 = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run0, false);
-                }
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, bias));
+            if (r & 1) l_run1 += pr; else l_run0 += pr;
+            pb[kt][r >> 3][r & 7] = (__bf16)pr;
         };
 #pragma unroll
         for (int r = 0; r < 16; ++r) prob(0, r);
-        row_sum(0);
         // O^T += V^T P^T: MFMA (kt, sub, dt) contracts the 16 keys held in
         // accumulator rows [8sub, 8sub+8) of S^T tile kt against V^T rows
         // [32dt, 32dt+32); for lane half h, element e is key 32kt + 16sub +
         // 8(e/4) + 4h + e%4, stored at positions 32kt + 16sub + 8h + e.
         // Tile 1's probabilities are computed between tile 0's MFMAs.
         constexpr int per = 16 / (NV / 2);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             __builtin_amdgcn_sched_barrier(0);
@@ -521,9 +516,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int e = 0; e < per; ++e) prob(1, per * i + e);
             }
-            if (i == NV / 2 - 1) row_sum(1);
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Sub-tile u is half u % 2 of list entry u / 2; its K sits in K slot u % 3,
