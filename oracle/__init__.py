@@ -65,11 +65,11 @@ def _load():
     lib.oracle_draw.restype = ctypes.c_uint32
     lib.oracle_sample.argtypes = [P, i32, i32, i32, i32, i32, u64, i32, P, P, P, P]
     lib.oracle_sample.restype = None
-    lib.oracle_attend.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f64, P, P, P, i32, P, i32, P, P, P, P]
+    lib.oracle_attend.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, f64, P, P, P, i32, P, i32, P, P, P, P]
     lib.oracle_attend.restype = None
     lib.oracle_attend_full.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f64, P, i32, P]
     lib.oracle_attend_full.restype = None
-    lib.oracle_block_mass.argtypes = [P, P, i32, i32, i32, i32, i32, i32, f64, P, i32, P]
+    lib.oracle_block_mass.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, f64, P, i32, P]
     lib.oracle_block_mass.restype = None
     lib.oracle_topk_mass.argtypes = [P, i32, i32]
     lib.oracle_topk_mass.restype = f64
@@ -142,7 +142,8 @@ def kmeans(q, n_valid: int, C: int = 8, T: int = 10, blk: int = BLOCK):
 
 
 def pool(k, n_valid: int, blk: int = BLOCK) -> np.ndarray:
-    """Mean of the valid keys of every key block (IBCS paragraph, "averaged keys")."""
+    """Mean of the valid keys of every key block of ``blk`` tokens (IBCS paragraph,
+    "averaged keys"; 4-token key blocks: the kernel paragraph)."""
     k = _f32(k)
     B, H, N_pad, D = k.shape
     NB = n_blocks(n_valid, blk)
@@ -201,13 +202,16 @@ def sample(scores, K: int, seed: int, cap: int | None = None):
 
 
 def attend(q, k, v, n_valid: int, idx, cnt, w, items=None, scale: float | None = None, shift=None,
-           blk: int = BLOCK):
+           blk: int = BLOCK, kblk: int | None = None):
     """HT-weighted softmax attention over each query block's kept list (SIP paragraph).
 
-    Returns out [n_items, blk, D] (fp64); with ``shift`` [n_items, blk] also (num, den)."""
+    List entries name key blocks of ``kblk`` tokens (default ``blk``; 4 for the
+    kernel paragraph's fine-grained key blocks).  Returns out [n_items, blk, D]
+    (fp64); with ``shift`` [n_items, blk] also (num, den)."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     B, H, N_pad, D = q.shape
     NB = n_blocks(n_valid, blk)
+    kblk = blk if kblk is None else kblk
     scale = default_scale(D) if scale is None else scale
     idx = np.ascontiguousarray(idx, np.int32)
     cnt = np.ascontiguousarray(cnt, np.int32)
@@ -221,7 +225,7 @@ def attend(q, k, v, n_valid: int, idx, cnt, w, items=None, scale: float | None =
         shift = np.ascontiguousarray(shift, np.float64).reshape(it.shape[0], blk)
         num = np.zeros((it.shape[0], blk, D), np.float64)
         den = np.zeros((it.shape[0], blk), np.float64)
-    _load().oracle_attend(_ptr(q), _ptr(k), _ptr(v), B, H, n_valid, N_pad, D, blk, scale, _ptr(idx), _ptr(cnt),
+    _load().oracle_attend(_ptr(q), _ptr(k), _ptr(v), B, H, n_valid, N_pad, D, blk, kblk, scale, _ptr(idx), _ptr(cnt),
                           _ptr(w), cap, _ptr(it), it.shape[0], _ptr(shift), _ptr(out), _ptr(num), _ptr(den))
     return (out, num, den) if shift is not None else out
 
@@ -239,15 +243,18 @@ def attend_full(q, k, v, n_valid: int, items=None, scale: float | None = None, b
     return out
 
 
-def block_mass(q, k, n_valid: int, items=None, scale: float | None = None, blk: int = BLOCK):
-    """Dense attention mass per key block, averaged over each query block's valid rows."""
+def block_mass(q, k, n_valid: int, items=None, scale: float | None = None, blk: int = BLOCK,
+               kblk: int | None = None):
+    """Dense attention mass per key block of ``kblk`` tokens (default ``blk``),
+    averaged over the valid rows of each listed query block of ``blk`` tokens."""
     q, k = _f32(q), _f32(k)
     B, H, N_pad, D = q.shape
     NB = n_blocks(n_valid, blk)
+    kblk = blk if kblk is None else kblk
     scale = default_scale(D) if scale is None else scale
     it = _items(items, B, H, NB)
-    mass = np.zeros((it.shape[0], NB), np.float64)
-    _load().oracle_block_mass(_ptr(q), _ptr(k), B, H, n_valid, N_pad, D, blk, scale, _ptr(it), it.shape[0],
+    mass = np.zeros((it.shape[0], n_blocks(n_valid, kblk)), np.float64)
+    _load().oracle_block_mass(_ptr(q), _ptr(k), B, H, n_valid, N_pad, D, blk, kblk, scale, _ptr(it), it.shape[0],
                               _ptr(mass))
     return mass
 

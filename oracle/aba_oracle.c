@@ -18,8 +18,14 @@
  *               passed widened to float32, which is exact.  All arithmetic is
  *               done in double.
  *   N         : valid tokens; rows >= N are padding and are ignored.
- *   blk       : tokens per query block and per key block (128 for the
- *               workloads here).  NB = ceil(N / blk).
+ *   blk       : tokens per query block (128: the page's query blocks).
+ *               NB = ceil(N / blk).
+ *   kblk      : tokens per key block: 128, or 4 for the fine-grained
+ *               selection of the page's third paragraph ("Три приёма
+ *               AB-Attention", the kernel paragraph: key/value blocks of 4
+ *               tokens).  NBk = ceil(N / kblk).  Pooling, scoring, sampling,
+ *               attention and the attention mass all work per key block of
+ *               kblk tokens; clustering works per query block of blk.
  *   items     : optional list of (b, h, query-block) triples, int32[n][3], so
  *               that large layers can be checked on a sample of query blocks.
  *
@@ -407,7 +413,7 @@ void oracle_sample(const float *scores, int B, int H, int NBq, int NBk, int K, u
 /*   den = sum_j w_j sum_{t in j} exp(l_t - M)                               */
 /*   o_i = num / den                                                         */
 /* ---------------------------------------------------------------------- */
-static void attend_row(const float *qi, const float *kh, const float *vh, int N, int D, int blk,
+static void attend_row(const float *qi, const float *kh, const float *vh, int N, int D, int kblk,
                        double scale, const int32_t *list, const float *wl, int n_list, int have_shift,
                        double shift, double *num, double *den_out, double *logit_buf)
 {
@@ -415,9 +421,9 @@ static void attend_row(const float *qi, const float *kh, const float *vh, int N,
     int pos = 0;
     for (int e = 0; e < n_list; ++e) {
         int j = list[e];
-        int n = rows_in_block(N, blk, j);
+        int n = rows_in_block(N, kblk, j);
         for (int t = 0; t < n; ++t) {
-            const float *kt = kh + ((long)j * blk + t) * D;
+            const float *kt = kh + ((long)j * kblk + t) * D;
             double dot = 0.0;
             for (int d = 0; d < D; ++d) dot += (double)qi[d] * (double)kt[d];
             logit_buf[pos] = scale * dot;
@@ -432,9 +438,9 @@ static void attend_row(const float *qi, const float *kh, const float *vh, int N,
     for (int e = 0; e < n_list; ++e) {
         int j = list[e];
         double wj = (double)wl[e];
-        int n = rows_in_block(N, blk, j);
+        int n = rows_in_block(N, kblk, j);
         for (int t = 0; t < n; ++t) {
-            const float *vt = vh + ((long)j * blk + t) * D;
+            const float *vt = vh + ((long)j * kblk + t) * D;
             double p = wj * exp(logit_buf[pos] - M);
             den += p;
             for (int d = 0; d < D; ++d) num[d] += p * (double)vt[d];
@@ -444,12 +450,13 @@ static void attend_row(const float *qi, const float *kh, const float *vh, int N,
     *den_out = den;
 }
 
-/* items: int32 [n_items][3] = (b, h, query block).  idx/w: [B,H,NBq,cap],    */
-/* cnt: [B,H,NBq].  out: [n_items, blk, D] double.  shift (nullable):        */
+/* items: int32 [n_items][3] = (b, h, query block).  idx/w: [B,H,NBq,cap]    */
+/* (entries are key blocks of kblk tokens), cnt: [B,H,NBq].                  */
+/* out: [n_items, blk, D] double.  shift (nullable):                         */
 /* [n_items, blk]; when given, num [n_items,blk,D] and den [n_items,blk] are */
 /* written too and out = num / den.                                          */
 void oracle_attend(const float *q, const float *k, const float *v, int B, int H, int N, int N_pad,
-                   int D, int blk, double scale, const int32_t *idx, const int32_t *cnt, const float *w,
+                   int D, int blk, int kblk, double scale, const int32_t *idx, const int32_t *cnt, const float *w,
                    int cap, const int32_t *items, int n_items, const double *shift, double *out,
                    double *num_out, double *den_out)
 {
@@ -464,7 +471,7 @@ void oracle_attend(const float *q, const float *k, const float *v, int B, int H,
         int n_list = cnt[row] < cap ? cnt[row] : cap;
         const float *kh = row_ptr(k, H, N_pad, D, b, h, 0);
         const float *vh = row_ptr(v, H, N_pad, D, b, h, 0);
-        double *logit_buf = (double *)malloc(sizeof(double) * (size_t)n_list * blk + 1);
+        double *logit_buf = (double *)malloc(sizeof(double) * ((size_t)n_list * kblk + 1));
         double *num = (double *)malloc(sizeof(double) * (size_t)D);
         int nq = rows_in_block(N, blk, qb);
         for (int r = 0; r < blk; ++r) {
@@ -479,7 +486,7 @@ void oracle_attend(const float *q, const float *k, const float *v, int B, int H,
             }
             const float *qi = row_ptr(q, H, N_pad, D, b, h, (long)qb * blk + r);
             double den;
-            attend_row(qi, kh, vh, N, D, blk, scale, list, wl, n_list, shift != NULL,
+            attend_row(qi, kh, vh, N, D, kblk, scale, list, wl, n_list, shift != NULL,
                        shift ? shift[(long)it * blk + r] : 0.0, num, &den, logit_buf);
             for (int d = 0; d < D; ++d) o[d] = num[d] / den;
             if (shift) {
@@ -537,12 +544,13 @@ void oracle_attend_full(const float *q, const float *k, const float *v, int B, i
 /* page's "share of attention mass kept by ideal top-k", section "Где       */
 /* ломаются прежние разреженные схемы"): mass[it][j] = mean over the valid  */
 /* queries i of query block qb of sum_{t in j} P_it, with P the dense       */
-/* softmax.  items as above; mass [n_items, NB].                            */
+/* softmax and j a key block of kblk tokens.  items as above (query blocks   */
+/* of blk tokens); mass [n_items, NBk].                                     */
 /* ---------------------------------------------------------------------- */
 void oracle_block_mass(const float *q, const float *k, int B, int H, int N, int N_pad, int D, int blk,
-                       double scale, const int32_t *items, int n_items, double *mass)
+                       int kblk, double scale, const int32_t *items, int n_items, double *mass)
 {
-    int NB = oracle_n_blocks(N, blk);
+    int NB = oracle_n_blocks(N, kblk);
     (void)B;
 #pragma omp parallel for schedule(dynamic)
     for (int it = 0; it < n_items; ++it) {
@@ -562,7 +570,7 @@ void oracle_block_mass(const float *q, const float *k, int B, int H, int N, int 
                 if (logit[t] > mx) mx = logit[t];
             }
             for (int t = 0; t < N; ++t) z += exp(logit[t] - mx);
-            for (int t = 0; t < N; ++t) m[t / blk] += exp(logit[t] - mx) / z / (double)nq;
+            for (int t = 0; t < N; ++t) m[t / kblk] += exp(logit[t] - mx) / z / (double)nq;
         }
         free(logit);
     }
