@@ -27,7 +27,9 @@ LIB_PATH = os.path.join(_HERE, "libaba.so")
 ABA_OK, ABA_E_INVALID, ABA_E_UNSUPPORTED, ABA_E_HIP = 0, 1, 2, 3
 ABA_F32, ABA_BF16 = 0, 1
 BLOCK = 128
+FINE_BLOCK = 4
 MAX_BLOCKS = 1024
+MAX_KEY_BLOCKS = 32768
 MAX_CLUSTERS = 8
 
 _DT = {"f32": ABA_F32, "bf16": ABA_BF16, torch.float32: ABA_F32, torch.bfloat16: ABA_BF16}
@@ -47,7 +49,8 @@ class PlanStruct(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
         ("seq_pad", ctypes.c_int32), ("n_clusters", ctypes.c_int32), ("kmeans_iters", ctypes.c_int32),
         ("budget", ctypes.c_int32), ("list_cap", ctypes.c_int32), ("dtype", ctypes.c_int32),
-        ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
+        ("softmax_scale", ctypes.c_float), ("key_block", ctypes.c_int32), ("n_key_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
     ]
 
 
@@ -68,7 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, i32, u64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float
     PP = ctypes.POINTER(PlanStruct)
-    lib.aba_plan.argtypes = [PP, i32, i32, i32, i32, i32, i32, i32, i32, f32]
+    lib.aba_plan.argtypes = [PP, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32]
     lib.aba_score.argtypes = [PP, P, P, P, P, P, P, P, P]
     lib.aba_sample.argtypes = [PP, P, u64, P, P, P, P]
     lib.aba_attend.argtypes = [PP, P, P, P, P, P, P, P, P, P]
@@ -104,11 +107,13 @@ class Plan:
 
 
 def plan(batch: int, heads: int, seq_len: int, head_dim: int, dtype="bf16", n_clusters: int = 8,
-         kmeans_iters: int = 10, budget: int = 1, softmax_scale: float = 0.0) -> Plan:
-    """aba_plan: validate the layer's sizes and fill a plan (host only)."""
+         kmeans_iters: int = 10, budget: int = 1, softmax_scale: float = 0.0, key_block: int = BLOCK) -> Plan:
+    """aba_plan: validate the layer's sizes and fill a plan (host only).  key_block is
+    BLOCK (128-token key blocks) or FINE_BLOCK (4-token key blocks); budget counts
+    key blocks of that size."""
     raw = PlanStruct()
     _check(load_library().aba_plan(ctypes.byref(raw), batch, heads, seq_len, head_dim, _DT[dtype], n_clusters,
-                                   kmeans_iters, budget, float(softmax_scale)))
+                                   kmeans_iters, budget, key_block, float(softmax_scale)))
     return Plan(raw)
 
 
@@ -152,21 +157,21 @@ def _ws(p: Plan, ws, device) -> torch.Tensor:
 
 def score(p: Plan, q: torch.Tensor, k: torch.Tensor, *, return_parts: bool = False, out: torch.Tensor | None = None,
           ws: torch.Tensor | None = None):
-    """aba_score: IBCS scores [B,H,NB,NB] (float32).  With return_parts also the
-    centroids [B,H,NB,C,D], cluster weights [B,H,NB,C] and pooled keys [B,H,NB,D]."""
+    """aba_score: IBCS scores [B,H,NB,NBk] (float32).  With return_parts also the
+    centroids [B,H,NB,C,D], cluster weights [B,H,NB,C] and pooled keys [B,H,NBk,D]."""
     dev = q.device
     _need(q, "q", _qkv_shape(p), p.torch_dtype, dev)
     _need(k, "k", _qkv_shape(p), p.torch_dtype, dev)
-    B, H, NB, C, D = p.batch, p.heads, p.n_blocks, p.n_clusters, p.head_dim
+    B, H, NB, NBk, C, D = p.batch, p.heads, p.n_blocks, p.n_key_blocks, p.n_clusters, p.head_dim
     if out is None:
-        out = torch.empty(B, H, NB, NB, dtype=torch.float32, device=dev)
-    _need(out, "scores", (B, H, NB, NB), torch.float32, dev)
+        out = torch.empty(B, H, NB, NBk, dtype=torch.float32, device=dev)
+    _need(out, "scores", (B, H, NB, NBk), torch.float32, dev)
     cent = wgt = kbar = None
     if return_parts:
         cent = torch.empty(B, H, NB, C, D, dtype=torch.float32, device=dev)
         wgt = torch.empty(B, H, NB, C, dtype=torch.float32, device=dev)
-        kbar = torch.empty(B, H, NB, D, dtype=torch.float32, device=dev)
-    else:
+        kbar = torch.empty(B, H, NBk, D, dtype=torch.float32, device=dev)
+    if not return_parts or p.key_block != BLOCK:
         ws = _ws(p, ws, dev)
     _check(load_library().aba_score(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(out), _ptr(cent), _ptr(wgt),
                                     _ptr(kbar), _ptr(ws), _stream()))
@@ -177,7 +182,7 @@ def sample(p: Plan, scores: torch.Tensor, seed: int, *, out=None):
     """aba_sample: (idx [B,H,NB,cap] int32, cnt [B,H,NB] int32, w [B,H,NB,cap] float32)."""
     dev = scores.device
     B, H, NB, cap = p.batch, p.heads, p.n_blocks, p.list_cap
-    _need(scores, "scores", (B, H, NB, NB), torch.float32, dev)
+    _need(scores, "scores", (B, H, NB, p.n_key_blocks), torch.float32, dev)
     if out is None:
         out = (torch.empty(B, H, NB, cap, dtype=torch.int32, device=dev),
                torch.empty(B, H, NB, dtype=torch.int32, device=dev),
@@ -226,13 +231,14 @@ def attend_full(p: Plan, q, k, v, *, out=None, ws=None) -> torch.Tensor:
 
 
 def block_mass(p: Plan, q, k, items) -> torch.Tensor:
-    """aba_block_mass: dense attention mass per key block for the listed (b, h, query block)
-    items, float32 [n_items, NB]; each row sums to one."""
+    """aba_block_mass: dense attention mass per key block (of the plan's key_block
+    tokens) for the listed (b, h, query block) items, float32 [n_items, NBk]; each
+    row sums to one."""
     dev = q.device
     _need(q, "q", _qkv_shape(p), p.torch_dtype, dev)
     _need(k, "k", _qkv_shape(p), p.torch_dtype, dev)
     it = torch.as_tensor(items, dtype=torch.int32).reshape(-1, 3).contiguous().to(dev)
-    mass = torch.empty(it.shape[0], p.n_blocks, dtype=torch.float32, device=dev)
+    mass = torch.empty(it.shape[0], p.n_key_blocks, dtype=torch.float32, device=dev)
     _check(load_library().aba_block_mass(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(it), it.shape[0], _ptr(mass),
                                          _stream()))
     return mass

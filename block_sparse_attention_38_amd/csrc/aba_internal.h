@@ -9,8 +9,11 @@
 
 namespace aba {
 
-constexpr int kBlock = 128;       // tokens per query block and per key block
+constexpr int kBlock = 128;       // tokens per query block (and per coarse key block)
+constexpr int kFineBlock = 4;     // tokens per fine-grained key block
 constexpr int kMaxBlocks = 1024;  // blocks per sequence the score/sample kernels hold in LDS
+constexpr int kMaxFineBlocks = 32768;            // fine key blocks per sequence (N <= 131072)
+constexpr int kSampleLdsLimit = 152 * 1024;      // dynamic LDS of the long-row sampler (of 160 KB per CU)
 constexpr int kMaxClusters = 8;
 
 enum Dtype : int { kF32 = 0, kBF16 = 1 };
@@ -22,13 +25,29 @@ hipError_t launch_pool(const void *k, int dtype, int B, int H, int N, int N_pad,
                        hipStream_t s);
 hipError_t launch_score(const float *cent, const float *weight, const float *kbar, int B, int H, int NB, int C, int D,
                         float scale, float *scores, hipStream_t s);
-hipError_t launch_sample(const float *scores, int B, int H, int NB, int K, uint64_t seed, int cap, int32_t *idx,
-                         int32_t *cnt, float *w, hipStream_t s);
+hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int cap,
+                         int32_t *idx, int32_t *cnt, float *w, hipStream_t s);
+// Dynamic LDS the sampler needs for rows of NB key blocks and budget K (0: the
+// short-row kernel, whose LDS is static).
+size_t sample_lds_bytes(int NB, int K);
+// 4-token key blocks: pooling and the two-pass MFMA scoring (workspace: per-chunk
+// partial statistics and per-centroid coefficients).
+hipError_t launch_fine_pool(const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NBk, float *kbar,
+                            hipStream_t s);
+size_t fine_score_workspace_bytes(int B, int H, int NBq, int NBk);
+hipError_t launch_fine_score(const float *cent, const float *weight, const float *kbar, int B, int H, int NBq, int NBk,
+                             int C, int D, float scale, void *ws, float *scores, hipStream_t s);
 hipError_t launch_attend(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad, int D,
                          int NB, float scale, const int32_t *idx, const int32_t *cnt, const float *w, int cap, bool full,
                          void *ws, void *out, hipStream_t s);
+// Sparse attention over lists of 4-token key blocks (bf16 with D = 128, or fp32
+// with D = 64); same workspace as launch_attend.
+hipError_t launch_attend_fine(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad,
+                              int D, int NBq, int NBk, float scale, const int32_t *idx, const int32_t *cnt,
+                              const float *w, int cap, void *ws, void *out, hipStream_t s);
+// Attention mass per key block of kb tokens (128 or 4) for the listed query blocks.
 hipError_t launch_block_mass(const void *q, const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB,
-                             float scale, const int32_t *items, int n_items, float *mass, hipStream_t s);
+                             int kb, float scale, const int32_t *items, int n_items, float *mass, hipStream_t s);
 // Device bytes launch_attend needs at ws (the V^T copy and the work order; 0 for fp32).
 size_t attend_workspace_bytes(int dtype, int B, int H, int N_pad, int D);
 

@@ -37,20 +37,25 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // One workspace serves every call, each using it from offset 0 and only for
 // the duration of the call: aba_score keeps centroids, weights and pooled keys
-// there when the caller does not ask for them, aba_attend and aba_attend_full
-// the V^T staging copy of v.
+// there when the caller does not ask for them (and, for 4-token key blocks, the
+// per-chunk softmax statistics of its two-pass scoring), aba_attend and
+// aba_attend_full the V^T staging copy of v and the work order.
 struct Workspace {
-    size_t cent, weight, kbar, score_total, attend_total, total;
+    size_t cent, weight, kbar, fine, score_total, attend_total, total;
 };
 
 Workspace workspace_layout(const aba_plan_t &p)
 {
     const size_t rows = (size_t)p.batch * p.heads * p.n_blocks;
+    const size_t krows = (size_t)p.batch * p.heads * p.n_key_blocks;
     Workspace w;
     w.cent = 0;
     w.weight = align256(rows * p.n_clusters * p.head_dim * sizeof(float));
     w.kbar = w.weight + align256(rows * p.n_clusters * sizeof(float));
-    w.score_total = w.kbar + align256(rows * p.head_dim * sizeof(float));
+    w.fine = w.kbar + align256(krows * p.head_dim * sizeof(float));
+    w.score_total = w.fine;
+    if (p.key_block == ABA_FINE_BLOCK)
+        w.score_total += align256(aba::fine_score_workspace_bytes(p.batch, p.heads, p.n_blocks, p.n_key_blocks));
     w.attend_total = align256(aba::attend_workspace_bytes(p.dtype, p.batch, p.heads, p.seq_pad, p.head_dim));
     w.total = w.score_total > w.attend_total ? w.score_total : w.attend_total;
     return w;
@@ -70,10 +75,10 @@ aba_status check_plan(const aba_plan_t *p)
     if (!p) return fail(ABA_E_INVALID, "plan is NULL");
     aba_plan_t ref;
     const aba_status st = aba_plan(&ref, p->batch, p->heads, p->seq_len, p->head_dim, (aba_dtype)p->dtype,
-                                   p->n_clusters, p->kmeans_iters, p->budget, p->softmax_scale);
+                                   p->n_clusters, p->kmeans_iters, p->budget, p->key_block, p->softmax_scale);
     if (st != ABA_OK) return st;
     if (ref.n_blocks != p->n_blocks || ref.seq_pad != p->seq_pad || ref.list_cap != p->list_cap ||
-        ref.block != p->block || ref.workspace_bytes != p->workspace_bytes)
+        ref.block != p->block || ref.n_key_blocks != p->n_key_blocks || ref.workspace_bytes != p->workspace_bytes)
         return fail(ABA_E_INVALID, "plan fields are inconsistent; fill the plan with aba_plan");
     return ABA_OK;
 }
@@ -83,7 +88,7 @@ aba_status check_plan(const aba_plan_t *p)
 extern "C" {
 
 aba_status aba_plan(aba_plan_t *p, int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim, aba_dtype dtype,
-                    int32_t n_clusters, int32_t kmeans_iters, int32_t budget, float softmax_scale)
+                    int32_t n_clusters, int32_t kmeans_iters, int32_t budget, int32_t key_block, float softmax_scale)
 {
     g_last_error.clear();
     if (!p) return fail(ABA_E_INVALID, "plan is NULL");
@@ -95,6 +100,8 @@ aba_status aba_plan(aba_plan_t *p, int32_t batch, int32_t heads, int32_t seq_len
     if (budget < 1) return fail(ABA_E_INVALID, "budget must be >= 1 (got %d)", budget);
     if (!(std::isfinite(softmax_scale))) return fail(ABA_E_INVALID, "softmax_scale is not finite");
     if (dtype != ABA_F32 && dtype != ABA_BF16) return fail(ABA_E_INVALID, "unknown dtype %d", (int)dtype);
+    if (key_block != ABA_BLOCK && key_block != ABA_FINE_BLOCK)
+        return fail(ABA_E_INVALID, "key_block must be %d or %d (got %d)", ABA_BLOCK, ABA_FINE_BLOCK, key_block);
     if (dtype == ABA_BF16 && head_dim != 64 && head_dim != 128)
         return fail(ABA_E_UNSUPPORTED, "bf16 kernels exist for head_dim 64 and 128 (got %d)", head_dim);
     if (dtype == ABA_F32 && head_dim != 64)
@@ -107,6 +114,21 @@ aba_status aba_plan(aba_plan_t *p, int32_t batch, int32_t heads, int32_t seq_len
         return fail(ABA_E_UNSUPPORTED, "at most %d blocks of %d tokens (got %lld)", ABA_MAX_BLOCKS, ABA_BLOCK,
                     (long long)nb);
     if ((int64_t)batch * heads * nb > 0x7FFFFFFF) return fail(ABA_E_UNSUPPORTED, "batch*heads*blocks exceeds 2^31");
+    const int64_t nbk = ((int64_t)seq_len + key_block - 1) / key_block;
+    if (key_block == ABA_FINE_BLOCK) {
+        if (dtype == ABA_BF16 && head_dim != 128)
+            return fail(ABA_E_UNSUPPORTED, "4-token key blocks with bf16 need head_dim 128 (got %d)", head_dim);
+        if (nbk > ABA_MAX_KEY_BLOCKS)
+            return fail(ABA_E_UNSUPPORTED, "at most %d key blocks of %d tokens (got %lld)", ABA_MAX_KEY_BLOCKS,
+                        ABA_FINE_BLOCK, (long long)nbk);
+        if ((int64_t)batch * heads * nb * nbk > ((int64_t)1 << 40))
+            return fail(ABA_E_UNSUPPORTED, "score matrix of %lld entries is too large",
+                        (long long)((int64_t)batch * heads * nb * nbk));
+        const size_t lds = aba::sample_lds_bytes((int)nbk, budget);
+        if (lds > (size_t)aba::kSampleLdsLimit)
+            return fail(ABA_E_UNSUPPORTED, "budget %d over %lld key blocks needs %zu bytes of sampling LDS (limit %d)",
+                        budget, (long long)nbk, lds, aba::kSampleLdsLimit);
+    }
 
     std::memset(p, 0, sizeof *p);
     p->batch = batch;
@@ -119,9 +141,11 @@ aba_status aba_plan(aba_plan_t *p, int32_t batch, int32_t heads, int32_t seq_len
     p->n_clusters = n_clusters;
     p->kmeans_iters = kmeans_iters;
     p->budget = budget;
-    p->list_cap = (int32_t)nb;
+    p->list_cap = (int32_t)nbk;
     p->dtype = dtype;
     p->softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    p->key_block = key_block;
+    p->n_key_blocks = (int32_t)nbk;
     p->workspace_bytes = workspace_layout(*p).total;
     return ABA_OK;
 }
@@ -133,9 +157,10 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
     aba_status st = check_plan(p);
     if (st != ABA_OK) return st;
     if (!q || !k || !scores) return fail(ABA_E_INVALID, "q, k and scores must be non-NULL");
-    if ((!centroids || !cluster_w || !pooled_k) && !workspace)
-        return fail(ABA_E_INVALID, "workspace of %llu bytes is required unless every optional output is given",
-                    (unsigned long long)p->workspace_bytes);
+    const bool fine = p->key_block == ABA_FINE_BLOCK;
+    if ((!centroids || !cluster_w || !pooled_k || fine) && !workspace)
+        return fail(ABA_E_INVALID, "workspace of %llu bytes is required (4-token key blocks always need it, 128-token "
+                    "ones unless every optional output is given)", (unsigned long long)p->workspace_bytes);
     const Workspace lay = workspace_layout(*p);
     char *ws = static_cast<char *>(workspace);
     float *cent = centroids ? centroids : reinterpret_cast<float *>(ws + lay.cent);
@@ -146,6 +171,14 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
     st = hip_status(aba::launch_kmeans(q, p->dtype, B, H, N, NP, D, NB, p->n_clusters, p->kmeans_iters, cent, wgt, stream),
                     "kmeans launch");
     if (st != ABA_OK) return st;
+    if (fine) {
+        const int NBk = p->n_key_blocks;
+        st = hip_status(aba::launch_fine_pool(k, p->dtype, B, H, N, NP, D, NBk, kbar, stream), "pool launch");
+        if (st != ABA_OK) return st;
+        return hip_status(aba::launch_fine_score(cent, wgt, kbar, B, H, NB, NBk, p->n_clusters, D, p->softmax_scale,
+                                                 ws + lay.fine, scores, stream),
+                          "score launch");
+    }
     st = hip_status(aba::launch_pool(k, p->dtype, B, H, N, NP, D, NB, kbar, stream), "pool launch");
     if (st != ABA_OK) return st;
     return hip_status(aba::launch_score(cent, wgt, kbar, B, H, NB, p->n_clusters, D, p->softmax_scale, scores, stream),
@@ -159,8 +192,8 @@ aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, i
     aba_status st = check_plan(p);
     if (st != ABA_OK) return st;
     if (!scores || !idx || !cnt || !w) return fail(ABA_E_INVALID, "scores, idx, cnt and w must be non-NULL");
-    return hip_status(aba::launch_sample(scores, p->batch, p->heads, p->n_blocks, p->budget, seed, p->list_cap, idx, cnt,
-                                         w, stream),
+    return hip_status(aba::launch_sample(scores, p->batch, p->heads, p->n_blocks, p->n_key_blocks, p->budget, seed,
+                                         p->list_cap, idx, cnt, w, stream),
                       "sample launch");
 }
 
@@ -174,6 +207,11 @@ aba_status aba_attend(const aba_plan_t *p, const void *q, const void *k, const v
         return fail(ABA_E_INVALID, "q, k, v, idx, cnt, w and out must be non-NULL");
     st = check_attend_workspace(p, workspace);
     if (st != ABA_OK) return st;
+    if (p->key_block == ABA_FINE_BLOCK)
+        return hip_status(aba::launch_attend_fine(q, k, v, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad,
+                                                  p->head_dim, p->n_blocks, p->n_key_blocks, p->softmax_scale, idx, cnt,
+                                                  w, p->list_cap, workspace, out, stream),
+                          "attend launch");
     return hip_status(aba::launch_attend(q, k, v, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad, p->head_dim,
                                          p->n_blocks, p->softmax_scale, idx, cnt, w, p->list_cap, false, workspace, out,
                                          stream),
@@ -206,7 +244,7 @@ aba_status aba_block_mass(const aba_plan_t *p, const void *q, const void *k, con
     if (n_items == 0) return ABA_OK;
     if (!q || !k || !items || !mass) return fail(ABA_E_INVALID, "q, k, items and mass must be non-NULL");
     return hip_status(aba::launch_block_mass(q, k, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad, p->head_dim,
-                                             p->n_blocks, p->softmax_scale, items, n_items, mass, stream),
+                                             p->n_blocks, p->key_block, p->softmax_scale, items, n_items, mass, stream),
                       "block_mass launch");
 }
 

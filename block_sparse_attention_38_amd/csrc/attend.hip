@@ -263,26 +263,31 @@ __device__ __forceinline__ Entry list_entry(const int32_t *lrow, const float *wr
 // block is computed by one workgroup, independently of the others).
 // ---------------------------------------------------------------------------
 constexpr int kOrderThreads = 1024;
+constexpr int kOrderBins = kMaxFineBlocks / (kSub / kFineBlock) + 1;   // cost ranks: 0 .. ceil(cap / unit)
 
-__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ cnt, int G, int cap,
+// cnt[i] entries cost ceil(cnt[i] / unit) units of work (unit = 1 for 128-token
+// key blocks, 16 for 4-token key blocks: one 64-key sub-tile).
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__restrict__ cnt, int G, int cap, int unit,
                                                              int32_t *__restrict__ order)
 {
-    __shared__ int bins[kMaxBlocks + 1];
+    __shared__ int bins[kOrderBins];
     __shared__ int part[kOrderThreads / 64];
     constexpr int kXcds = 8;
     const int x = blockIdx.x, per = G / kXcds, extra = G % kXcds;
     const int start = x * per + (x < extra ? x : extra), n = per + (x < extra ? 1 : 0);
-    const int nb = cap + 1, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    auto key = [&](int i) {   // count rank: 0 for the largest possible count
+    const int capu = (cap + unit - 1) / unit;
+    const int nb = capu + 1, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto key = [&](int i) {   // cost rank: 0 for the largest possible cost
         const int c = cnt[start + i];
-        return cap - (c < 0 ? 0 : (c > cap ? cap : c));
+        const int u = c <= 0 ? 0 : (c >= cap ? capu : (c + unit - 1) / unit);
+        return capu - u;
     };
     for (int b = tid; b < nb; b += kOrderThreads) bins[b] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kOrderThreads) atomicAdd(&bins[key(i)], 1);
     __syncthreads();
     // exclusive scan of bins[0 .. nb): each thread owns a run of consecutive bins
-    constexpr int kRun = (kMaxBlocks + 1 + kOrderThreads - 1) / kOrderThreads;
+    constexpr int kRun = (kOrderBins + kOrderThreads - 1) / kOrderThreads;
     int run[kRun], sum = 0;
 #pragma unroll
     for (int r = 0; r < kRun; ++r) {
@@ -593,6 +598,439 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
 }
 
+
+// ---------------------------------------------------------------------------
+// 4-token key blocks (kernel paragraph: the unit of selection is smaller than
+// the compute tile).  A list entry is a key block of 4 tokens; 16 of them fill
+// a 64-key sub-tile, gathered by index with direct loads into the same LDS
+// ring as above, so the MFMA work per sub-tile is unchanged.  At D = 128 one
+// 4-token block of K (4 rows) or of V^T is exactly 1024 bytes, one direct load
+// of a wavefront: load t of wavefront w fills block slot 4w + t, its source
+// address a scalar (block index x 1024) taken from the list window with
+// v_readlane.
+//
+// V^T is staged block-major here (vtg_kernel): block g of a head is a [D][4]
+// bf16 tile at byte offset 1024 g, so a gathered block lands in LDS as one
+// contiguous 1 KB piece.  The PV operand of lane half h (keys 8(e/4) + 4h + e%4
+// of its S^T accumulators, e = 0..7) is then the 4 keys of block slot ga at
+// dimension d followed by the 4 keys of slot ga + 2: two 8-byte LDS reads, one
+// per 256 contiguous bytes in each half-wavefront.
+//
+// Weights: an S^T element in row 8(r/4) + 4h + r%4 of 32-key tile kt belongs
+// to block slot 8kt + 2(r/4) + h, so each lane needs 8 log2 weights per
+// sub-tile, read from the window with v_readlane and selected by lane half.
+// The lazy rescale tests an upper bound of the sub-tile's shifted maximum
+// (max raw logit x scale + max log2 weight of the sub-tile): still no exp2
+// argument exceeds the slack, and the running max can only overshoot by the
+// spread of log2 weights (at most 32), harmless in fp32.
+// Entries that are invalid or past the list load block 0 and get weight 0
+// (log2 w = -inf); a sub-tile with no valid entry is not computed.  Keys past
+// N can only sit in the last key block when N % 4 != 0; sub-tiles holding it
+// mask those keys explicitly.
+// ---------------------------------------------------------------------------
+constexpr int kFineSub = kSub / kFineBlock;   // 4-token key blocks per sub-tile
+
+template <int D>
+__global__ __launch_bounds__(256) void vtg_kernel(const uint16_t *__restrict__ v, int N, int N_pad, int NBk, long total,
+                                                  uint16_t *__restrict__ vt)
+{
+    // one thread per (b, h, key block g, dimension pair p): reads 4 B of each
+    // of the block's 4 rows, writes dims 2p and 2p + 1 x 4 keys (16 B)
+    constexpr int PAIRS = D / 2;
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int p = (int)(i % PAIRS);
+    const long row = i / PAIRS;
+    const int g = (int)(row % NBk);
+    const long bh = row / NBk;
+    const long t0 = (long)g * kFineBlock;
+    const uint16_t *src = v + (bh * N_pad + t0) * D + 2 * p;
+    uint32_t x[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x[t] = (t0 + t < N) ? *reinterpret_cast<const uint32_t *>(src + (long)t * D) : 0u;
+    const uint4 o = make_uint4((x[0] & 0xFFFFu) | (x[1] << 16), (x[2] & 0xFFFFu) | (x[3] << 16),
+                               (x[0] >> 16) | (x[1] & 0xFFFF0000u), (x[2] >> 16) | (x[3] & 0xFFFF0000u));
+    *reinterpret_cast<uint4 *>(vt + (bh * N_pad + t0) * D + 8 * p) = o;
+}
+
+// 64 list entries held lane-distributed: lane i has entry 64m + i as the block
+// to load (0 for invalid entries and entries past the list) and its log2
+// weight (-inf for those).  Ballots mark the entries that contribute and the
+// entries whose block is the partial last block.
+struct FineWindow {
+    int j;
+    float lw;
+    uint64_t valid, partial;
+};
+
+__device__ __forceinline__ FineWindow load_fine_window(const int32_t *lrow, const float *wrow, int m, int n_list,
+                                                       int NBk, bool ragged, int lane)
+{
+    const int e = 64 * m + lane;
+    int j = 0;
+    float lw = -INFINITY;
+    if (e < n_list) {
+        const int jj = lrow[e];
+        const float wj = wrow[e];
+        if (jj >= 0 && jj < NBk && wj > 0.f && wj < INFINITY) {
+            j = jj;
+            lw = __log2f(wj);
+        }
+    }
+    FineWindow win;
+    win.j = j;
+    win.lw = lw;
+    win.valid = __ballot(lw > -INFINITY);
+    win.partial = __ballot(ragged && j == NBk - 1);
+    return win;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_fine_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
+    const int32_t *__restrict__ order, uint16_t *__restrict__ out, int N, int N_pad, int NBq, int NBk, int cap,
+    float scale_log2)
+{
+    static_assert(D == 128, "a 4-token key block of K or V^T is one 1024-byte direct load at D = 128");
+    using L = Lds<D>;
+    constexpr int KS = D / 16, DT = D / 32, KT = kSub / 32, NK = KT * KS, NV = KT * 2 * DT, PF = 4;
+    constexpr int GB = kFineBlock * D * 2;   // bytes of one 4-token block of K or V^T
+    constexpr int KL = kFineSub / kWaves;    // direct loads per wavefront and tensor per sub-tile
+    __shared__ __align__(16) char ks0[L::kBytes], ks1[L::kBytes], ks2[L::kBytes];
+    __shared__ __align__(16) char vs0[L::vBytes], vs1[L::vBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, half = lane >> 5;
+    const int slot = xcd_contiguous_id(blockIdx.x, gridDim.x);
+    const int blk = order[slot];
+    const int qb = blk % NBq;
+    const long bh = blk / NBq;
+    const uint16_t *qh = q + bh * N_pad * D;
+    const int4v rk = head_rsrc(k + bh * N_pad * D, N_pad * D * 2);
+    const int4v rv = head_rsrc(vt + bh * N_pad * D, N_pad * D * 2);
+
+    const int qrow = qb * kBlock + 32 * wave + l32;
+    const bool qvalid = qrow < N;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (qvalid) raw = *reinterpret_cast<const uint4 *>(qh + (long)qrow * D + 16 * ks + 8 * half);
+        qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+
+    floatx16 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m_run = -INFINITY, l_run0 = 0.f, l_run1 = 0.f;
+    const floatx16 zero16 = {};
+
+    int n_list = cnt[blk];
+    n_list = n_list < 0 ? 0 : (n_list > cap ? cap : n_list);
+    const int32_t *lrow = idx + (long)blk * cap;
+    const float *wrow = w + (long)blk * cap;
+    const int n_sub = (n_list + kFineSub - 1) / kFineSub;
+    const bool ragged = (N % kFineBlock) != 0;
+
+    int k_rd[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_rd[ks] = l32 * L::pitch + 16 * ((2 * ks + half) ^ k_swz<D>(l32));
+    auto k_frag = [&](const char *st, int i) __attribute__((always_inline)) {
+        return __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const uint4 *>(st + k_rd[i % KS] + (i / KS) * 32 * L::pitch));
+    };
+    // V^T fragment i = (ksub = 2 kt + sub, dt): block slots ga = 8kt + 4sub + half and ga + 2, dimension 32dt + l32
+    const int v_rd = half * GB + l32 * 8;
+    auto v_frag = [&](const char *st, int i) __attribute__((always_inline)) {
+        const int ksub = i / DT, dt = i % DT;
+        const int ga = 8 * (ksub >> 1) + 4 * (ksub & 1);
+        const uint2 a = *reinterpret_cast<const uint2 *>(st + v_rd + ga * GB + dt * 32 * 8);
+        const uint2 b = *reinterpret_cast<const uint2 *>(st + v_rd + (ga + 2) * GB + dt * 32 * 8);
+        return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+    };
+
+    // direct-load source offsets inside a 4-token block of K: lane L fills row
+    // L / 16 of the block, LDS chunk L % 16, which holds logical chunk
+    // (L % 16) ^ (LDS row % 16), and LDS row % 16 = 4t + L / 16 for load t
+    int koff[KL];
+#pragma unroll
+    for (int t = 0; t < KL; ++t) koff[t] = (lane >> 4) * L::pitch + 16 * ((lane & 15) ^ (4 * t + (lane >> 4)));
+
+    FineWindow win0 = load_fine_window(lrow, wrow, 0, n_list, NBk, ragged, lane);
+    FineWindow win1{0, -INFINITY, 0, 0};
+    // block to load for entry 16u + 4 wave + t (sub-tile u, this wavefront's load t)
+    auto block_of = [&](int u, int t) __attribute__((always_inline)) {
+        const int src = ((u >> 2) & 1) ? win1.j : win0.j;
+        return __builtin_amdgcn_readlane(src, 16 * (u & 3) + 4 * wave + t);
+    };
+    auto issue_k = [&](char *dst, int u) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < KL; ++t) load_lds16(rk, koff[t], block_of(u, t) * GB, dst + (KL * wave + t) * 1024);
+    };
+    auto issue_v = [&](char *dst, int u) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < KL; ++t) load_lds16(rv, 16 * lane, block_of(u, t) * GB, dst + (KL * wave + t) * 1024);
+    };
+
+    auto tile = [&](const char *kst, const char *vst, int u) __attribute__((always_inline)) {
+        const bool odd = (u >> 2) & 1;
+        const int base = 16 * (u & 3);
+        const float lw_src = odd ? win1.lw : win0.lw;
+        // log2 weights of this lane's 8 block slots 8kt + 2i + half
+        float lwe[KT][4];
+        float lwm = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = base + 8 * kt + 2 * i;
+                const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lw_src), e));
+                const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lw_src), e + 1));
+                lwe[kt][i] = half ? b : a;
+                lwm = max2(lwm, lwe[kt][i]);
+            }
+        lwm = half_pair_max(lwm);
+
+        floatx16 s[KT];
+        bf16x8 kf[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) kf[i] = k_frag(kst, i);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int kt = i / KS, ks = i % KS;
+            s[kt] = mfma32(kf[i % PF], qf[ks], ks == 0 ? zero16 : s[kt]);
+            if (i + PF < NK) kf[i % PF] = k_frag(kst, i + PF);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        bf16x8 vf[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) vf[i] = v_frag(vst, i);
+
+        const uint64_t pmask = odd ? win1.partial : win0.partial;
+        if ((pmask >> base) & 0xFFFFull) {   // keys past N: the partial last block is in this sub-tile
+            const int j_src = odd ? win1.j : win0.j;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = base + 8 * kt + 2 * i;
+                    const int ja = __builtin_amdgcn_readlane(j_src, e), jb = __builtin_amdgcn_readlane(j_src, e + 1);
+                    const int key0 = (half ? jb : ja) * kFineBlock;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (key0 + c >= N) s[kt][4 * i + c] = -INFINITY;
+                }
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (kt | r) mx = max2(mx, s[kt][r]);
+        const float m_tile = fmaf(half_pair_max(mx), scale_log2, lwm);
+        if (__ballot(m_tile > m_run + kRescaleSlack) != 0) {
+            asm volatile("s_nop 0");
+            const float m_new = max2(m_run, m_tile);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run0 *= alpha;
+            l_run1 *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        }
+        float bias[KT][4];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bias[kt][i] = lwe[kt][i] - m_run;
+        bf16x8 pb[KT][2];
+        auto prob = [&](int kt, int r) __attribute__((always_inline)) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, bias[kt][r >> 2]));
+            if (r & 1) l_run1 += pr; else l_run0 += pr;
+            pb[kt][r >> 3][r & 7] = (__bf16)pr;
+        };
+#pragma unroll
+        for (int r = 0; r < 16; ++r) prob(0, r);
+        constexpr int per = 16 / (NV / 2);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int ksub = i / DT, dt = i % DT;
+            o[dt] = mfma32(vf[i % PF], pb[ksub >> 1][ksub & 1], o[dt]);
+            if (i + PF < NV) vf[i % PF] = v_frag(vst, i + PF);
+            if (i < NV / 2) {
+#pragma unroll
+                for (int e = 0; e < per; ++e) prob(1, per * i + e);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // Sub-tile u: K in K slot u % 3, V^T in V slot u % 2.  Iteration u issues
+    // V^T(u + 1) and K(u + 2), computes u and waits for all but the K(u + 2)
+    // loads.  Window m (sub-tiles 4m .. 4m+3) sits in win{m % 2}; window m + 1 is
+    // read at iteration 4m, two iterations before its first use.  Unrolled six
+    // times, so that every slot is a compile-time offset.
+    auto kptr = [&](int sl) __attribute__((always_inline)) { return sl == 0 ? ks0 : (sl == 1 ? ks1 : ks2); };
+    auto vptr = [&](int sl) __attribute__((always_inline)) { return sl == 0 ? vs0 : vs1; };
+    auto sub_valid = [&](int u) __attribute__((always_inline)) {
+        const uint64_t vm = ((u >> 2) & 1) ? win1.valid : win0.valid;
+        return ((vm >> (16 * (u & 3))) & 0xFFFFull) != 0;
+    };
+    if (n_sub > 0) {
+        issue_k(kptr(0), 0);
+        issue_v(vptr(0), 0);
+    }
+    if (n_sub > 1) issue_k(kptr(1), 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    if (n_sub > 1) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
+    auto step = [&](auto u6c, int u) __attribute__((always_inline)) {
+        constexpr int U6 = decltype(u6c)::value;   // u % 6
+        const int u1 = u + 1, u2 = u + 2;
+        if ((u & 3) == 0 && u + 4 < n_sub) {
+            const FineWindow nw = load_fine_window(lrow, wrow, (u >> 2) + 1, n_list, NBk, ragged, lane);
+            if ((u >> 2) & 1) win0 = nw; else win1 = nw;
+        }
+        if (u1 < n_sub) issue_v(vptr((U6 + 1) % 2), u1);
+        if (u2 < n_sub) issue_k(kptr((U6 + 2) % 3), u2);
+        if (sub_valid(u)) tile(kptr(U6 % 3), vptr(U6 % 2), u);
+        if (u2 < n_sub) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
+    };
+    for (int u = 0; u < n_sub; u += 6) {
+        step(std::integral_constant<int, 0>{}, u);
+        if (u + 1 >= n_sub) break;
+        step(std::integral_constant<int, 1>{}, u + 1);
+        if (u + 2 >= n_sub) break;
+        step(std::integral_constant<int, 2>{}, u + 2);
+        if (u + 3 >= n_sub) break;
+        step(std::integral_constant<int, 3>{}, u + 3);
+        if (u + 4 >= n_sub) break;
+        step(std::integral_constant<int, 4>{}, u + 4);
+        if (u + 5 >= n_sub) break;
+        step(std::integral_constant<int, 5>{}, u + 5);
+    }
+
+    const float l_lane = l_run0 + l_run1;
+    const auto lr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
+    const float lsum = __uint_as_float(lr[0]) + __uint_as_float(lr[1]);
+    const float inv = (lsum > 0.f && qvalid) ? 1.f / lsum : 0.f;
+    uint16_t *orow = out + (bh * N_pad + qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = dt * 32 + 8 * g + 4 * half;
+            __bf16 b0 = (__bf16)(o[dt][4 * g + 0] * inv), b1 = (__bf16)(o[dt][4 * g + 1] * inv);
+            __bf16 b2 = (__bf16)(o[dt][4 * g + 2] * inv), b3 = (__bf16)(o[dt][4 * g + 3] * inv);
+            const uint32_t lo =
+                (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+            const uint32_t hi =
+                (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+            *reinterpret_cast<uint2 *>(orow + d) = make_uint2(lo, hi);
+        }
+}
+
+// fp32 inputs with 4-token key blocks: the fp32 kernel below, with 16 list
+// entries gathered into each 64-row key/value tile.
+template <int D>
+__global__ __launch_bounds__(256) void attend_f32_fine_kernel(const float *__restrict__ q, const float *__restrict__ k,
+                                                              const float *__restrict__ v, const int32_t *__restrict__ idx,
+                                                              const int32_t *__restrict__ cnt,
+                                                              const float *__restrict__ w, float *__restrict__ out,
+                                                              int N, int N_pad, int NBq, int NBk, int cap,
+                                                              float scale_log2)
+{
+    constexpr int kTile = 64, HD = D / 2, kChunk = 16;
+    __shared__ float4 k_s[kTile][D / 4];
+    __shared__ float4 v_s[kTile][D / 4];
+    __shared__ float lw_s[kTile];
+
+    const int tid = threadIdx.x;
+    const int blk = xcd_contiguous_id(blockIdx.x, gridDim.x);
+    const int qb = blk % NBq;
+    const long bh = blk / NBq;
+    const int r = tid >> 1, hd = tid & 1;
+    const int qrow = qb * kBlock + r;
+    const bool qvalid = qrow < N;
+    const float *kh = k + bh * N_pad * D, *vh = v + bh * N_pad * D;
+
+    float qv[HD], ov[HD];
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+        qv[d] = qvalid ? q[(bh * N_pad + qrow) * D + hd * HD + d] : 0.f;
+        ov[d] = 0.f;
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+    int n_list = cnt[blk];
+    n_list = n_list < 0 ? 0 : (n_list > cap ? cap : n_list);
+    for (int e0 = 0; e0 < n_list; e0 += kTile / kFineBlock) {
+        __syncthreads();
+        for (int i = tid; i < kTile * D / 4; i += 256) {
+            const int rr = i / (D / 4), c = i % (D / 4);
+            const int e = e0 + rr / kFineBlock;
+            int j = -1;
+            float wj = 0.f;
+            if (e < n_list) {
+                j = idx[(long)blk * cap + e];
+                wj = w[(long)blk * cap + e];
+                if (j < 0 || j >= NBk || !(wj > 0.f) || !(wj < INFINITY)) j = -1;
+            }
+            const int key = j * kFineBlock + rr % kFineBlock;
+            const bool ok = j >= 0 && key < N;
+            k_s[rr][c] = ok ? reinterpret_cast<const float4 *>(kh + (long)key * D)[c] : make_float4(0, 0, 0, 0);
+            v_s[rr][c] = ok ? reinterpret_cast<const float4 *>(vh + (long)key * D)[c] : make_float4(0, 0, 0, 0);
+            if (c == 0) lw_s[rr] = ok ? __log2f(wj) : -INFINITY;
+        }
+        __syncthreads();
+        for (int c0 = 0; c0 < kTile; c0 += kChunk) {
+            float lg[kChunk];
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int tt = 0; tt < kChunk; ++tt) {
+                const float *kr = reinterpret_cast<const float *>(&k_s[c0 + tt][0]) + hd * HD;
+                float dot = 0.f;
+#pragma unroll
+                for (int d = 0; d < HD; ++d) dot = fmaf(qv[d], kr[d], dot);
+                dot += __shfl_xor(dot, 1, 64);
+                const float lw = lw_s[c0 + tt];
+                lg[tt] = lw > -INFINITY ? fmaf(dot, scale_log2, lw) : -INFINITY;
+                cmax = fmaxf(cmax, lg[tt]);
+            }
+            if (cmax == -INFINITY) continue;   // nothing in this chunk (the same for every row)
+            const float m_new = fmaxf(m_run, cmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < HD; ++d) ov[d] *= alpha;
+#pragma unroll
+            for (int tt = 0; tt < kChunk; ++tt) {
+                const float p = __builtin_amdgcn_exp2f(lg[tt] - m_new);
+                l_run += p;
+                const float *vr = reinterpret_cast<const float *>(&v_s[c0 + tt][0]) + hd * HD;
+#pragma unroll
+                for (int d = 0; d < HD; ++d) ov[d] = fmaf(p, vr[d], ov[d]);
+            }
+        }
+    }
+    const float inv = (l_run > 0.f && qvalid) ? 1.f / l_run : 0.f;
+    float *orow = out + (bh * N_pad + qrow) * D + hd * HD;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) orow[d] = ov[d] * inv;
+}
+
 // ---------------------------------------------------------------------------
 // fp32 path: two lanes per query row, each owning half of the head dimension;
 // key/value tiles of 64 rows in LDS.
@@ -705,7 +1143,7 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
         int32_t *order = nullptr;
         if (!full) {
             order = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + vt_bytes(B, H, N_pad, D));
-            order_kernel<<<dim3(8), dim3(kOrderThreads), 0, s>>>(cnt, G, cap, order);
+            order_kernel<<<dim3(8), dim3(kOrderThreads), 0, s>>>(cnt, G, cap, 1, order);
         }
         if (D == 128) {
             vt_kernel<128><<<vt_grid, block, 0, s>>>((const uint16_t *)v, N, N_pad, vt);
@@ -719,6 +1157,33 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
     } else if (dtype == kF32 && D == 64) {
         attend_f32_kernel<64, full><<<grid, block, 0, s>>>((const float *)q, (const float *)k, (const float *)v, idx,
                                                           cnt, w, (float *)out, N, N_pad, NB, cap, sl2);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// Sparse attention over lists of 4-token key blocks.
+hipError_t launch_attend_fine(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad,
+                              int D, int NBq, int NBk, float scale, const int32_t *idx, const int32_t *cnt,
+                              const float *w, int cap, void *ws, void *out, hipStream_t s)
+{
+    const int G = B * H * NBq;
+    const float sl2 = scale * kLog2e;
+    if (dtype == kBF16 && D == 128) {
+        uint16_t *vt = static_cast<uint16_t *>(ws);
+        int32_t *order = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + vt_bytes(B, H, N_pad, D));
+        order_kernel<<<dim3(8), dim3(kOrderThreads), 0, s>>>(cnt, G, cap, kFineSub, order);
+        const long total = (long)B * H * NBk * (D / 2);
+        vtg_kernel<128><<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>((const uint16_t *)v, N, N_pad, NBk,
+                                                                                   total, vt);
+        attend_fine_kernel<128><<<dim3((unsigned)G), dim3(kThreads), 0, s>>>(
+            (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, order, (uint16_t *)out, N, N_pad, NBq, NBk, cap,
+            sl2);
+    } else if (dtype == kF32 && D == 64) {
+        attend_f32_fine_kernel<64><<<dim3((unsigned)G), dim3(256), 0, s>>>((const float *)q, (const float *)k,
+                                                                          (const float *)v, idx, cnt, w, (float *)out,
+                                                                          N, N_pad, NBq, NBk, cap, sl2);
     } else {
         return hipErrorInvalidValue;
     }

@@ -6,8 +6,10 @@
 // attention mass its blocks hold; the best K blocks hold the ideal top-K mass.
 // For a query block b' with n valid query rows,
 //     M[b', j] = (1/n) sum_i sum_{t in key block j} softmax_t(s q_i . k_t),
-// so every row of M sums to one.  Not on the attention path: it exists to
-// measure how much of M the sampled (or scored) blocks keep.
+// so every row of M sums to one.  Key blocks are 128 tokens, or 4 tokens for
+// the fine-grained selection of the page's kernel paragraph.  Not on the
+// attention path: it exists to measure how much of M the sampled (or scored)
+// blocks keep.
 //
 // One workgroup of 4 wavefronts per listed query block; wavefront w owns query
 // rows [32w, 32w + 32) as the MFMA column of S^T = K Q^T (32x32x16 bf16 MFMA,
@@ -25,22 +27,24 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D>
+template <int D, bool fine>
 __global__ __launch_bounds__(256) void block_mass_kernel(const uint16_t *__restrict__ q,
                                                          const uint16_t *__restrict__ k,
                                                          const int32_t *__restrict__ items, int B, int H, int N,
-                                                         int N_pad, int NB, float scale_log2, float *__restrict__ mass)
+                                                         int N_pad, int NB, int NBk, float scale_log2,
+                                                         float *__restrict__ mass)
 {
     constexpr int KS = D / 16;
-    __shared__ float part[4][kMaxBlocks];
+    constexpr int kPart = fine ? kBlock / kFineBlock : kMaxBlocks;   // per-wavefront partial sums kept in LDS
+    __shared__ float part[4][kPart];
     const int it = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
-    float *out = mass + (long)it * NB;
+    float *out = mass + (long)it * NBk;
 
     const int b = items[3 * it], h = items[3 * it + 1], qb = items[3 * it + 2];
     if (b < 0 || b >= B || h < 0 || h >= H || qb < 0 || qb >= NB) {   // an item outside the layer: zeros
-        for (int j = tid; j < NB; j += 256) out[j] = 0.f;
+        for (int j = tid; j < NBk; j += 256) out[j] = 0.f;
         return;
     }
     const long bh = (long)b * H + h;
@@ -95,35 +99,68 @@ __global__ __launch_bounds__(256) void block_mass_kernel(const uint16_t *__restr
     const float inv = qvalid ? 1.f / ((float)nq * l) : 0.f;
 
     // pass 2: normalised probabilities summed per key block
-    for (int j = 0; j < NB; ++j) {
-        float acc = 0.f;
-        for (int key0 = j * kBlock; key0 < min(N, (j + 1) * kBlock); key0 += 32) {
-            floatx16 s;
-            tile(key0, s);
+    if (!fine) {
+        for (int j = 0; j < NB; ++j) {
+            float acc = 0.f;
+            for (int key0 = j * kBlock; key0 < min(N, (j + 1) * kBlock); key0 += 32) {
+                floatx16 s;
+                tile(key0, s);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f(s[r] - m);
+                for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f(s[r] - m);
+            }
+            acc = wave_sum(acc * inv);
+            if (lane == 0) part[wave][j] = acc;
         }
-        acc = wave_sum(acc * inv);
-        if (lane == 0) part[wave][j] = acc;
+        __syncthreads();
+        for (int j = tid; j < NBk; j += 256) out[j] = part[0][j] + part[1][j] + part[2][j] + part[3][j];
+    } else {
+        // 4-token blocks: element r of a 32-key tile is in block key0/4 + 2(r/4) + half;
+        // each 128-key stretch fills part[][0..32) and is flushed after a barrier
+        for (int j = 0; j < NB; ++j) {
+            for (int t = 0; t < kBlock / 32; ++t) {
+                const int key0 = j * kBlock + 32 * t;
+                float g[4] = {0.f, 0.f, 0.f, 0.f};
+                if (key0 < N) {
+                    floatx16 s;
+                    tile(key0, s);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) g[r >> 2] += __builtin_amdgcn_exp2f(s[r] - m);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = g[i] * inv;
+#pragma unroll
+                    for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o, 64);   // over the 32 query lanes of a half
+                    if (l32 == 0) part[wave][8 * t + 2 * i + half] = x;
+                }
+            }
+            __syncthreads();
+            const int jj = j * kPart + tid;
+            if (tid < kPart && jj < NBk) out[jj] = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+            __syncthreads();
+        }
     }
-    __syncthreads();
-    for (int j = tid; j < NB; j += 256) out[j] = part[0][j] + part[1][j] + part[2][j] + part[3][j];
 }
 
 }  // namespace
 
 hipError_t launch_block_mass(const void *q, const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB,
-                             float scale, const int32_t *items, int n_items, float *mass, hipStream_t s)
+                             int kb, float scale, const int32_t *items, int n_items, float *mass, hipStream_t s)
 {
     if (n_items <= 0) return hipSuccess;
     const dim3 grid((unsigned)n_items), block(256);
     const float sl2 = scale * kLog2e;
-    if (dtype == kBF16 && D == 128)
-        block_mass_kernel<128><<<grid, block, 0, s>>>((const uint16_t *)q, (const uint16_t *)k, items, B, H, N, N_pad,
-                                                      NB, sl2, mass);
-    else if (dtype == kBF16 && D == 64)
-        block_mass_kernel<64><<<grid, block, 0, s>>>((const uint16_t *)q, (const uint16_t *)k, items, B, H, N, N_pad,
-                                                     NB, sl2, mass);
+    const int NBk = (N + kb - 1) / kb;
+    const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k;
+    if (dtype != kBF16 || (kb != kBlock && kb != kFineBlock)) return hipErrorInvalidValue;
+    if (D == 128 && kb == kBlock)
+        block_mass_kernel<128, false><<<grid, block, 0, s>>>(q16, k16, items, B, H, N, N_pad, NB, NBk, sl2, mass);
+    else if (D == 128)
+        block_mass_kernel<128, true><<<grid, block, 0, s>>>(q16, k16, items, B, H, N, N_pad, NB, NBk, sl2, mass);
+    else if (D == 64 && kb == kBlock)
+        block_mass_kernel<64, false><<<grid, block, 0, s>>>(q16, k16, items, B, H, N, N_pad, NB, NBk, sl2, mass);
+    else if (D == 64)
+        block_mass_kernel<64, true><<<grid, block, 0, s>>>(q16, k16, items, B, H, N, N_pad, NB, NBk, sl2, mass);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

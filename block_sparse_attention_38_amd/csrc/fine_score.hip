@@ -1,0 +1,374 @@
+// fine_score.hip -- IBCS pooling and scoring for 4-token key blocks (gfx950).
+//
+// AB-Attention page, section "Три приёма AB-Attention": key/value blocks of
+// only 4 tokens are selected while queries stay in 128-token blocks (kernel
+// paragraph), and every key block is scored by the cluster-weighted attention
+// of the query block's centroids to its averaged keys (IBCS paragraph):
+//     S[b', j] = sum_m w_m softmax_j(s c_m . kbar_j),  j over all 4-token blocks.
+// With 4-token blocks a query block scores N/4 key blocks (8190 at 32K
+// tokens), so the centroid x pooled-key contraction is a real matrix product
+// (2 * C * N/4 * D flops per query block) and runs on the bf16 MFMA.
+//
+// Precision.  Scores must stay within 1e-4 relative of an fp64 evaluation, which
+// bf16 operands (2^-9) cannot give.  Both operands are split into two bf16
+// parts, x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), and a logit is
+//     hi_c.hi_k + hi_c.lo_k + lo_c.hi_k
+// with fp32 accumulation: the dropped lo.lo term and the residuals of the
+// splits are below 2^-16 of |c||kbar| per term.
+//
+// Layout of the work.  The softmax over j needs each centroid's maximum and
+// normaliser over every key block before any score can be written, so there
+// are two passes over the same contraction, with a small merge in between:
+//   fine_score_kernel<D, false>  per (b, h, chunk of 256 key blocks): logits of
+//       every centroid of the head against the chunk; per centroid the chunk's
+//       max and sum of exponentials (log2 domain) -> partial[b,h,chunk,slot];
+//   fine_merge_kernel            per (b, h, slot): M = max over chunks,
+//       Z = sum over chunks; coef = w_m / Z -> stat[b,h,slot] = (M, coef);
+//   fine_score_kernel<D, true>   the same logits again; per query block and key
+//       block the sum over its centroids of coef * 2^(x - M) -> scores.
+// A workgroup keeps the split pooled keys of its chunk in registers (4
+// wavefronts x 64 key blocks, the MFMA operand of both passes) and streams the
+// head's centroids through LDS in tiles of 32 slots (4 query blocks x 8
+// slots; slots >= C are zero centroids with zero weight).  The stats pass uses
+// S^T orientation (rows = key blocks, columns = slots: one centroid per lane,
+// so its reductions over key blocks stay in the lane); the write pass uses S
+// orientation (rows = slots: a query block's 8 centroids are 4 accumulator
+// rows in each half of the wavefront, one permlane32 swap apart).  Both
+// passes evaluate identical MFMA sequences, so every logit of the write pass
+// is bitwise the one the stats pass saw and 2^(x - M) <= 1.
+#include "aba_internal.h"
+
+namespace aba {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSlots = 8;                         // centroid slots per query block
+constexpr int kTileSlots = 32;                    // slots per MFMA tile (4 query blocks)
+constexpr int kTileBlocks = kTileSlots / kSlots;
+constexpr int kChunk = 256;                       // key blocks per workgroup (64 per wavefront)
+
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Pooling: one thread per (b, h, key block, 8-element chunk of the row).  A
+// 4-token block of K is 4 consecutive rows, so consecutive threads read
+// consecutive 16-byte pieces of them.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fine_pool_kernel(const T *__restrict__ k, int N, int N_pad, int NBk,
+                                                        long total, float *__restrict__ kbar)
+{
+    constexpr int CH = D / 8;
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int c = (int)(i % CH);
+    const long row = i / CH;                      // (b*H + h) * NBk + j
+    const int j = (int)(row % NBk);
+    const long bh = row / NBk;
+    const int n = min(kFineBlock, N - j * kFineBlock);
+    const T *src = k + (bh * N_pad + (long)j * kFineBlock) * D + 8 * c;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = 0; r < n; ++r) {
+        float x[8];
+        load8(src + (long)r * D, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+    const float fn = (float)n;
+    float4 *dst = reinterpret_cast<float4 *>(kbar + row * D + 8 * c);
+    dst[0] = make_float4(acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn);
+    dst[1] = make_float4(acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn);
+}
+
+// bf16 split of eight floats: hi = bf16(x) (round to nearest even), lo = bf16(x - hi).
+__device__ __forceinline__ void split8(const float x[8], bf16x8 &hi, bf16x8 &lo)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)x[e];
+        hi[e] = h;
+        lo[e] = (__bf16)(x[e] - (float)h);
+    }
+}
+
+// LDS tile of 32 centroid slots: hi and lo parts, [32][D] bf16 each, 16-byte
+// chunk c of row r stored at c ^ (r % (D/8)), so that the 16 rows one phase of
+// a 128-bit read touches fall on different banks.
+template <int D> struct CentLds {
+    static constexpr int chunks = D / 8;
+    static constexpr int pitch = D * 2;
+    static constexpr int part = kTileSlots * pitch;   // bytes of hi (or lo)
+    static constexpr int bytes = 2 * part;
+    static constexpr int per_thread = kTileSlots * chunks / 256;   // chunks staged per thread
+};
+template <int D> __device__ __forceinline__ int cent_off(int r, int c)
+{
+    return r * CentLds<D>::pitch + 16 * (c ^ (r & (CentLds<D>::chunks - 1)));
+}
+
+template <int D, bool write>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fine_score_kernel(
+    const float *__restrict__ cent, const float *__restrict__ kbar, const float2 *__restrict__ stat, int NBq,
+    int NBk, int C, int n_chunks, int splits, float scale_log2, float2 *__restrict__ partial,
+    float *__restrict__ scores)
+{
+    using L = CentLds<D>;
+    constexpr int KS = D / 16;
+    __shared__ __align__(16) char ct_lds[2][L::bytes];
+    __shared__ float2 red[2][4][kTileSlots];
+    __shared__ float2 st_lds[2][kTileSlots];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int sp = blockIdx.x % splits;
+    const int chunk = (blockIdx.x / splits) % n_chunks;
+    const long bh = blockIdx.x / splits / n_chunks;
+    const int NT = (NBq + kTileBlocks - 1) / kTileBlocks;   // centroid tiles of the head
+
+    // split pooled keys of this wavefront's 64 key blocks: fragment (kt, ks) is
+    // block chunk*256 + 64 wave + 32 kt + l32, elements 16 ks + 8 half .. +7
+    const int j0 = chunk * kChunk + 64 * wave;
+    bf16x8 khi[2][KS], klo[2][KS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        const int j = j0 + 32 * kt + l32;
+        const float *row = kbar + (bh * NBk + j) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (j < NBk) load8(row + 16 * ks + 8 * half, x);
+            split8(x, khi[kt][ks], klo[kt][ks]);
+        }
+    }
+
+    // staging of centroid tile ct: thread stages chunks tid + 256 i (slot = chunk / (D/8))
+    auto fetch = [&](int ct, float (&x)[L::per_thread][8], float2 &st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < L::per_thread; ++i) {
+            const int ch = tid + 256 * i, s = ch / L::chunks, c = ch % L::chunks;
+            const int qb = kTileBlocks * ct + s / kSlots, m = s % kSlots;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+            if (qb < NBq && m < C) load8(cent + ((bh * NBq + qb) * C + m) * D + 8 * c, x[i]);
+        }
+        if (write && tid < kTileSlots) st = stat[bh * (long)NT * kTileSlots + (long)ct * kTileSlots + tid];
+    };
+    auto store = [&](int buf, const float (&x)[L::per_thread][8], const float2 &st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < L::per_thread; ++i) {
+            const int ch = tid + 256 * i, s = ch / L::chunks, c = ch % L::chunks;
+            bf16x8 hi, lo;
+            split8(x[i], hi, lo);
+            *reinterpret_cast<bf16x8 *>(ct_lds[buf] + cent_off<D>(s, c)) = hi;
+            *reinterpret_cast<bf16x8 *>(ct_lds[buf] + L::part + cent_off<D>(s, c)) = lo;
+        }
+        if (write && tid < kTileSlots) st_lds[buf][tid] = st;
+    };
+
+    int ct = sp;
+    {
+        float x[L::per_thread][8];
+        float2 st{0.f, 0.f};
+        if (ct < NT) {
+            fetch(ct, x, st);
+            store(0, x, st);
+        }
+    }
+    __syncthreads();
+    for (int it = 0; ct < NT; ct += splits, ++it) {
+        const int buf = it & 1;
+        const int nct = ct + splits;
+        float x[L::per_thread][8];
+        float2 st{0.f, 0.f};
+        if (nct < NT) fetch(nct, x, st);   // next tile's loads overlap this tile's MFMAs
+
+        const char *hi_base = ct_lds[buf], *lo_base = ct_lds[buf] + L::part;
+        floatx16 acc[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int off = cent_off<D>(l32, 2 * ks + half);
+            const bf16x8 chi = *reinterpret_cast<const bf16x8 *>(hi_base + off);
+            const bf16x8 clo = *reinterpret_cast<const bf16x8 *>(lo_base + off);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                if (!write) {   // rows = key blocks, columns = slots
+                    acc[kt] = mfma32(khi[kt][ks], chi, acc[kt]);
+                    acc[kt] = mfma32(klo[kt][ks], chi, acc[kt]);
+                    acc[kt] = mfma32(khi[kt][ks], clo, acc[kt]);
+                } else {        // rows = slots, columns = key blocks
+                    acc[kt] = mfma32(chi, khi[kt][ks], acc[kt]);
+                    acc[kt] = mfma32(chi, klo[kt][ks], acc[kt]);
+                    acc[kt] = mfma32(clo, khi[kt][ks], acc[kt]);
+                }
+            }
+        }
+
+        if (!write) {
+            // lane (l32, half) element r of tile kt: key block j0 + 32kt + 8(r/4) + 4half + r%4, slot l32
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = j0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+                    acc[kt][r] = j < NBk ? acc[kt][r] * scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, acc[kt][r]);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            float sum = 0.f;
+            if (mx > -INFINITY) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(acc[kt][r] - mx);
+            }
+            sum += __shfl_xor(sum, 32, 64);
+            if (half == 0) red[buf][wave][l32] = make_float2(mx, sum);
+        } else {
+            // lane (l32, half) element r of tile kt: slot 8(r/4) + 4half + r%4 (query block
+            // 4ct + r/4, centroid 4half + r%4), key block j0 + 32kt + l32
+            float2 sv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[r] = st_lds[buf][8 * (r >> 2) + 4 * half + (r & 3)];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                float part[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * p + i;
+                        a += sv[r].y * __builtin_amdgcn_exp2f(fmaf(acc[kt][r], scale_log2, -sv[r].x));
+                    }
+                    part[p] = a + __shfl_xor(a, 32, 64);
+                }
+                const int j = j0 + 32 * kt + l32;
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const int p = 2 * half + pp;
+                    const int qb = kTileBlocks * ct + p;
+                    if (j < NBk && qb < NBq) scores[(bh * NBq + qb) * NBk + j] = part[p];
+                }
+            }
+        }
+
+        if (nct < NT) store(buf ^ 1, x, st);
+        __syncthreads();
+        if (!write && tid < kTileSlots) {   // combine the four wavefronts' partials of this tile
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) M = fmaxf(M, red[buf][w][tid].x);
+            float Z = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float2 r = red[buf][w][tid];
+                if (r.x > -INFINITY) Z += r.y * __builtin_amdgcn_exp2f(r.x - M);
+            }
+            partial[((bh * n_chunks + chunk) * (long)NT + ct) * kTileSlots + tid] = make_float2(M, Z);
+        }
+    }
+}
+
+// Per (b, h, slot): maximum and normaliser over all chunks, and the slot's
+// coefficient w_m / Z (0 for slots >= C and for query blocks past the end).
+__global__ __launch_bounds__(256) void fine_merge_kernel(const float2 *__restrict__ partial,
+                                                         const float *__restrict__ weight, int NBq, int C,
+                                                         int n_chunks, long total, float2 *__restrict__ stat)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int NT = (NBq + kTileBlocks - 1) / kTileBlocks;
+    const int slot = (int)(i % ((long)NT * kTileSlots));
+    const long bh = i / ((long)NT * kTileSlots);
+    const int qb = slot / kSlots, m = slot % kSlots;
+    const float2 *p = partial + bh * n_chunks * (long)NT * kTileSlots + slot;
+    float M = -INFINITY;
+    for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, p[(long)c * NT * kTileSlots].x);
+    float Z = 0.f;
+    for (int c = 0; c < n_chunks; ++c) {
+        const float2 r = p[(long)c * NT * kTileSlots];
+        if (r.x > -INFINITY) Z += r.y * __builtin_amdgcn_exp2f(r.x - M);
+    }
+    float coef = 0.f;
+    if (qb < NBq && m < C && Z > 0.f) coef = weight[(bh * NBq + qb) * C + m] / Z;
+    stat[i] = make_float2(M, coef);
+}
+
+}  // namespace
+
+hipError_t launch_fine_pool(const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NBk, float *kbar,
+                            hipStream_t s)
+{
+    const long total = (long)B * H * NBk * (D / 8);
+    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+    if (dtype == kBF16 && D == 128)
+        fine_pool_kernel<uint16_t, 128><<<grid, block, 0, s>>>((const uint16_t *)k, N, N_pad, NBk, total, kbar);
+    else if (dtype == kBF16 && D == 64)
+        fine_pool_kernel<uint16_t, 64><<<grid, block, 0, s>>>((const uint16_t *)k, N, N_pad, NBk, total, kbar);
+    else if (dtype == kF32 && D == 64)
+        fine_pool_kernel<float, 64><<<grid, block, 0, s>>>((const float *)k, N, N_pad, NBk, total, kbar);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// Work split: enough workgroups to give every SIMD of the 256 CUs about three
+// wavefronts, each workgroup taking every splits-th centroid tile.
+static int fine_splits(long base_wgs, int NT)
+{
+    int sp = 1;
+    while (base_wgs * sp < 768 && sp * 2 <= NT) sp *= 2;
+    return sp;
+}
+
+size_t fine_score_workspace_bytes(int B, int H, int NBq, int NBk)
+{
+    const long NT = (NBq + kTileBlocks - 1) / kTileBlocks;
+    const long n_chunks = (NBk + kChunk - 1) / kChunk;
+    const size_t part = (size_t)B * H * n_chunks * NT * kTileSlots * sizeof(float2);
+    const size_t stat = (size_t)B * H * NT * kTileSlots * sizeof(float2);
+    return ((part + 255) & ~(size_t)255) + ((stat + 255) & ~(size_t)255);
+}
+
+hipError_t launch_fine_score(const float *cent, const float *weight, const float *kbar, int B, int H, int NBq, int NBk,
+                             int C, int D, float scale, void *ws, float *scores, hipStream_t s)
+{
+    if (C < 1 || C > kSlots) return hipErrorInvalidValue;
+    const int NT = (NBq + kTileBlocks - 1) / kTileBlocks;
+    const int n_chunks = (NBk + kChunk - 1) / kChunk;
+    const size_t part_bytes = (size_t)B * H * n_chunks * NT * kTileSlots * sizeof(float2);
+    float2 *partial = static_cast<float2 *>(ws);
+    float2 *stat = reinterpret_cast<float2 *>(static_cast<char *>(ws) + ((part_bytes + 255) & ~(size_t)255));
+    const long base = (long)B * H * n_chunks;
+    const int splits = fine_splits(base, NT);
+    const dim3 grid((unsigned)(base * splits)), block(256);
+    const float sl2 = scale * kLog2e;
+    const long slots = (long)B * H * NT * kTileSlots;
+    if (D == 128) {
+        fine_score_kernel<128, false><<<grid, block, 0, s>>>(cent, kbar, nullptr, NBq, NBk, C, n_chunks, splits, sl2,
+                                                             partial, nullptr);
+        fine_merge_kernel<<<dim3((unsigned)((slots + 255) / 256)), block, 0, s>>>(partial, weight, NBq, C, n_chunks,
+                                                                                 slots, stat);
+        fine_score_kernel<128, true><<<grid, block, 0, s>>>(cent, kbar, stat, NBq, NBk, C, n_chunks, splits, sl2,
+                                                            nullptr, scores);
+    } else if (D == 64) {
+        fine_score_kernel<64, false><<<grid, block, 0, s>>>(cent, kbar, nullptr, NBq, NBk, C, n_chunks, splits, sl2,
+                                                            partial, nullptr);
+        fine_merge_kernel<<<dim3((unsigned)((slots + 255) / 256)), block, 0, s>>>(partial, weight, NBq, C, n_chunks,
+                                                                                 slots, stat);
+        fine_score_kernel<64, true><<<grid, block, 0, s>>>(cent, kbar, stat, NBq, NBk, C, n_chunks, splits, sl2,
+                                                           nullptr, scores);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace aba

@@ -15,6 +15,7 @@ import math
 from dataclasses import dataclass, field
 
 BLOCK = 128          # tokens per query block and per key block
+FINE_BLOCK = 4       # tokens per key block of the fine-grained selection
 CLUSTERS = 8         # IBCS clusters per query block
 KMEANS_ITERS = 10    # Lloyd iterations
 
@@ -51,6 +52,16 @@ class Workload:
     def budget(self, density: float | None = None) -> int:
         d = self.densities[0] if density is None else density
         return budget_for(d, self.n_blocks)
+
+    @property
+    def n_fine_blocks(self) -> int:
+        return (self.seq_len + FINE_BLOCK - 1) // FINE_BLOCK
+
+    def fine_budget(self, density: float | None = None) -> int:
+        """Budget in 4-token key blocks with the same number of 128-key tiles as the
+        128-token budget (the page's kernel paragraph compares the two at a fixed
+        number of tiles)."""
+        return (BLOCK // FINE_BLOCK) * self.budget(density)
 
     @property
     def dense_flops(self) -> float:

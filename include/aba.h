@@ -57,11 +57,17 @@ typedef enum aba_status {
 
 typedef enum aba_dtype { ABA_F32 = 0, ABA_BF16 = 1 } aba_dtype;
 
-/* Block size of queries and keys: the page splits queries into 128-token blocks
- * (IBCS paragraph); key blocks use the same size here. */
+/* Query block size: the page splits queries into 128-token blocks (IBCS
+ * paragraph).  Key blocks are either the same 128 tokens or, as in the page's
+ * kernel paragraph, 4 tokens: the unit of selection is then smaller than the
+ * compute tile, and the kept 4-token blocks are gathered by index into full
+ * 128-key matrix-core tiles. */
 #define ABA_BLOCK 128
-/* Largest number of blocks per sequence (N <= 131072 tokens). */
+#define ABA_FINE_BLOCK 4
+/* Largest number of query blocks per sequence (N <= 131072 tokens), and of
+ * 4-token key blocks. */
 #define ABA_MAX_BLOCKS 1024
+#define ABA_MAX_KEY_BLOCKS 32768
 /* Largest number of clusters per query block (the page uses 8). */
 #define ABA_MAX_CLUSTERS 8
 
@@ -72,15 +78,17 @@ typedef struct aba_plan {
     int32_t heads;          /* H */
     int32_t seq_len;        /* N, valid tokens */
     int32_t head_dim;       /* D: 64 or 128 (ABA_F32: 64) */
-    int32_t block;          /* ABA_BLOCK */
-    int32_t n_blocks;       /* NB = ceil(N / 128) */
+    int32_t block;          /* ABA_BLOCK: tokens per query block */
+    int32_t n_blocks;       /* NB = ceil(N / 128) query blocks */
     int32_t seq_pad;        /* N_pad = 128 * NB */
     int32_t n_clusters;     /* C, 1..8 (the page: 8) */
     int32_t kmeans_iters;   /* T, Lloyd rounds (0..64) */
     int32_t budget;         /* K >= 1: expected kept key blocks per query block */
-    int32_t list_cap;       /* capacity of one sampled list = NB */
+    int32_t list_cap;       /* capacity of one sampled list = NBk */
     int32_t dtype;          /* aba_dtype of q, k, v, out */
     float softmax_scale;    /* s, 1/sqrt(D) unless given */
+    int32_t key_block;      /* tokens per key block: ABA_BLOCK or ABA_FINE_BLOCK */
+    int32_t n_key_blocks;   /* NBk = ceil(N / key_block) */
     int32_t reserved;
     uint64_t workspace_bytes; /* device scratch for aba_score (when its optional
                                  outputs are NULL), aba_attend and aba_attend_full;
@@ -89,30 +97,37 @@ typedef struct aba_plan {
                                  stream (calls that overlap in time need their own) */
 } aba_plan_t;
 
-/* Fill *p for a layer of `batch` x `heads` sequences of `seq_len` valid tokens.
- * softmax_scale <= 0 selects 1/sqrt(head_dim).  Host-only; launches nothing.
- * Returns ABA_E_INVALID for non-positive sizes, budget < 1 or a null p, and
- * ABA_E_UNSUPPORTED for a head_dim/dtype pair without kernels, more than
- * ABA_MAX_BLOCKS blocks or more than ABA_MAX_CLUSTERS clusters. */
+/* Fill *p for a layer of `batch` x `heads` sequences of `seq_len` valid tokens,
+ * selecting key blocks of `key_block` tokens (ABA_BLOCK or ABA_FINE_BLOCK) with
+ * an expected `budget` of them per query block (at equal attention work, a
+ * 4-token budget is 32 times the 128-token one).  softmax_scale <= 0 selects
+ * 1/sqrt(head_dim).  Host-only; launches nothing.
+ * Returns ABA_E_INVALID for non-positive sizes, budget < 1, a key_block other
+ * than 128 or 4, or a null p, and ABA_E_UNSUPPORTED for a head_dim/dtype pair
+ * without kernels (4-token key blocks: bf16 with head_dim 128, or fp32 with
+ * 64), more than ABA_MAX_BLOCKS query blocks, more than ABA_MAX_CLUSTERS
+ * clusters, or a 4-token budget whose sampling state exceeds the LDS of a CU
+ * (8 * 2^ceil(log2 K) + 4 * NBk bytes > 155648 when K < NBk). */
 aba_status aba_plan(aba_plan_t *p, int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
-                    aba_dtype dtype, int32_t n_clusters, int32_t kmeans_iters, int32_t budget,
+                    aba_dtype dtype, int32_t n_clusters, int32_t kmeans_iters, int32_t budget, int32_t key_block,
                     float softmax_scale);
 
 /* IBCS block scores (IBCS paragraph): for every (b, h, query block) cluster the
  * block's valid queries into C centroids with Lloyd k-means (strided initial
  * centroids q[floor(m*n/C)], T rounds of assign + update, ties to the lowest
  * index, an empty cluster keeps its centroid), weight each centroid by its
- * share of the block's queries, mean-pool every key block over its valid keys,
- * and score key block j by
+ * share of the block's queries, mean-pool every key block (of the plan's
+ * key_block tokens) over its valid keys, and score key block j by
  *     S[j] = sum_m w_m softmax_j(s * c_m . kbar_j).
  * Each row of scores sums to one.
  *   q, k       : [B,H,N_pad,D] in the plan's dtype
- *   scores     : out, float32 [B,H,NB,NB]
+ *   scores     : out, float32 [B,H,NB,NBk]
  *   centroids  : out, nullable, float32 [B,H,NB,C,D]
  *   cluster_w  : out, nullable, float32 [B,H,NB,C]
- *   pooled_k   : out, nullable, float32 [B,H,NB,D]
+ *   pooled_k   : out, nullable, float32 [B,H,NBk,D]
  *   workspace  : at least p->workspace_bytes of device memory (may be NULL only
- *                when all three optional outputs are given) */
+ *                for 128-token key blocks when all three optional outputs are
+ *                given) */
 aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *scores, float *centroids,
                      float *cluster_w, float *pooled_k, void *workspace, hipStream_t stream);
 
@@ -127,7 +142,7 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
  *   SC'11) with key (seed_lo, seed_hi) and counter (j >> 2, query block, h, b);
  *   block j is kept iff draw < theta_j, with weight w = float(2^32 / theta_j)
  *   (an fp64 division), the Horvitz-Thompson factor 1/pi.
- *   scores : float32 [B,H,NB,NB]
+ *   scores : float32 [B,H,NB,NBk]
  *   idx    : out, int32 [B,H,NB,list_cap], kept key blocks in ascending order
  *   cnt    : out, int32 [B,H,NB], number kept (>= 1)
  *   w      : out, float32 [B,H,NB,list_cap], weights of the listed blocks
@@ -138,11 +153,13 @@ aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, i
                       float *w, hipStream_t stream);
 
 /* Block-sparse attention over a sampling plan (SIP and kernel paragraphs).  For
- * each valid query i of query block b, with the kept list (j, w_j):
+ * each valid query i of query block b, with the kept list (j, w_j) of key
+ * blocks of the plan's key_block tokens:
  *     o_i = sum_j w_j sum_{t in j} e^{s q_i.k_t} v_t / sum_j w_j sum_{t in j} e^{s q_i.k_t}
  * i.e. softmax attention with the logits of block j shifted by ln w_j; keys
- * >= N are masked.  List entries outside [0, NB) are skipped; cnt is clamped
- * to [0, list_cap]; a query block with nothing to attend gets zeros.
+ * >= N are masked.  List entries outside [0, NBk) or with a weight that is not
+ * positive and finite are skipped; cnt is clamped to [0, list_cap]; a query
+ * block with nothing to attend gets zeros.
  *   q, k, v   : [B,H,N_pad,D];  idx, cnt, w : as produced by aba_sample
  *   out       : out, [B,H,N_pad,D] in the plan's dtype
  *   workspace : at least p->workspace_bytes of device memory; required for
@@ -153,14 +170,15 @@ aba_status aba_attend(const aba_plan_t *p, const void *q, const void *k, const v
 
 /* Dense softmax attention softmax(s q k^T) v over all valid keys, non-causal
  * (the full-attention reference of "Как мерили и что вышло").  Same layout,
- * workspace rule and output convention as aba_attend. */
+ * workspace rule and output convention as aba_attend; the key block size of
+ * the plan does not matter here. */
 aba_status aba_attend_full(const aba_plan_t *p, const void *q, const void *k, const void *v, void *out,
                            void *workspace, hipStream_t stream);
 
-/* Dense attention mass per key block, for judging a block selection (IBCS
- * paragraph and the opening of "Три приёма AB-Attention": the share of the
- * attention a selection keeps).  For each listed query block b' with n valid
- * query rows:
+/* Dense attention mass per key block (of the plan's key_block tokens), for
+ * judging a block selection (IBCS paragraph and the opening of "Три приёма
+ * AB-Attention": the share of the attention a selection keeps).  For each
+ * listed query block b' with n valid query rows:
  *     mass[item][j] = (1/n) sum_i sum_{t in key block j, t < N} softmax_t(s q_i . k_t)
  * so each row sums to one; its K largest entries sum to the ideal top-K mass.
  * ABA_BF16 only (ABA_E_UNSUPPORTED otherwise).  A diagnostic, off the attention
@@ -169,7 +187,7 @@ aba_status aba_attend_full(const aba_plan_t *p, const void *q, const void *k, co
  *   items   : device int32 [n_items][3] of (b, h, query block); an item outside
  *             the layer yields a row of zeros
  *   n_items : >= 0 (0 launches nothing)
- *   mass    : out, device float32 [n_items][NB] */
+ *   mass    : out, device float32 [n_items][NBk] */
 aba_status aba_block_mass(const aba_plan_t *p, const void *q, const void *k, const int32_t *items, int32_t n_items,
                           float *mass, hipStream_t stream);
 

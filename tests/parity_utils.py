@@ -33,6 +33,13 @@ def make_plan(aba, w: Workload, density: float | None = None, budget: int | None
     return aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, CLUSTERS, KMEANS_ITERS, K)
 
 
+def make_fine_plan(aba, w: Workload, density: float | None = None, budget: int | None = None):
+    """A plan with 4-token key blocks, at the 128-token budget's number of tiles unless given."""
+    K = w.fine_budget(density) if budget is None else budget
+    return aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, CLUSTERS, KMEANS_ITERS, K,
+                    key_block=aba.FINE_BLOCK)
+
+
 def att_tol(w: Workload) -> float:
     return ATT_ATOL_BF16 if w.dtype == "bf16" else ATT_ATOL_F32
 

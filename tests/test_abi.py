@@ -40,9 +40,10 @@ def test_library_exports_every_declared_symbol(aba):
 
 
 def test_plan_struct_matches_header_layout(aba):
-    # aba_plan_t: 14 int32/float fields then a uint64 -> 64 bytes
-    assert ctypes.sizeof(aba.PlanStruct) == 64
-    assert aba.PlanStruct.workspace_bytes.offset == 56
+    # aba_plan_t: 16 int32/float fields then a uint64 -> 72 bytes
+    assert ctypes.sizeof(aba.PlanStruct) == 72
+    assert aba.PlanStruct.key_block.offset == 52 and aba.PlanStruct.n_key_blocks.offset == 56
+    assert aba.PlanStruct.workspace_bytes.offset == 64
 
 
 def test_plan_fills_the_layer_sizes(aba):
@@ -56,6 +57,20 @@ def test_plan_fills_the_layer_sizes(aba):
     assert (p.n_blocks, p.seq_pad) == (929, 118912)
     p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 2, softmax_scale=0.5)
     assert p.softmax_scale == 0.5 and p.dtype == aba.ABA_F32
+    assert (p.key_block, p.n_key_blocks) == (128, 8)
+
+
+def test_fine_plan_fills_the_key_block_sizes(aba):
+    p = aba.plan(1, 12, 32760, 128, "bf16", 8, 10, 832, key_block=aba.FINE_BLOCK)
+    assert (p.key_block, p.n_key_blocks, p.list_cap, p.n_blocks, p.seq_pad) == (4, 8190, 8190, 256, 32768)
+    coarse = aba.plan(1, 12, 32760, 128, "bf16", 8, 10, 26)
+    # the pooled keys are 32x more, plus the scoring statistics
+    assert p.workspace_bytes >= coarse.workspace_bytes
+    assert p.workspace_bytes >= 4 * 12 * 8190 * 128
+    p = aba.plan(1, 24, 118800, 128, "bf16", 8, 10, 74 * 32, key_block=4)
+    assert (p.n_key_blocks, p.list_cap) == (29700, 29700)
+    p = aba.plan(1, 2, 1023, 64, "f32", 8, 10, 64, key_block=4)
+    assert p.n_key_blocks == 256                        # a partial last block of 3 tokens
 
 
 @pytest.mark.parametrize("args,status", [
@@ -68,6 +83,10 @@ def test_plan_fills_the_layer_sizes(aba):
     ((1, 1, 128, 128, "f32", 8, 10, 1), 2),           # fp32 only at head_dim 64
     ((1, 1, 128, 128, "bf16", 9, 10, 1), 2),          # more than 8 clusters
     ((1, 1, 1024 * 128 + 1, 128, "bf16", 8, 10, 1), 2),  # more than 1024 blocks
+    ((1, 1, 128, 128, "bf16", 8, 10, 1, 0.0, 8), 1),      # key blocks of neither 128 nor 4 tokens
+    ((1, 1, 128, 128, "bf16", 8, 10, 1, 0.0, 0), 1),
+    ((1, 1, 128, 64, "bf16", 8, 10, 1, 0.0, 4), 2),       # 4-token blocks with bf16 need head_dim 128
+    ((1, 1, 131072, 128, "bf16", 8, 10, 20000, 0.0, 4), 2),  # sampling state beyond the LDS of a CU
 ])
 def test_plan_rejects_bad_sizes(aba, args, status):
     with pytest.raises(aba.AbaError) as ei:
@@ -117,6 +136,21 @@ def test_tampered_plan_is_rejected(aba):
     fake = ctypes.c_void_p(1)
     assert lib.aba_attend_full(ctypes.byref(p.raw), fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
     assert b"inconsistent" in lib.aba_last_error()
+    p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 64, key_block=4)
+    p.raw.n_key_blocks = 8      # the 128-token count under a 4-token plan
+    assert lib.aba_attend_full(ctypes.byref(p.raw), fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
+    p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 64, key_block=4)
+    p.raw.key_block = 128       # fields of the other key block size
+    assert lib.aba_attend_full(ctypes.byref(p.raw), fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
+
+
+def test_fine_scores_always_need_a_workspace(aba):
+    lib = aba.load_library()
+    p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 64, key_block=4)
+    fake = ctypes.c_void_p(1)
+    # every optional output given, still no workspace: the two-pass scoring keeps its statistics there
+    assert lib.aba_score(ctypes.byref(p.raw), fake, fake, fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
+    assert b"workspace" in lib.aba_last_error()
 
 
 def test_binding_refuses_cpu_tensors(aba):
