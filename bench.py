@@ -54,15 +54,16 @@ def log(msg: str):
 
 def kept_flops(p, cnt: np.ndarray, idx: np.ndarray) -> float:
     """4 * D * sum over kept (query block, key block) pairs of valid queries x valid keys."""
-    N, NB = p.seq_len, p.n_blocks
-    valid = np.minimum(128, N - 128 * np.arange(NB)).astype(np.float64)   # valid tokens per block
+    N, NB, NBk, kb = p.seq_len, p.n_blocks, p.n_key_blocks, p.key_block
+    valid_q = np.minimum(128, N - 128 * np.arange(NB)).astype(np.float64)    # valid tokens per query block
+    valid_k = np.minimum(kb, N - kb * np.arange(NBk)).astype(np.float64)     # valid tokens per key block
     total = 0.0
     flat_c = cnt.reshape(-1, NB)
     flat_i = idx.reshape(-1, NB, idx.shape[-1])
     for r in range(flat_c.shape[0]):
         for qb in range(NB):
             c = int(flat_c[r, qb])
-            total += valid[qb] * valid[flat_i[r, qb, :c]].sum()
+            total += valid_q[qb] * valid_k[flat_i[r, qb, :c]].sum()
     return 4.0 * p.head_dim * total
 
 
@@ -90,6 +91,7 @@ def cpu_baseline(w, p, q, k, v, seed: int, target_s: float):
     import oracle
 
     N, NB, D = w.seq_len, w.n_blocks, w.head_dim
+    NBk, kb = p.n_key_blocks, p.key_block
     valid = np.minimum(128, N - 128 * np.arange(NB))
 
     def run(h, blocks):
@@ -101,15 +103,16 @@ def cpu_baseline(w, p, q, k, v, seed: int, target_s: float):
                                               T=p.kmeans_iters)
             cents.append(c)
             wts.append(wt)
-        kbar = oracle.pool(kh, N)
+        kbar = oracle.pool(kh, N, blk=kb)
         s = oracle.score(np.stack(cents)[None, None], np.stack(wts)[None, None], kbar, p.softmax_scale)
         idx_s, cnt_s, w_s, _ = oracle.sample(s.astype(np.float32), p.budget, seed)
-        idx = np.zeros((1, 1, NB, NB), np.int32)
+        idx = np.zeros((1, 1, NB, NBk), np.int32)
         cnt = np.zeros((1, 1, NB), np.int32)
-        wl = np.zeros((1, 1, NB, NB), np.float32)
+        wl = np.zeros((1, 1, NB, NBk), np.float32)
         for r, qb in enumerate(blocks):
             idx[0, 0, qb], cnt[0, 0, qb], wl[0, 0, qb] = idx_s[0, 0, r], cnt_s[0, 0, r], w_s[0, 0, r]
-        oracle.attend(qh, kh, vh, N, idx, cnt, wl, items=[(0, 0, qb) for qb in blocks], scale=p.softmax_scale)
+        oracle.attend(qh, kh, vh, N, idx, cnt, wl, items=[(0, 0, qb) for qb in blocks], scale=p.softmax_scale,
+                      kblk=kb)
         return time.perf_counter() - t0
 
     probe = list(range(0, NB, max(1, NB // 16)))[:16]
@@ -198,6 +201,121 @@ def selection_diagnostics(w, p, qkv, lists, ws, n_blocks: int):
         "sip_ht_weighted_mass": float(np.mean(ht)),
         "attention_rel_err_vs_dense": {"sip": rel_err(o_sip), "hard_topk": rel_err(o_top)},
     }
+
+
+def fine_leg(args, w, sets, density, coarse_plan, coarse_lists, dense_ms, n_diag: int, diagnostics: bool):
+    """The same layer with 4-token key blocks (the page's kernel paragraph) at the
+    number of 128-key tiles of the 128-token budget: score, sample and attend timed
+    over the same input sets, kept work, and (untimed) the dense attention mass the
+    ideal, IBCS and sampled selections keep at either granularity on the same
+    query blocks, with the attention error of both sampled lists against dense."""
+    dev = torch.device("cuda:0")
+    p = aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, CLUSTERS, KMEANS_ITERS, w.fine_budget(density),
+                 key_block=aba.FINE_BLOCK)
+    B, H, NB, NBk, cap = p.batch, p.heads, p.n_blocks, p.n_key_blocks, p.list_cap
+    ws = aba.workspace(p, dev)
+    scores = torch.empty(B, H, NB, NBk, dtype=torch.float32, device=dev)
+    lists = (torch.empty(B, H, NB, cap, dtype=torch.int32, device=dev),
+             torch.empty(B, H, NB, dtype=torch.int32, device=dev),
+             torch.empty(B, H, NB, cap, dtype=torch.float32, device=dev))
+    out = torch.empty_like(sets[0][0])
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        qd, kd, vd = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        aba.score(p, qd, kd, out=scores, ws=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        aba.sample(p, scores, args.seed + i % len(sets), out=lists)
+        if ev is not None:
+            ev[2].record(stream)
+        aba.attend(p, qd, kd, vd, *lists, out=out, ws=ws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(10, args.steps // 2)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(n):
+        step(i, evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / n
+    st = {k: float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+          for k, a, b in (("score", 0, 1), ("sample", 1, 2), ("attend", 2, 3))}
+    kfl, kept = [], []
+    set_lists = []
+    for i in range(len(sets)):
+        qd, kd, vd = sets[i]
+        s_i = aba.score(p, qd, kd, ws=ws)
+        l_i = aba.sample(p, s_i, args.seed + i)
+        idx, cnt, _ = (x.cpu().numpy() for x in l_i)
+        kfl.append(kept_flops(p, cnt, idx))
+        kept.append(float(cnt.mean()))
+        set_lists.append((s_i, l_i))
+    kflops = float(np.mean(kfl))
+    res = {
+        "key_block": p.key_block, "key_blocks": NBk, "budget_blocks": p.budget, "ms_per_step": ms,
+        "effective_tflops": w.dense_flops / (ms * 1e-3) / 1e12, "stages_ms": st,
+        "mean_kept_blocks": float(np.mean(kept)), "realised_density": float(np.mean(kept)) / NBk,
+        "kept_tflop_per_call": kflops / 1e12, "attend_kept_tflops": kflops / (st["attend"] * 1e-3) / 1e12,
+        "attend_kept_mfma_frac": kflops / (st["attend"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "speedup_vs_dense": {"layer": dense_ms / ms, "attention": dense_ms / st["attend"]} if dense_ms else None,
+    }
+    log(f"[bench] 4-token key blocks: {ms:.3f} ms/step (score {st['score']:.3f}, sample {st['sample']:.3f}, "
+        f"attend {st['attend']:.3f}); kept {res['mean_kept_blocks']:.1f} of {NBk}; "
+        f"attention {res['attend_kept_tflops']:.0f} TFLOP/s on kept blocks")
+    if not diagnostics:
+        return res
+
+    # selection quality at both granularities on the same sampled query blocks
+    qd, kd, vd = sets[0]
+    rng = np.random.default_rng(5)
+    items = sorted({(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(NB))) for _ in range(4 * n_diag)})
+    items = items[:max(n_diag, 32)]
+    it = np.array(items)
+    K, Kf = coarse_plan.budget, p.budget
+    mass_c = aba.block_mass(coarse_plan, qd, kd, items).double().cpu().numpy()
+    mass_f = aba.block_mass(p, qd, kd, items).double().cpu().numpy()
+    ideal_c = np.sort(mass_c, axis=1)[:, ::-1][:, :K].sum(axis=1)
+    ideal_f = np.sort(mass_f, axis=1)[:, ::-1][:, :Kf].sum(axis=1)
+    sc_f = set_lists[0][0].double().cpu().numpy()[it[:, 0], it[:, 1], it[:, 2]]
+    ibcs_f = np.take_along_axis(mass_f, np.argsort(-sc_f, axis=1, kind="stable")[:, :Kf], axis=1).sum(axis=1)
+    sc_c = coarse_lists[0].double().cpu().numpy()[it[:, 0], it[:, 1], it[:, 2]]
+    ibcs_c = np.take_along_axis(mass_c, np.argsort(-sc_c, axis=1, kind="stable")[:, :K], axis=1).sum(axis=1)
+
+    def sip_mass(mass, lists_):
+        idx, cnt, _ = (x.cpu().numpy() for x in lists_)
+        return float(np.mean([mass[r, idx[b, h, qb, :cnt[b, h, qb]]].sum() for r, (b, h, qb) in enumerate(items)]))
+
+    dense = aba.attend_full(p, qd, kd, vd, ws=ws)
+    o_f = aba.attend(p, qd, kd, vd, *set_lists[0][1], ws=ws)
+    o_c = aba.attend(coarse_plan, qd, kd, vd, *coarse_lists[1], ws=aba.workspace(coarse_plan, dev))
+    torch.cuda.synchronize()
+
+    def rel_err(o):
+        e = []
+        for b, h, qb in items:
+            nq = min(128, w.seq_len - 128 * qb)
+            ref = dense[b, h, 128 * qb:128 * qb + nq].float()
+            e.append(((o[b, h, 128 * qb:128 * qb + nq].float() - ref).norm() / ref.norm()).item())
+        return float(np.mean(e))
+
+    res["diagnostics"] = {
+        "query_blocks": len(items),
+        "ideal_topk_mass": {"128_token": float(ideal_c.mean()), "4_token": float(ideal_f.mean())},
+        "ibcs_topk_mass": {"128_token": float(ibcs_c.mean()), "4_token": float(ibcs_f.mean())},
+        "sip_kept_mass": {"128_token": sip_mass(mass_c, coarse_lists[1]), "4_token": sip_mass(mass_f, set_lists[0][1])},
+        "attention_rel_err_vs_dense": {"128_token": rel_err(o_c), "4_token": rel_err(o_f)},
+    }
+    log(f"[bench] 4-token diagnostics: {json.dumps(res['diagnostics'])}")
+    return res
 
 
 def run_sweep(args, w):
@@ -314,6 +432,10 @@ def main():
     ap.add_argument("--diag-blocks", type=int, default=32, help="sampled query blocks for the selection diagnostics")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--key-block", type=int, default=128, choices=(128, 4),
+                    help="key block size of the timed layer (4: the page's fine-grained selection)")
+    ap.add_argument("--no-fine", action="store_true",
+                    help="skip the 4-token key block measurement that follows the 128-token one")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -338,9 +460,11 @@ def main():
     sets = [tuple(x.to(dev) for x in hs) for hs in host_sets]
     log(f"[bench] {len(sets)} input sets ready in {time.perf_counter() - t0:.1f} s")
 
-    p = aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, CLUSTERS, KMEANS_ITERS, w.budget(density))
+    fine_main = args.key_block == aba.FINE_BLOCK
+    p = aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, CLUSTERS, KMEANS_ITERS,
+                 w.fine_budget(density) if fine_main else w.budget(density), key_block=args.key_block)
     B, H, NB, cap, D = p.batch, p.heads, p.n_blocks, p.list_cap, p.head_dim
-    scores = torch.empty(B, H, NB, NB, dtype=torch.float32, device=dev)
+    scores = torch.empty(B, H, NB, p.n_key_blocks, dtype=torch.float32, device=dev)
     ws = aba.workspace(p, dev)
     lists = (torch.empty(B, H, NB, cap, dtype=torch.int32, device=dev),
              torch.empty(B, H, NB, dtype=torch.int32, device=dev),
@@ -390,7 +514,7 @@ def main():
         l_i = aba.sample(p, s_i, args.seed + i)
         idx, cnt, wt = (x.cpu().numpy() for x in l_i)
         kflops_sets.append(kept_flops(p, cnt, idx))
-        dens_sets.append(float(cnt.mean() / NB))
+        dens_sets.append(float(cnt.mean() / p.n_key_blocks))
         set_lists.append((s_i, l_i))
     kflops = float(np.mean(kflops_sets))
     dense_flops = w.dense_flops
@@ -411,7 +535,7 @@ def main():
         log(f"[bench] dense attention: {dense_ms:.3f} ms")
 
     diagnostics = None
-    if not args.no_diagnostics and w.dtype == "bf16":
+    if not args.no_diagnostics and w.dtype == "bf16" and not fine_main:
         diagnostics = selection_diagnostics(w, p, sets[0], set_lists[0], ws, args.diag_blocks)
         log(f"[bench] diagnostics: {json.dumps(diagnostics)}")
 
@@ -424,9 +548,9 @@ def main():
 
     # scoring-stage bytes: q and k read once, centroids/weights/pooled keys written and re-read, scores written
     elem = 2 if w.dtype == "bf16" else 4
-    rows = B * H * NB
-    score_bytes = (2 * B * H * w.seq_len * D * elem
-                   + 2 * 4 * rows * (p.n_clusters * D + p.n_clusters + D) + 4 * rows * NB)
+    rows, krows = B * H * NB, B * H * p.n_key_blocks
+    score_bytes = (2 * B * H * w.seq_len * D * elem + 2 * 4 * rows * (p.n_clusters * D + p.n_clusters)
+                   + 2 * 4 * krows * D + 4 * rows * p.n_key_blocks)
     attend_tflops = kflops / (attend_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC,
@@ -444,8 +568,8 @@ def main():
         "config": {
             "workload": w.name, "batch": B, "heads": H, "seq_len": w.seq_len, "seq_pad": p.seq_pad,
             "head_dim": D, "grid": list(w.grid), "density": density, "budget_blocks": p.budget,
-            "clusters": p.n_clusters, "kmeans_iters": p.kmeans_iters, "block": 128, "seed": args.seed,
-            "input_sets": len(sets),
+            "clusters": p.n_clusters, "kmeans_iters": p.kmeans_iters, "block": 128, "key_block": p.key_block,
+            "seed": args.seed, "input_sets": len(sets),
         },
         "stages_ms": {"score": score_ms, "sample": sample_ms, "attend": attend_ms},
         "dense_attention_ms": dense_ms,
@@ -457,18 +581,23 @@ def main():
         "score_stage_hbm_frac": score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "roofline": {
             # the whole aba_attend call: the V^T copy and the work order are part of it
-            "kernel": ("aba_attend: vt_kernel<128> + order_kernel + attend_bf16_kernel<128,false>"
+            "kernel": (("aba_attend: vtg_kernel<128> + order_kernel + attend_fine_kernel<128>" if fine_main else
+                        "aba_attend: vt_kernel<128> + order_kernel + attend_bf16_kernel<128,false>")
                        if w.dtype == "bf16" else "aba_attend: attend_f32_kernel<64,false>"),
             "bound": "mfma",
             "achieved": attend_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attend_tflops / PEAK_BF16_TFLOPS,
-            "traffic": traffic_entry(),
+            "traffic": None if fine_main else traffic_entry(),
         },
         "diagnostics": diagnostics,
+        "fine_key_blocks": None,
         "cpu_baseline": None,
     }
+    if not fine_main and not args.no_fine and w.dtype == "bf16":
+        result["fine_key_blocks"] = fine_leg(args, w, sets, density, p, set_lists[0], dense_ms, args.diag_blocks,
+                                             not args.no_diagnostics)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         q, k, v = host_sets[0]

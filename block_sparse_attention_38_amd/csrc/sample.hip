@@ -15,6 +15,8 @@
 //   kept blocks compacted in ascending order with a workgroup prefix sum.
 #include "aba_internal.h"
 
+#include <array>
+
 namespace aba {
 namespace {
 
@@ -197,63 +199,86 @@ __global__ __launch_bounds__(256) void sample_kernel(const float *__restrict__ s
 // ---------------------------------------------------------------------------
 // Long rows (more than kMaxBlocks key blocks: 4-token key blocks give N/4 per
 // row).  The decisions are the ones above, bit for bit, without sorting the
-// row: the water-filling loop never looks past position min(K, NB) - 1 of the
-// sorted order, so only the top T = min(K, NB) keys (sigma desc, j asc) are
-// sorted.
-//   1. sigma - 1 of every block into LDS (uint32), row total;
-//   2. radix select (4 passes of 8 bits) of the T-th largest sigma, v, and
-//      how many of the blocks with sigma - 1 == v belong to the top T (the
-//      lowest indices among them);
-//   3. the top T gathered in index order (per-thread ranges + a workgroup
-//      scan) and bitonic-sorted by the packed key (sigma - 1) << 15 | ~j;
-//   4. the loop's stopping point t: the first position p >= 1 of the sorted
-//      prefix where (K - p) sigma_p < R_p (R_p = total - sum of the first p),
-//      found in parallel from a prefix sum, else min(K, NB);
-//   5. capped blocks are those whose key is >= the key at position t - 1;
+// row: the water-filling loop stops at the first position p >= 1 of the sorted
+// order where (K - p) sigma_p < R_p (R_p = total - sum of the first p), and
+// never looks past position min(K, NB) - 1, so only a sorted top of the row is
+// needed.
+//
+// Work is split in "quads" of 4 consecutive blocks (one Philox call, one
+// 16-byte LDS read): wavefront w owns a contiguous run of quads and its lane l
+// takes quad q0 + 64k + l at step k, so reads are conflict-free and every
+// ordered pass runs in index order.
+//   1. sigma - 1 of every block into LDS (uint32), the row total, min and max;
+//   2. top(T): the T-th largest sigma - 1, v, by a radix select over the row's
+//      own range [min, max] (8 bits per pass from the top of the range:
+//      per-wavefront LDS histograms, one atomic per wavefront when all its lanes
+//      fall in one bin; v = min directly when fewer than T blocks exceed it);
+//      when more blocks equal v than the top has room for, the lowest indices
+//      among them are taken (an 8-way bisection on the index).  The top T is
+//      gathered with wavefront-aggregated LDS atomics (order does not matter: it
+//      is sorted next, by the packed key (sigma - 1) << 15 | ~j);
+//   3. the stopping point: first with T = min(K, 64), sorted and scanned inside
+//      one wavefront with shuffles; when the loop stops inside that top (fewer
+//      than 64 blocks capped, the usual case) nothing more is needed;
+//      otherwise the top T = K is sorted by the whole workgroup in LDS and
+//      scanned in parallel;
+//   4. capped blocks are those whose key is >= the key at position t - 1;
 //      another block is kept iff draw < theta = ceil(x 2^32 / R) with x =
 //      (K - t) sigma, which for an integer draw is draw * R < x * 2^32, an
-//      exact 128-bit comparison; theta itself (for the weight) is formed only
-//      for kept blocks.  Kept blocks are written in index order.
+//      exact 128-bit comparison.  theta itself (for the weight) is formed only
+//      for kept blocks: an fp64 estimate (x 2^32 times 1/R), corrected to the
+//      exact ceiling with two 128-bit products.  Kept blocks are compacted in index order (a
+//      count pass, a scan over wavefronts, a write pass with a shuffle scan
+//      per step).
 // K >= NB caps every block (the loop then ends at t = NB), so that case keeps
-// everything with weight 1 and skips 2-5.
+// everything with weight 1 and skips 2-4.
 // ---------------------------------------------------------------------------
 constexpr int kKeyIdxBits = 15;                       // key blocks per row < 2^15
 constexpr uint32_t kKeyIdxMask = (1u << kKeyIdxBits) - 1;
+constexpr int kFastTop = 64;                          // sorted top tried first (one wavefront)
+constexpr int kMaxQuadSteps = kMaxFineBlocks / 4 / 256;   // quads per lane at most
 
 __device__ __forceinline__ uint64_t pack_key(uint32_t sig_m1, int j)
 {
     return ((uint64_t)sig_m1 << kKeyIdxBits) | (uint64_t)(kKeyIdxMask - (uint32_t)j);
 }
 
-// Exclusive prefix sum over the 256 threads of the workgroup (tmp: 4 slots).
-template <typename T> __device__ __forceinline__ T block_excl_scan(T v, T *tmp, T &total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    T inc = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const T y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += y;
-    }
-    if (lane == 63) tmp[wave] = inc;
-    __syncthreads();
-    T base = 0, all = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (i < wave) base += tmp[i];
-        all += tmp[i];
-    }
-    __syncthreads();
-    total = all;
-    return base + inc - v;
-}
-
-// 128-bit test a * b < c * 2^32 for a < 2^32, b, c < 2^63.
-__device__ __forceinline__ bool mul_less_shift32(uint64_t a, uint64_t b, uint64_t c)
+// 128-bit a * b for a < 2^33, b < 2^48, against c * 2^32 for c < 2^48.
+__device__ __forceinline__ int cmp_mul_shift32(uint64_t a, uint64_t b, uint64_t c)
 {
     const uint64_t lo = a * b, hi = __umul64hi(a, b);
     const uint64_t clo = c << 32, chi = c >> 32;
-    return hi < chi || (hi == chi && lo < clo);
+    if (hi != chi) return hi < chi ? -1 : 1;
+    return lo < clo ? -1 : (lo > clo ? 1 : 0);
+}
+
+// ceil(x * 2^32 / r) for 1 <= x < r < 2^48, given inv_r ~ 1/r in fp64: the
+// estimate is within a few 2^-52 relative of x 2^32 / r < 2^32, so its ceiling
+// is off by at most one; fixed exactly.
+__device__ __forceinline__ uint64_t ceil_ratio_shift32(uint64_t x, uint64_t r, double inv_r)
+{
+    uint64_t th = (uint64_t)ceil((double)x * 4294967296.0 * inv_r);
+    if (cmp_mul_shift32(th, r, x) < 0) ++th;                        // th * r < x 2^32: too small
+    else if (th > 0 && cmp_mul_shift32(th - 1, r, x) >= 0) --th;    // (th - 1) r >= x 2^32: too large
+    return th;
+}
+
+template <typename T> __device__ __forceinline__ T wave_sum_t(T x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+template <typename T> __device__ __forceinline__ T wave_incl_scan(T x, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const T y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
 }
 
 __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restrict__ scores, int H, int NBq, int NB,
@@ -262,36 +287,68 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
                                                           float *__restrict__ w)
 {
     extern __shared__ __align__(16) char dyn[];
-    uint64_t *top = reinterpret_cast<uint64_t *>(dyn);          // P sorted keys
-    uint32_t *sig = reinterpret_cast<uint32_t *>(dyn + 8 * (size_t)P);   // NB values sigma - 1
-    __shared__ int hist[256];
-    __shared__ int itmp[4];
-    __shared__ uint64_t utmp[4];
-    __shared__ int sel_s[2];          // radix digit, remaining count
-    __shared__ int t_s;
+    uint64_t *top = reinterpret_cast<uint64_t *>(dyn);                          // P keys
+    uint32_t *sig = reinterpret_cast<uint32_t *>(dyn + 16 * (((size_t)P + 1) / 2));   // 4 * NB4 values
+    __shared__ uint32_t red[2][4][4];
+    __shared__ int hist[4][256];
+    __shared__ int sel_s[3];
+    __shared__ uint64_t ured[4];
+    __shared__ uint32_t mm_s[2][4];
+    __shared__ int wtot[4];
+    __shared__ int top_n, t_s;
     __shared__ uint64_t r_s, cut_s;
 
     const int row = blockIdx.x;
     const int qb = row % NBq, h = (row / NBq) % H, b = row / (NBq * H);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float *srow = scores + (long)row * NB;
     int32_t *irow = idx + (long)row * cap;
     float *wrow = w + (long)row * cap;
 
-    // 1. fixed-point scores and the row total
-    uint64_t part = 0;
-    for (int j = tid; j < NB; j += 256) {
-        const uint64_t sg = fixed_point(srow[j]);
-        part += sg;
-        sig[j] = (uint32_t)(sg - 1);
-    }
-    uint64_t total;
-    block_excl_scan<uint64_t>(part, utmp, total);   // also a barrier: sig[] is complete
+    const int NB4 = (NB + 3) / 4;
+    const int Qw = ((NB4 + 3) / 4 + 63) / 64 * 64;   // quads per wavefront
+    const int steps = Qw / 64;
+    const int q0 = wave * Qw;
+    auto quad = [&](int k) { return q0 + 64 * k + lane; };   // valid if < NB4
 
-    // per-thread contiguous ranges of 4-aligned indices (one Philox block per 4)
-    const int per = 4 * ((((NB + 3) / 4) + 255) / 256);
-    const int lo_j = min(NB, tid * per), hi_j = min(NB, lo_j + per);
-    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    // 1. fixed-point scores, row total, min and max of sigma - 1
+    uint64_t part = 0;
+    uint32_t vmin = 0xFFFFFFFFu, vmax = 0;
+#pragma unroll 8
+    for (int k = 0; k < steps; ++k) {
+        const int q = quad(k);
+        if (q >= NB4) continue;
+        uint32_t x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * q + e;
+            x[e] = 0;
+            if (j < NB) {
+                const uint64_t sg = fixed_point(srow[j]);
+                part += sg;
+                x[e] = (uint32_t)(sg - 1);
+                vmin = min(vmin, x[e]);
+                vmax = max(vmax, x[e]);
+            }
+        }
+        *reinterpret_cast<uint4 *>(sig + 4 * q) = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+    part = wave_sum_t<uint64_t>(part);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        vmin = min(vmin, (uint32_t)__shfl_xor((int)vmin, o, 64));
+        vmax = max(vmax, (uint32_t)__shfl_xor((int)vmax, o, 64));
+    }
+    if (lane == 0) {
+        ured[wave] = part;
+        mm_s[0][wave] = vmin;
+        mm_s[1][wave] = vmax;
+    }
+    if (tid == 0) top_n = 0;
+    __syncthreads();
+    const uint64_t total = ured[0] + ured[1] + ured[2] + ured[3];
+    vmin = min(min(mm_s[0][0], mm_s[0][1]), min(mm_s[0][2], mm_s[0][3]));
+    vmax = max(max(mm_s[1][0], mm_s[1][1]), max(mm_s[1][2], mm_s[1][3]));
 
     if (K >= NB) {   // every block capped: keep all, weight 1
         for (int j = tid; j < NB; j += 256)
@@ -302,148 +359,323 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         if (tid == 0) cnt[row] = NB < cap ? NB : cap;
         return;
     }
-    const int T = K;   // K < NB here
 
-    // 2. radix select of the T-th largest sigma - 1
-    uint32_t prefix = 0, himask = 0;
-    int need = T;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        hist[tid] = 0;
-        __syncthreads();
-        for (int j = tid; j < NB; j += 256) {
-            const uint32_t v = sig[j];
-            if (((v ^ prefix) & himask) == 0) atomicAdd(&hist[(v >> shift) & 255], 1);
+    // Workgroup counts of a per-block predicate at 7 pivots (16-bit fields), one barrier.
+    int parity = 0;
+    auto count7 = [&](auto pred) {
+        uint32_t c[4] = {0, 0, 0, 0};
+#pragma unroll 4
+        for (int k = 0; k < steps; ++k) {
+            const int q = quad(k);
+            if (q >= NB4) continue;
+            const uint4 xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+            const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * q + e;
+                if (j >= NB) continue;
+#pragma unroll
+                for (int i = 0; i < 7; ++i) c[i >> 1] += (uint32_t)pred(xs[e], j, i) << (16 * (i & 1));
+            }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = wave_sum_t<uint32_t>(c[i]);
+        if (lane == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[parity][wave][i] = c[i];
         __syncthreads();
-        const int c = hist[255 - tid];                // digits from high to low
-        int tot;
-        const int before = block_excl_scan<int>(c, itmp, tot);
-        if (before < need && need <= before + c) {
-            sel_s[0] = 255 - tid;
-            sel_s[1] = need - before;
+        int out[7];
+#pragma unroll
+        for (int i = 0; i < 7; ++i) {
+            const uint32_t s4 = red[parity][0][i >> 1] + red[parity][1][i >> 1] + red[parity][2][i >> 1] +
+                                red[parity][3][i >> 1];
+            out[i] = (int)((s4 >> (16 * (i & 1))) & 0xFFFFu);
         }
-        __syncthreads();
-        prefix |= (uint32_t)sel_s[0] << shift;
-        himask |= 255u << shift;
-        need = sel_s[1];
-    }
-    const uint32_t v = prefix;   // T-th largest sigma - 1; `need` of its ties (lowest j) are in the top T
+        parity ^= 1;
+        return std::array<int, 7>{out[0], out[1], out[2], out[3], out[4], out[5], out[6]};
+    };
 
-    // 3. gather the top T in index order, then sort them
-    int n_gt = 0, n_eq = 0;
-    for (int j = lo_j; j < hi_j; ++j) {
-        const uint32_t x = sig[j];
-        n_gt += x > v;
-        n_eq += x == v;
-    }
-    int tot_packed;
-    const int base_packed = block_excl_scan<int>((n_gt << 16) | n_eq, itmp, tot_packed);
-    int gt_before = base_packed >> 16, eq_before = base_packed & 0xFFFF;
-    for (int j = lo_j; j < hi_j; ++j) {
-        const uint32_t x = sig[j];
-        if (x > v) {
-            top[gt_before + min(eq_before, need)] = pack_key(x, j);
-            ++gt_before;
-        } else if (x == v) {
-            if (eq_before < need) top[gt_before + eq_before] = pack_key(x, j);
-            ++eq_before;
+    // 2. gathers the top T (unsorted) into top[0 .. T), pads top[T .. PT) with 0
+    auto gather_top = [&](int T, int PT) {
+        // v: the T-th largest sigma - 1; need: how many blocks equal to v are in the top; n_eq: blocks equal to v
+        uint32_t v;
+        int need, n_eq;
+        {
+            // shortcut: fewer than T blocks above the minimum (rows whose scores mostly underflow)
+            int above = 0;
+            for (int k = 0; k < steps; ++k) {
+                const int q = quad(k);
+                if (q >= NB4) continue;
+                const uint4 xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+                const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) above += (4 * q + e < NB) && xs[e] > vmin;
+            }
+            above = wave_sum_t<int>(above);
+            if (lane == 0) wtot[wave] = above;
+            __syncthreads();
+            above = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+            __syncthreads();
+            if (above < T) {
+                v = vmin;
+                need = T - above;
+                n_eq = NB - above;
+            } else {
+                // radix select over [vmin, vmax], 8 bits per pass from the top of the range
+                uint32_t base = vmin;
+                int bits = 0;
+                while (bits < 32 && ((uint64_t)(vmax - vmin) >> bits) != 0) ++bits;   // range < 2^bits
+                int rem = T;   // blocks still needed from the current range [base, base + 2^bits)
+                int cnt_bin = 0;
+                for (;;) {
+                    const int shift = bits > 8 ? bits - 8 : 0;
+                    hist[wave][lane] = 0;
+                    hist[wave][lane + 64] = 0;
+                    hist[wave][lane + 128] = 0;
+                    hist[wave][lane + 192] = 0;
+                    __syncthreads();
+                    for (int k = 0; k < steps; ++k) {
+                        const int q = quad(k);
+                        uint4 xv = make_uint4(0, 0, 0, 0);
+                        if (q < NB4) xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+                        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint64_t off = (uint64_t)xs[e] - base;
+                            const bool in = q < NB4 && 4 * q + e < NB && xs[e] >= base && (off >> bits) == 0;
+                            const int bin = in ? (int)(off >> shift) : -1;
+                            const int b0 = __builtin_amdgcn_readfirstlane(bin);
+                            const uint64_t same = __ballot(bin == b0);
+                            if (same == ~0ull) {   // the whole wavefront in one bin: one atomic
+                                if (lane == 0 && b0 >= 0) atomicAdd(&hist[wave][b0], 64);
+                            } else if (in) {
+                                atomicAdd(&hist[wave][bin], 1);
+                            }
+                        }
+                    }
+                    __syncthreads();
+                    const int bb = 255 - tid;   // bins from the top
+                    const int c = hist[0][bb] + hist[1][bb] + hist[2][bb] + hist[3][bb];
+                    const int incl = wave_incl_scan<int>(c, lane);
+                    if (lane == 63) wtot[wave] = incl;
+                    __syncthreads();
+                    int before = incl - c;
+                    for (int i = 0; i < wave; ++i) before += wtot[i];
+                    if (before < rem && rem <= before + c) {
+                        sel_s[0] = bb;
+                        sel_s[1] = rem - before;
+                        sel_s[2] = c;
+                    }
+                    __syncthreads();
+                    base += (uint32_t)sel_s[0] << shift;
+                    rem = sel_s[1];
+                    cnt_bin = sel_s[2];
+                    bits = shift;
+                    __syncthreads();   // sel_s and wtot are rewritten by the next pass
+                    if (shift == 0) break;
+                }
+                v = base;
+                need = rem;
+                n_eq = cnt_bin;
+            }
         }
-    }
-    for (int i = T + tid; i < P; i += 256) top[i] = 0;   // below every real key (or equal to, and decoding alike)
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < P / 2; i += 256) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = ((lo & size) == 0);
-                const uint64_t a = top[lo], c = top[hi];
-                if ((a < c) == desc) {
-                    top[lo] = c;
-                    top[hi] = a;
+        int jcut = NB;                          // those with index < jcut
+        if (n_eq > need) {                      // more ties at v than room: the lowest indices
+            int jl = 0, jh = NB;                // count(eq, j < jl) < need <= count(eq, j < jh)
+            while (jh - jl > 1) {
+                int piv[7];
+#pragma unroll
+                for (int i = 0; i < 7; ++i) piv[i] = jl + (int)(((int64_t)(jh - jl) * (i + 1)) / 8);
+                const auto c = count7([&](uint32_t x, int j, int i) { return x == v && j < piv[i]; });
+                int njl = jl, njh = jh;
+#pragma unroll
+                for (int i = 0; i < 7; ++i) {
+                    if (c[i] < need) njl = max(njl, piv[i]);
+                    else njh = min(njh, piv[i]);
+                }
+                jl = njl;
+                jh = njh;
+            }
+            jcut = jh;
+        }
+        for (int k = 0; k < steps; ++k) {
+            const int q = quad(k);
+            uint4 xv = make_uint4(0, 0, 0, 0);
+            if (q < NB4) xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+            const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * q + e;
+                const bool sel = q < NB4 && j < NB && (xs[e] > v || (xs[e] == v && j < jcut));
+                const uint64_t bal = __ballot(sel);
+                if (bal) {
+                    int base = 0;
+                    if (lane == __builtin_ctzll(bal)) base = atomicAdd(&top_n, __popcll(bal));
+                    base = __shfl(base, __builtin_ctzll(bal), 64);
+                    if (sel) top[base + __popcll(bal & ((1ull << lane) - 1))] = pack_key(xs[e], j);
                 }
             }
-            __syncthreads();
         }
-    }
+        for (int i = T + tid; i < PT; i += 256) top[i] = 0;   // below every real key (or equal, decoding alike)
+        __syncthreads();
+    };
 
-    // 4. stopping point of the water-filling loop over positions 1 .. T-1
-    if (tid == 0) t_s = T;
-    const int q = (T + 255) / 256;
-    const int p0 = min(T, tid * q), p1 = min(T, p0 + q);
-    uint64_t local = 0;
-    for (int p = p0; p < p1; ++p) local += (top[p] >> kKeyIdxBits) + 1;
-    uint64_t dummy;
-    uint64_t pre = block_excl_scan<uint64_t>(local, utmp, dummy);   // barrier: t_s is set
-    for (int p = p0; p < p1; ++p) {
-        const uint64_t sg = (top[p] >> kKeyIdxBits) + 1;
-        if (p >= 1 && (uint64_t)(K - p) * sg < total - pre) {
-            atomicMin(&t_s, p);
-            break;
+    int t = 0;
+    {   // fast path: the top min(K, 64), sorted and scanned by wavefront 0
+        const int T = min(K, kFastTop);
+        gather_top(T, kFastTop);
+        if (wave == 0) {
+            uint64_t key = top[lane];
+#pragma unroll
+            for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    const uint64_t other = __shfl_xor(key, stride, 64);
+                    const bool desc = (lane & size) == 0, lower = (lane & stride) == 0;
+                    const uint64_t mx = key > other ? key : other, mn = key > other ? other : key;
+                    key = (lower == desc) ? mx : mn;
+                }
+            const uint64_t sg = lane < T ? (key >> kKeyIdxBits) + 1 : 0;
+            const uint64_t incl = wave_incl_scan<uint64_t>(sg, lane);
+            const bool fail = lane >= 1 && lane < T && (uint64_t)(K - lane) * sg < total - (incl - sg);
+            const uint64_t fb = __ballot(fail);
+            int tt = fb ? __builtin_ctzll(fb) : T;
+            const bool found = tt < T || T == K;
+            if (found) {
+                const uint64_t r = total - __shfl(incl, tt - 1, 64);
+                const uint64_t c = __shfl(key, tt - 1, 64);
+                if (lane == 0) {
+                    r_s = r;
+                    cut_s = c;
+                }
+            }
+            if (lane == 0) t_s = found ? tt : 0;
         }
-        pre += sg;
+        __syncthreads();
+        t = t_s;
     }
-    __syncthreads();
-    const int t = t_s;
-    if (tid == 0) cut_s = top[t - 1];
-    {   // R = total - (sum of the first t sorted sigma)
-        uint64_t pre2 = block_excl_scan<uint64_t>(local, utmp, dummy);
+    if (t == 0) {   // 64 or more blocks capped: the top K, sorted by the workgroup
+        if (tid == 0) top_n = 0;
+        __syncthreads();
+        int PT = 1;
+        while (PT < K) PT <<= 1;
+        gather_top(K, PT);
+        for (int size = 2; size <= PT; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = tid; i < PT / 2; i += 256) {
+                    const int a = 2 * i - (i & (stride - 1));
+                    const int c = a + stride;
+                    const bool desc = ((a & size) == 0);
+                    const uint64_t x = top[a], y = top[c];
+                    if ((x < y) == desc) {
+                        top[a] = y;
+                        top[c] = x;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // first failure at a position 1 .. K-1, else K
+        if (tid == 0) t_s = K;
+        const int qn = (K + 255) / 256;
+        const int p0 = min(K, tid * qn), p1 = min(K, p0 + qn);
+        uint64_t local = 0;
+        for (int p = p0; p < p1; ++p) local += (top[p] >> kKeyIdxBits) + 1;
+        const uint64_t wincl = wave_incl_scan<uint64_t>(local, lane);
+        if (lane == 63) ured[wave] = wincl;
+        __syncthreads();
+        uint64_t pre = wincl - local;
+        for (int i = 0; i < wave; ++i) pre += ured[i];
+        const uint64_t pre0 = pre;
         for (int p = p0; p < p1; ++p) {
             const uint64_t sg = (top[p] >> kKeyIdxBits) + 1;
-            if (p == t - 1) r_s = total - (pre2 + sg);
-            pre2 += sg;
+            if (p >= 1 && (uint64_t)(K - p) * sg < total - pre) {
+                atomicMin(&t_s, p);
+                break;
+            }
+            pre += sg;
         }
+        __syncthreads();
+        t = t_s;
+        pre = pre0;
+        for (int p = p0; p < p1; ++p) {
+            const uint64_t sg = (top[p] >> kKeyIdxBits) + 1;
+            if (p == t - 1) {
+                r_s = total - (pre + sg);
+                cut_s = top[p];
+            }
+            pre += sg;
+        }
+        __syncthreads();
     }
-    __syncthreads();
     const uint64_t R = r_s, cut = cut_s;
-    const uint64_t Kt = (uint64_t)(K - t);   // >= 0 since t <= T = K
+    const uint64_t Kt = (uint64_t)(K - t);   // >= 0 since t <= K
 
-    // 5. keep decisions over this thread's range, then the compaction in index order
-    uint32_t mask[(kMaxFineBlocks / 256 + 31) / 32] = {};
+    // 4. keep decisions (4 bits per quad step), then the compaction in index order
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    uint32_t bits[(kMaxQuadSteps + 7) / 8] = {};
     int mine = 0;
-    // a non-empty range starts at a multiple of 4 (ranges past the row are empty
-    // and start at NB, which need not be one)
-    for (int g = lo_j / 4; lo_j < hi_j && 4 * g < hi_j; ++g) {
-        const uint4 r = philox4x32_10(make_uint4((uint32_t)g, (uint32_t)qb, (uint32_t)h, (uint32_t)b), k0, k1);
+#pragma unroll 2
+    for (int k = 0; k < steps; ++k) {
+        const int q = quad(k);
+        if (q >= NB4) continue;
+        const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)qb, (uint32_t)h, (uint32_t)b), k0, k1);
         const uint32_t draw[4] = {r.x, r.y, r.z, r.w};
+        const uint4 xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        uint32_t nib = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int j = 4 * g + e;
-            if (j >= hi_j) break;
-            const uint32_t x = sig[j];
+            const int j = 4 * q + e;
+            if (j >= NB) continue;
             bool keep;
-            if (pack_key(x, j) >= cut) keep = true;
-            else if (Kt == 0) keep = draw[e] == 0;                       // theta = 1
-            else keep = mul_less_shift32(draw[e], R, Kt * ((uint64_t)x + 1));
-            if (keep) {
-                const int o = j - lo_j;
-                mask[o >> 5] |= 1u << (o & 31);
-                ++mine;
-            }
+            if (pack_key(xs[e], j) >= cut) keep = true;
+            else if (Kt == 0) keep = draw[e] == 0;                                     // theta = 1
+            else keep = cmp_mul_shift32(draw[e], R, Kt * ((uint64_t)xs[e] + 1)) < 0;   // draw R < x 2^32
+            nib |= (uint32_t)keep << e;
         }
+        bits[k >> 3] |= nib << (4 * (k & 7));
+        mine += __popc(nib);
     }
-    int kept_total;
-    int pos = block_excl_scan<int>(mine, itmp, kept_total);
-    for (int o = 0; lo_j + o < hi_j; ++o) {
-        if (!(mask[o >> 5] & (1u << (o & 31)))) continue;
-        const int j = lo_j + o;
-        if (pos < cap) {
-            const uint32_t x = sig[j];
-            uint64_t th;
-            if (pack_key(x, j) >= cut) {
-                th = kOne;
-            } else if (Kt == 0) {
-                th = 1;
-            } else {
-                const uint64_t xx = Kt * ((uint64_t)x + 1);
-                th = (xx >= R) ? kOne : ceil_scaled_ratio(xx, R);
-                th = th < 1 ? 1 : (th > kOne ? kOne : th);
+    mine = wave_sum_t<int>(mine);
+    if (lane == 0) wtot[wave] = mine;
+    __syncthreads();
+    int running = 0, kept_total = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < wave) running += wtot[i];
+        kept_total += wtot[i];
+    }
+    const double inv_r = R > 0 ? 1.0 / (double)R : 0.0;
+    for (int k = 0; k < steps; ++k) {
+        const uint32_t nib = (bits[k >> 3] >> (4 * (k & 7))) & 15u;
+        const int c = __popc(nib);
+        const int incl = wave_incl_scan<int>(c, lane);
+        int pos = running + incl - c;
+        running += __shfl(incl, 63, 64);
+        if (!nib) continue;
+        const int q = quad(k);
+        const uint4 xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+        for (uint32_t rest = nib; rest; rest &= rest - 1) {
+            const int e = __builtin_ctz(rest);
+            const int j = 4 * q + e;
+            if (pos < cap) {
+                uint64_t th;
+                if (pack_key(xs[e], j) >= cut) {
+                    th = kOne;
+                } else if (Kt == 0) {
+                    th = 1;
+                } else {
+                    const uint64_t xx = Kt * ((uint64_t)xs[e] + 1);
+                    th = (xx >= R) ? kOne : ceil_ratio_shift32(xx, R, inv_r);
+                    th = th < 1 ? 1 : (th > kOne ? kOne : th);
+                }
+                irow[pos] = j;
+                wrow[pos] = (float)(4294967296.0 / (double)th);
             }
-            irow[pos] = j;
-            wrow[pos] = (float)(4294967296.0 / (double)th);
+            ++pos;
         }
-        ++pos;
     }
     if (tid == 0) cnt[row] = kept_total < cap ? kept_total : cap;
 }
@@ -454,7 +686,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
 // followed by sigma - 1 of every block.
 static int topk_pad(int NB, int K)
 {
-    int P = 1;
+    int P = kFastTop;
     while (K < NB && P < K) P <<= 1;
     return P;
 }
@@ -462,7 +694,8 @@ static int topk_pad(int NB, int K)
 size_t sample_lds_bytes(int NB, int K)
 {
     if (NB <= kMaxBlocks) return 0;
-    return 8 * (size_t)topk_pad(NB, K) + 4 * (size_t)NB;
+    const size_t P = (size_t)topk_pad(NB, K);
+    return 16 * ((P + 1) / 2) + 16 * (((size_t)NB + 3) / 4);
 }
 
 hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int cap,
