@@ -99,4 +99,57 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+// ---------------------------------------------------------------------------
+// Buffer -> LDS direct loads (used by the attention and 4-token scoring kernels)
+// ---------------------------------------------------------------------------
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over one slice of device memory (base, stride 0, size in
+// bytes, raw dword access): the loads below address it by byte offset, and the
+// hardware range check returns zeros past its end.
+__device__ __forceinline__ int4v head_rsrc(const void *base, int bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return int4v{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)), bytes, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_address(char *p)
+{
+    return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)p);
+}
+
+// Direct copy of 16 bytes per lane from a buffer into LDS: lane L's bytes land
+// at dst + 16 L (dst is wavefront-uniform; M0 holds its LDS address).  Issued
+// as inline assembly: the compiler then does not track these LDS writes, and
+// would otherwise wait for every copy in flight before each LDS read it cannot
+// prove disjoint from them.  Ordering is explicit instead: a slot is read only
+// after wait_loads_and_sync has covered the copies into it, and is refilled
+// only after the barrier that follows its last read.
+__device__ __forceinline__ void load_lds16(int4v rs, int voff, int soff, char *dst)
+{
+    const uint32_t m0 = lds_address(dst);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
+                 : "memory");
+}
+
+// The same with 4 bytes per lane (lane L's bytes land at dst + 4 L).
+__device__ __forceinline__ void load_lds4(int4v rs, int voff, int soff, char *dst)
+{
+    const uint32_t m0 = lds_address(dst);
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
+                 : "memory");
+}
+
+// Wait until at most n of this wavefront's vector memory operations are in
+// flight (they complete in issue order), then meet the other wavefronts: their
+// direct loads up to the same point are then in LDS as well.  A bare
+// s_barrier: the workgroup fence of __syncthreads would also wait for the loads
+// that are meant to stay in flight.  Every LDS read before the barrier has been
+// consumed by then.
+template <int n> __device__ __forceinline__ void wait_loads_and_sync()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+
 }  // namespace aba

@@ -137,34 +137,6 @@ template <int D> struct Lds {
 template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Lds<D>::chunks - 1); }
 __device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-typedef int int4v __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor over one (b, h) slice of a [.., N_pad, D] bf16 tensor
-// (base, stride 0, size in bytes, raw dword access): the loads below address
-// it by byte offset, and the hardware range check returns zeros past its end.
-__device__ __forceinline__ int4v head_rsrc(const uint16_t *base, int bytes)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return int4v{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)), bytes, 0x00020000};
-}
-
-// Direct copy of 16 bytes per lane from a buffer into LDS: lane L's bytes land
-// at dst + 16 L (dst is wavefront-uniform; M0 holds its LDS address).  Issued
-// as inline assembly: the compiler then does not track these LDS writes, and
-// would otherwise wait for every copy in flight before each LDS read it cannot
-// prove disjoint from them.  Ordering is explicit instead: a slot is read only
-// after wait_loads_and_sync has covered the copies into it, and is refilled
-// only after the barrier that follows its last read.
-__device__ __forceinline__ void load_lds16(int4v rs, int voff, int soff, char *dst)
-{
-    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)dst);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(m0)
-                 : "memory");
-}
-
 // Direct loads of one 64-key sub-tile: K rows key0 .. key0+63 into a K slot,
 // the matching V^T tile into a V slot.  Every load moves 1024 bytes: whole K
 // rows (4 at D = 128) or 8 V^T rows.  The per-lane byte offsets inside a
@@ -223,16 +195,6 @@ __device__ __forceinline__ void issue_v(int4v rv, int key0, char *slot, int wave
     char *dst = slot + O::loads * 1024 * wave;
 #pragma unroll
     for (int t = 0; t < O::loads; ++t) load_lds16(rv, off.v[t % 2], base + (t / 2) * 16 * L::vPitch, dst + 1024 * t);
-}
-
-// Wait until at most n of this wavefront's direct loads are in flight (they
-// complete in issue order), then meet the other wavefronts: their loads up to
-// the same point are then in LDS as well.  A bare s_barrier: the workgroup
-// fence of __syncthreads would also wait for the loads that are meant to stay
-// in flight.  Every LDS read before the barrier has been consumed by then.
-template <int n> __device__ __forceinline__ void wait_loads_and_sync()
-{
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
 }
 
 // One list entry: key block j with log2 weight lw; j < 0 marks an entry to skip.
@@ -663,19 +625,30 @@ struct FineWindow {
     uint64_t valid, partial;
 };
 
-__device__ __forceinline__ FineWindow load_fine_window(const int32_t *lrow, const float *wrow, int m, int n_list,
-                                                       int NBk, bool ragged, int lane)
+// Raw list entries of window m, loaded without a branch on their values (index
+// clamped into the list; entries past it are dropped by make_fine_window), so
+// that both loads are in flight together and nothing waits for them until
+// make_fine_window runs.
+struct RawWindow {
+    int j;
+    float w;
+};
+
+__device__ __forceinline__ RawWindow load_raw_window(const int32_t *lrow, const float *wrow, int m, int n_list, int lane)
+{
+    const int e = min(64 * m + lane, n_list - 1);   // n_list >= 1 wherever a window is loaded
+    return RawWindow{lrow[e], wrow[e]};
+}
+
+__device__ __forceinline__ FineWindow make_fine_window(const RawWindow &raw, int m, int n_list, int NBk, bool ragged,
+                                                       int lane)
 {
     const int e = 64 * m + lane;
     int j = 0;
     float lw = -INFINITY;
-    if (e < n_list) {
-        const int jj = lrow[e];
-        const float wj = wrow[e];
-        if (jj >= 0 && jj < NBk && wj > 0.f && wj < INFINITY) {
-            j = jj;
-            lw = __log2f(wj);
-        }
+    if (e < n_list && raw.j >= 0 && raw.j < NBk && raw.w > 0.f && raw.w < INFINITY) {
+        j = raw.j;
+        lw = __log2f(raw.w);
     }
     FineWindow win;
     win.j = j;
@@ -760,8 +733,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int t = 0; t < KL; ++t) koff[t] = (lane >> 4) * L::pitch + 16 * ((lane & 15) ^ (4 * t + (lane >> 4)));
 
-    FineWindow win0 = load_fine_window(lrow, wrow, 0, n_list, NBk, ragged, lane);
-    FineWindow win1{0, -INFINITY, 0, 0};
+    FineWindow win0{0, -INFINITY, 0, 0}, win1{0, -INFINITY, 0, 0};
+    if (n_list > 0) win0 = make_fine_window(load_raw_window(lrow, wrow, 0, n_list, lane), 0, n_list, NBk, ragged, lane);
+    RawWindow raw{0, 0.f};   // window m + 1, loaded at iteration 4m and turned into a window at 4m + 2
     // block to load for entry 16u + 4 wave + t (sub-tile u, this wavefront's load t)
     auto block_of = [&](int u, int t) __attribute__((always_inline)) {
         const int src = ((u >> 2) & 1) ? win1.j : win0.j;
@@ -879,9 +853,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // Sub-tile u: K in K slot u % 3, V^T in V slot u % 2.  Iteration u issues
     // V^T(u + 1) and K(u + 2), computes u and waits for all but the K(u + 2)
-    // loads.  Window m (sub-tiles 4m .. 4m+3) sits in win{m % 2}; window m + 1 is
-    // read at iteration 4m, two iterations before its first use.  Unrolled six
-    // times, so that every slot is a compile-time offset.
+    // loads.  Window m (sub-tiles 4m .. 4m+3) sits in win{m % 2}; the entries of
+    // window m + 1 are loaded at iteration 4m and validated at 4m + 2, just
+    // before their first use, so the wait the compiler puts before that use
+    // finds them long arrived.  Unrolled six times, so that every slot is a
+    // compile-time offset.
     auto kptr = [&](int sl) __attribute__((always_inline)) { return sl == 0 ? ks0 : (sl == 1 ? ks1 : ks2); };
     auto vptr = [&](int sl) __attribute__((always_inline)) { return sl == 0 ? vs0 : vs1; };
     auto sub_valid = [&](int u) __attribute__((always_inline)) {
@@ -899,8 +875,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto step = [&](auto u6c, int u) __attribute__((always_inline)) {
         constexpr int U6 = decltype(u6c)::value;   // u % 6
         const int u1 = u + 1, u2 = u + 2;
-        if ((u & 3) == 0 && u + 4 < n_sub) {
-            const FineWindow nw = load_fine_window(lrow, wrow, (u >> 2) + 1, n_list, NBk, ragged, lane);
+        if ((u & 3) == 0 && u + 4 < n_sub) raw = load_raw_window(lrow, wrow, (u >> 2) + 1, n_list, lane);
+        if ((u & 3) == 2 && u + 2 < n_sub) {   // window (u >> 2) + 1 is first used below, for K(u + 2)
+            const FineWindow nw = make_fine_window(raw, (u >> 2) + 1, n_list, NBk, ragged, lane);
             if ((u >> 2) & 1) win0 = nw; else win1 = nw;
         }
         if (u1 < n_sub) issue_v(vptr((U6 + 1) % 2), u1);

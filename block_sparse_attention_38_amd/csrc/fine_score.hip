@@ -97,39 +97,73 @@ __device__ __forceinline__ void split8(const float x[8], bf16x8 &hi, bf16x8 &lo)
     }
 }
 
-// LDS tile of 32 centroid slots: hi and lo parts, [32][D] bf16 each, 16-byte
-// chunk c of row r stored at c ^ (r % (D/8)), so that the 16 rows one phase of
-// a 128-bit read touches fall on different banks.
-template <int D> struct CentLds {
+// A tile of 32 centroid slots, split: hi rows 0..31 then lo rows 32..63, D
+// bf16 each.  In memory (written once per call by fine_cent_kernel) the tiles
+// of a head are consecutive and unswizzled; in LDS chunk c of row r sits at
+// c ^ (r % (D/8)), so the 16 rows one phase of a 128-bit read touches fall on
+// different banks.  The swizzle is applied by the direct loads: each lane
+// fetches the source chunk that belongs at its LDS position.
+template <int D> struct CentTile {
     static constexpr int chunks = D / 8;
     static constexpr int pitch = D * 2;
-    static constexpr int part = kTileSlots * pitch;   // bytes of hi (or lo)
-    static constexpr int bytes = 2 * part;
-    static constexpr int per_thread = kTileSlots * chunks / 256;   // chunks staged per thread
+    static constexpr int part = kTileSlots * pitch;          // offset of the lo rows
+    static constexpr int bytes = 2 * part;                   // 16 KB at D = 128
+    static constexpr int loads = bytes / 1024;               // 1 KB direct loads per tile
+    static constexpr int wave_loads = loads / 4;
+    static constexpr int rows_per_load = 1024 / pitch;
+    static constexpr int period = chunks / rows_per_load;    // distinct per-lane offsets
 };
 template <int D> __device__ __forceinline__ int cent_off(int r, int c)
 {
-    return r * CentLds<D>::pitch + 16 * (c ^ (r & (CentLds<D>::chunks - 1)));
+    return r * CentTile<D>::pitch + 16 * (c ^ (r & (CentTile<D>::chunks - 1)));
+}
+
+// Split centroid tiles: one thread per (b, h, tile, slot, 8-element chunk).
+template <int D>
+__global__ __launch_bounds__(256) void fine_cent_kernel(const float *__restrict__ cent, int NBq, int C, int NT, long total,
+                                                        uint16_t *__restrict__ tiles)
+{
+    using T = CentTile<D>;
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int c = (int)(i % T::chunks);
+    const int s = (int)((i / T::chunks) % kTileSlots);
+    const long tile = i / T::chunks / kTileSlots;   // (b*H + h) * NT + ct
+    const int ct = (int)(tile % NT);
+    const long bh = tile / NT;
+    const int qb = kTileBlocks * ct + s / kSlots, m = s % kSlots;
+    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (qb < NBq && m < C) load8(cent + ((bh * NBq + qb) * C + m) * D + 8 * c, x);
+    bf16x8 hi, lo;
+    split8(x, hi, lo);
+    uint16_t *base = tiles + tile * (T::bytes / 2);
+    *reinterpret_cast<bf16x8 *>(base + s * D + 8 * c) = hi;
+    *reinterpret_cast<bf16x8 *>(base + (kTileSlots + s) * D + 8 * c) = lo;
 }
 
 template <int D, bool write>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fine_score_kernel(
-    const float *__restrict__ cent, const float *__restrict__ kbar, const float2 *__restrict__ stat, int NBq,
-    int NBk, int C, int n_chunks, int splits, float scale_log2, float2 *__restrict__ partial,
-    float *__restrict__ scores)
+    const uint16_t *__restrict__ ctiles, const float *__restrict__ kbar, const float2 *__restrict__ stat, int NBq,
+    int NBk, int n_chunks, int splits, float scale_log2, float2 *__restrict__ partial, float *__restrict__ scores)
 {
-    using L = CentLds<D>;
+    using CT = CentTile<D>;
     constexpr int KS = D / 16;
-    __shared__ __align__(16) char ct_lds[2][L::bytes];
+    constexpr int WL = CT::wave_loads;
+    // three tile slots: the tile in use and the next two, whose loads are in flight
+    __shared__ __align__(16) char ring[3][CT::bytes];
+    __shared__ __align__(16) float2 st_ring[3][kTileSlots];
     __shared__ float2 red[2][4][kTileSlots];
-    __shared__ float2 st_lds[2][kTileSlots];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, half = lane >> 5;
     const int sp = blockIdx.x % splits;
     const int chunk = (blockIdx.x / splits) % n_chunks;
     const long bh = blockIdx.x / splits / n_chunks;
     const int NT = (NBq + kTileBlocks - 1) / kTileBlocks;   // centroid tiles of the head
+    const int n_my = NT > sp ? (NT - sp + splits - 1) / splits : 0;   // tiles sp, sp + splits, ...
+    const int4v rc = head_rsrc(ctiles + bh * NT * (CT::bytes / 2), NT * CT::bytes);
+    const int4v rs = head_rsrc(stat + bh * NT * kTileSlots, NT * kTileSlots * (int)sizeof(float2));
 
     // split pooled keys of this wavefront's 64 key blocks: fragment (kt, ks) is
     // block chunk*256 + 64 wave + 32 kt + l32, elements 16 ks + 8 half .. +7
@@ -147,67 +181,95 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     }
 
-    // staging of centroid tile ct: thread stages chunks tid + 256 i (slot = chunk / (D/8))
-    auto fetch = [&](int ct, float (&x)[L::per_thread][8], float2 &st) __attribute__((always_inline)) {
+    // direct loads of tile ct into ring slot sl: load t (wavefront w issues t =
+    // w*WL .. w*WL + WL - 1) fills rows t*rows_per_load .., lane L row L / chunks of
+    // them and LDS chunk L % chunks, which holds source chunk (L % chunks) ^ (row % chunks)
+    int voff[CT::period];
 #pragma unroll
-        for (int i = 0; i < L::per_thread; ++i) {
-            const int ch = tid + 256 * i, s = ch / L::chunks, c = ch % L::chunks;
-            const int qb = kTileBlocks * ct + s / kSlots, m = s % kSlots;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
-            if (qb < NBq && m < C) load8(cent + ((bh * NBq + qb) * C + m) * D + 8 * c, x[i]);
-        }
-        if (write && tid < kTileSlots) st = stat[bh * (long)NT * kTileSlots + (long)ct * kTileSlots + tid];
-    };
-    auto store = [&](int buf, const float (&x)[L::per_thread][8], const float2 &st) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < L::per_thread; ++i) {
-            const int ch = tid + 256 * i, s = ch / L::chunks, c = ch % L::chunks;
-            bf16x8 hi, lo;
-            split8(x[i], hi, lo);
-            *reinterpret_cast<bf16x8 *>(ct_lds[buf] + cent_off<D>(s, c)) = hi;
-            *reinterpret_cast<bf16x8 *>(ct_lds[buf] + L::part + cent_off<D>(s, c)) = lo;
-        }
-        if (write && tid < kTileSlots) st_lds[buf][tid] = st;
-    };
-
-    int ct = sp;
-    {
-        float x[L::per_thread][8];
-        float2 st{0.f, 0.f};
-        if (ct < NT) {
-            fetch(ct, x, st);
-            store(0, x, st);
-        }
+    for (int v = 0; v < CT::period; ++v) {
+        const int r = CT::rows_per_load * v + lane / CT::chunks;   // row % chunks for loads t with t % period == v
+        voff[v] = (lane / CT::chunks) * CT::pitch + 16 * ((lane % CT::chunks) ^ (r & (CT::chunks - 1)));
     }
-    __syncthreads();
-    for (int it = 0; ct < NT; ct += splits, ++it) {
-        const int buf = it & 1;
-        const int nct = ct + splits;
-        float x[L::per_thread][8];
-        float2 st{0.f, 0.f};
-        if (nct < NT) fetch(nct, x, st);   // next tile's loads overlap this tile's MFMAs
+    auto issue = [&](int sl, int ct) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < WL; ++i) {
+            const int t = WL * wave + i;
+            load_lds16(rc, voff[t % CT::period], ct * CT::bytes + t * 1024, ring[sl] + t * 1024);
+        }
+        if (write && wave == 0) load_lds4(rs, 4 * lane, ct * kTileSlots * (int)sizeof(float2), (char *)st_ring[sl]);
+    };
+    // wait for everything but the next-next tile's loads (or for everything)
+    auto wait_tile = [&](bool more) __attribute__((always_inline)) {
+        if (!more) wait_loads_and_sync<0>();
+        else if (write && wave == 0) wait_loads_and_sync<WL + 1>();
+        else wait_loads_and_sync<WL>();
+    };
 
-        const char *hi_base = ct_lds[buf], *lo_base = ct_lds[buf] + L::part;
-        floatx16 acc[2] = {floatx16{}, floatx16{}};
+    if (n_my > 0) issue(0, sp);
+    if (n_my > 1) issue(1, sp + splits);
+    // settle the pooled-key loads here, once, rather than inside the loop
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int off = cent_off<D>(l32, 2 * ks + half);
-            const bf16x8 chi = *reinterpret_cast<const bf16x8 *>(hi_base + off);
-            const bf16x8 clo = *reinterpret_cast<const bf16x8 *>(lo_base + off);
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                if (!write) {   // rows = key blocks, columns = slots
-                    acc[kt] = mfma32(khi[kt][ks], chi, acc[kt]);
-                    acc[kt] = mfma32(klo[kt][ks], chi, acc[kt]);
-                    acc[kt] = mfma32(khi[kt][ks], clo, acc[kt]);
-                } else {        // rows = slots, columns = key blocks
-                    acc[kt] = mfma32(chi, khi[kt][ks], acc[kt]);
-                    acc[kt] = mfma32(chi, klo[kt][ks], acc[kt]);
-                    acc[kt] = mfma32(clo, khi[kt][ks], acc[kt]);
-                }
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(khi[kt][ks]), "v"(klo[kt][ks]));
+    wait_tile(n_my > 1);
+
+    // scores of the previous tile, stored at the start of the next iteration so that
+    // the stores are older than the loads a wait must leave in flight
+    float pend[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    int pend_ct = -1;
+    auto flush = [&]() __attribute__((always_inline)) {
+        if (!write || pend_ct < 0) return;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int j = j0 + 32 * kt + l32;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const int qb = kTileBlocks * pend_ct + 2 * half + pp;
+                if (j < NBk && qb < NBq) scores[(bh * NBq + qb) * NBk + j] = pend[kt][pp];
             }
         }
+    };
+
+    for (int i = 0; i < n_my; ++i) {
+        const int ct = sp + i * splits;
+        const int sl = i % 3;
+        flush();
+        if (i + 2 < n_my) issue((i + 2) % 3, ct + 2 * splits);
+
+        const char *hi_base = ring[sl], *lo_base = ring[sl] + CT::part;
+        floatx16 acc[2] = {floatx16{}, floatx16{}};
+        // centroid fragments are read PF steps ahead of their MFMAs; the
+        // scheduling fences keep the compiler from pulling the reads back
+        constexpr int PF = KS < 3 ? KS : 3;
+        bf16x8 fh[PF], fl[PF];
+#pragma unroll
+        for (int f = 0; f < PF; ++f) {
+            fh[f] = *reinterpret_cast<const bf16x8 *>(hi_base + cent_off<D>(l32, 2 * f + half));
+            fl[f] = *reinterpret_cast<const bf16x8 *>(lo_base + cent_off<D>(l32, 2 * f + half));
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 chi = fh[ks % PF], clo = fl[ks % PF];
+            if (ks + PF < KS) {
+                fh[ks % PF] = *reinterpret_cast<const bf16x8 *>(hi_base + cent_off<D>(l32, 2 * (ks + PF) + half));
+                fl[ks % PF] = *reinterpret_cast<const bf16x8 *>(lo_base + cent_off<D>(l32, 2 * (ks + PF) + half));
+            }
+            // the two accumulators alternate, so no MFMA waits on the one just issued
+#pragma unroll
+            for (int term = 0; term < 3; ++term)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    const bf16x8 kf = term == 1 ? klo[kt][ks] : khi[kt][ks];
+                    const bf16x8 cf = term == 2 ? clo : chi;
+                    // stats: rows = key blocks, columns = slots; write: rows = slots, columns = key blocks
+                    acc[kt] = write ? mfma32(cf, kf, acc[kt]) : mfma32(kf, cf, acc[kt]);
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
 
         if (!write) {
             // lane (l32, half) element r of tile kt: key block j0 + 32kt + 8(r/4) + 4half + r%4, slot l32
@@ -229,51 +291,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(acc[kt][r] - mx);
             }
             sum += __shfl_xor(sum, 32, 64);
-            if (half == 0) red[buf][wave][l32] = make_float2(mx, sum);
+            if (half == 0) red[i & 1][wave][l32] = make_float2(mx, sum);
         } else {
             // lane (l32, half) element r of tile kt: slot 8(r/4) + 4half + r%4 (query block
             // 4ct + r/4, centroid 4half + r%4), key block j0 + 32kt + l32
-            float2 sv[16];
+            float part[2][4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sv[r] = st_lds[buf][8 * (r >> 2) + 4 * half + (r & 3)];
+            for (int p = 0; p < 4; ++p) {
+                float2 sv[4];   // (M, coef) of the slots 8p + 4half + e
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                float part[4];
+                for (int e = 0; e < 4; ++e) sv[e] = st_ring[sl][8 * p + 4 * half + e];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
+                for (int kt = 0; kt < 2; ++kt) {
                     float a = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * p + i;
-                        a += sv[r].y * __builtin_amdgcn_exp2f(fmaf(acc[kt][r], scale_log2, -sv[r].x));
-                    }
-                    part[p] = a + __shfl_xor(a, 32, 64);
-                }
-                const int j = j0 + 32 * kt + l32;
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    const int p = 2 * half + pp;
-                    const int qb = kTileBlocks * ct + p;
-                    if (j < NBk && qb < NBq) scores[(bh * NBq + qb) * NBk + j] = part[p];
+                    for (int e = 0; e < 4; ++e)
+                        a += sv[e].y * __builtin_amdgcn_exp2f(fmaf(acc[kt][4 * p + e], scale_log2, -sv[e].x));
+                    part[kt][p] = a + __shfl_xor(a, 32, 64);
                 }
             }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {   // lane half h stores query blocks 2h and 2h + 1
+                pend[kt][0] = half ? part[kt][2] : part[kt][0];
+                pend[kt][1] = half ? part[kt][3] : part[kt][1];
+            }
+            pend_ct = ct;
         }
 
-        if (nct < NT) store(buf ^ 1, x, st);
-        __syncthreads();
+        wait_tile(i + 2 < n_my);
         if (!write && tid < kTileSlots) {   // combine the four wavefronts' partials of this tile
             float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) M = fmaxf(M, red[buf][w][tid].x);
+            for (int w = 0; w < 4; ++w) M = fmaxf(M, red[i & 1][w][tid].x);
             float Z = 0.f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const float2 r = red[buf][w][tid];
+                const float2 r = red[i & 1][w][tid];
                 if (r.x > -INFINITY) Z += r.y * __builtin_amdgcn_exp2f(r.x - M);
             }
             partial[((bh * n_chunks + chunk) * (long)NT + ct) * kTileSlots + tid] = make_float2(M, Z);
         }
     }
+    flush();
 }
 
 // Per (b, h, slot): maximum and normaliser over all chunks, and the slot's
@@ -319,14 +378,25 @@ hipError_t launch_fine_pool(const void *k, int dtype, int B, int H, int N, int N
     return hipGetLastError();
 }
 
-// Work split: enough workgroups to give every SIMD of the 256 CUs about three
-// wavefronts, each workgroup taking every splits-th centroid tile.
+// Work split over the centroid tiles: the kernel holds two workgroups per CU
+// (512 at once); pick the split count that minimises rounds of 512 per unit of
+// work, the smaller one on ties.
 static int fine_splits(long base_wgs, int NT)
 {
-    int sp = 1;
-    while (base_wgs * sp < 768 && sp * 2 <= NT) sp *= 2;
-    return sp;
+    int best = 1;
+    double best_t = 1e30;
+    for (int sp = 1; sp <= 16 && sp <= NT; sp *= 2) {
+        const double rounds = (double)((base_wgs * sp + 511) / 512);
+        const double t = rounds / sp;
+        if (t < best_t - 1e-9) {
+            best_t = t;
+            best = sp;
+        }
+    }
+    return best;
 }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t fine_score_workspace_bytes(int B, int H, int NBq, int NBk)
 {
@@ -334,7 +404,8 @@ size_t fine_score_workspace_bytes(int B, int H, int NBq, int NBk)
     const long n_chunks = (NBk + kChunk - 1) / kChunk;
     const size_t part = (size_t)B * H * n_chunks * NT * kTileSlots * sizeof(float2);
     const size_t stat = (size_t)B * H * NT * kTileSlots * sizeof(float2);
-    return ((part + 255) & ~(size_t)255) + ((stat + 255) & ~(size_t)255);
+    const size_t tiles = (size_t)B * H * NT * CentTile<128>::bytes;   // the larger of D = 64, 128
+    return align256(part) + align256(stat) + align256(tiles);
 }
 
 hipError_t launch_fine_score(const float *cent, const float *weight, const float *kbar, int B, int H, int NBq, int NBk,
@@ -344,26 +415,32 @@ hipError_t launch_fine_score(const float *cent, const float *weight, const float
     const int NT = (NBq + kTileBlocks - 1) / kTileBlocks;
     const int n_chunks = (NBk + kChunk - 1) / kChunk;
     const size_t part_bytes = (size_t)B * H * n_chunks * NT * kTileSlots * sizeof(float2);
-    float2 *partial = static_cast<float2 *>(ws);
-    float2 *stat = reinterpret_cast<float2 *>(static_cast<char *>(ws) + ((part_bytes + 255) & ~(size_t)255));
+    const size_t stat_bytes = (size_t)B * H * NT * kTileSlots * sizeof(float2);
+    char *w = static_cast<char *>(ws);
+    float2 *partial = reinterpret_cast<float2 *>(w);
+    float2 *stat = reinterpret_cast<float2 *>(w + align256(part_bytes));
+    uint16_t *tiles = reinterpret_cast<uint16_t *>(w + align256(part_bytes) + align256(stat_bytes));
     const long base = (long)B * H * n_chunks;
     const int splits = fine_splits(base, NT);
     const dim3 grid((unsigned)(base * splits)), block(256);
     const float sl2 = scale * kLog2e;
     const long slots = (long)B * H * NT * kTileSlots;
+    const dim3 merge_grid((unsigned)((slots + 255) / 256));
     if (D == 128) {
-        fine_score_kernel<128, false><<<grid, block, 0, s>>>(cent, kbar, nullptr, NBq, NBk, C, n_chunks, splits, sl2,
+        const long tt = (long)B * H * NT * kTileSlots * CentTile<128>::chunks;
+        fine_cent_kernel<128><<<dim3((unsigned)((tt + 255) / 256)), block, 0, s>>>(cent, NBq, C, NT, tt, tiles);
+        fine_score_kernel<128, false><<<grid, block, 0, s>>>(tiles, kbar, nullptr, NBq, NBk, n_chunks, splits, sl2,
                                                              partial, nullptr);
-        fine_merge_kernel<<<dim3((unsigned)((slots + 255) / 256)), block, 0, s>>>(partial, weight, NBq, C, n_chunks,
-                                                                                 slots, stat);
-        fine_score_kernel<128, true><<<grid, block, 0, s>>>(cent, kbar, stat, NBq, NBk, C, n_chunks, splits, sl2,
+        fine_merge_kernel<<<merge_grid, block, 0, s>>>(partial, weight, NBq, C, n_chunks, slots, stat);
+        fine_score_kernel<128, true><<<grid, block, 0, s>>>(tiles, kbar, stat, NBq, NBk, n_chunks, splits, sl2,
                                                             nullptr, scores);
     } else if (D == 64) {
-        fine_score_kernel<64, false><<<grid, block, 0, s>>>(cent, kbar, nullptr, NBq, NBk, C, n_chunks, splits, sl2,
+        const long tt = (long)B * H * NT * kTileSlots * CentTile<64>::chunks;
+        fine_cent_kernel<64><<<dim3((unsigned)((tt + 255) / 256)), block, 0, s>>>(cent, NBq, C, NT, tt, tiles);
+        fine_score_kernel<64, false><<<grid, block, 0, s>>>(tiles, kbar, nullptr, NBq, NBk, n_chunks, splits, sl2,
                                                             partial, nullptr);
-        fine_merge_kernel<<<dim3((unsigned)((slots + 255) / 256)), block, 0, s>>>(partial, weight, NBq, C, n_chunks,
-                                                                                 slots, stat);
-        fine_score_kernel<64, true><<<grid, block, 0, s>>>(cent, kbar, stat, NBq, NBk, C, n_chunks, splits, sl2,
+        fine_merge_kernel<<<merge_grid, block, 0, s>>>(partial, weight, NBq, C, n_chunks, slots, stat);
+        fine_score_kernel<64, true><<<grid, block, 0, s>>>(tiles, kbar, stat, NBq, NBk, n_chunks, splits, sl2,
                                                            nullptr, scores);
     } else {
         return hipErrorInvalidValue;
