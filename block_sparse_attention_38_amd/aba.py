@@ -171,8 +171,7 @@ def score(p: Plan, q: torch.Tensor, k: torch.Tensor, *, return_parts: bool = Fal
         cent = torch.empty(B, H, NB, C, D, dtype=torch.float32, device=dev)
         wgt = torch.empty(B, H, NB, C, dtype=torch.float32, device=dev)
         kbar = torch.empty(B, H, NBk, D, dtype=torch.float32, device=dev)
-    if not return_parts or p.key_block != BLOCK:
-        ws = _ws(p, ws, dev)
+    ws = _ws(p, ws, dev)
     _check(load_library().aba_score(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(out), _ptr(cent), _ptr(wgt),
                                     _ptr(kbar), _ptr(ws), _stream()))
     return (out, cent, wgt, kbar) if return_parts else out

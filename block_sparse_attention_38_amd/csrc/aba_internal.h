@@ -23,15 +23,14 @@ hipError_t launch_kmeans(const void *q, int dtype, int B, int H, int N, int N_pa
                          float *cent, float *weight, hipStream_t s);
 hipError_t launch_pool(const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB, float *kbar,
                        hipStream_t s);
-hipError_t launch_score(const float *cent, const float *weight, const float *kbar, int B, int H, int NB, int C, int D,
-                        float scale, float *scores, hipStream_t s);
 hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int cap,
                          int32_t *idx, int32_t *cnt, float *w, hipStream_t s);
 // Dynamic LDS the sampler needs for rows of NB key blocks and budget K (0: the
 // short-row kernel, whose LDS is static).
 size_t sample_lds_bytes(int NB, int K);
-// 4-token key blocks: pooling and the two-pass MFMA scoring (workspace: per-chunk
-// partial statistics and per-centroid coefficients).
+// 4-token key pooling, and the two-pass MFMA scoring of either key block size
+// (workspace: per-chunk partial statistics, per-centroid coefficients and the
+// split centroid tiles).
 hipError_t launch_fine_pool(const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NBk, float *kbar,
                             hipStream_t s);
 size_t fine_score_workspace_bytes(int B, int H, int NBq, int NBk);

@@ -53,9 +53,7 @@ Workspace workspace_layout(const aba_plan_t &p)
     w.weight = align256(rows * p.n_clusters * p.head_dim * sizeof(float));
     w.kbar = w.weight + align256(rows * p.n_clusters * sizeof(float));
     w.fine = w.kbar + align256(krows * p.head_dim * sizeof(float));
-    w.score_total = w.fine;
-    if (p.key_block == ABA_FINE_BLOCK)
-        w.score_total += align256(aba::fine_score_workspace_bytes(p.batch, p.heads, p.n_blocks, p.n_key_blocks));
+    w.score_total = w.fine + align256(aba::fine_score_workspace_bytes(p.batch, p.heads, p.n_blocks, p.n_key_blocks));
     w.attend_total = align256(aba::attend_workspace_bytes(p.dtype, p.batch, p.heads, p.seq_pad, p.head_dim));
     w.total = w.score_total > w.attend_total ? w.score_total : w.attend_total;
     return w;
@@ -158,9 +156,9 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
     if (st != ABA_OK) return st;
     if (!q || !k || !scores) return fail(ABA_E_INVALID, "q, k and scores must be non-NULL");
     const bool fine = p->key_block == ABA_FINE_BLOCK;
-    if ((!centroids || !cluster_w || !pooled_k || fine) && !workspace)
-        return fail(ABA_E_INVALID, "workspace of %llu bytes is required (4-token key blocks always need it, 128-token "
-                    "ones unless every optional output is given)", (unsigned long long)p->workspace_bytes);
+    if (!workspace)
+        return fail(ABA_E_INVALID, "workspace of %llu bytes is required (the scoring passes keep their statistics there)",
+                    (unsigned long long)p->workspace_bytes);
     const Workspace lay = workspace_layout(*p);
     char *ws = static_cast<char *>(workspace);
     float *cent = centroids ? centroids : reinterpret_cast<float *>(ws + lay.cent);
@@ -171,17 +169,13 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
     st = hip_status(aba::launch_kmeans(q, p->dtype, B, H, N, NP, D, NB, p->n_clusters, p->kmeans_iters, cent, wgt, stream),
                     "kmeans launch");
     if (st != ABA_OK) return st;
-    if (fine) {
-        const int NBk = p->n_key_blocks;
-        st = hip_status(aba::launch_fine_pool(k, p->dtype, B, H, N, NP, D, NBk, kbar, stream), "pool launch");
-        if (st != ABA_OK) return st;
-        return hip_status(aba::launch_fine_score(cent, wgt, kbar, B, H, NB, NBk, p->n_clusters, D, p->softmax_scale,
-                                                 ws + lay.fine, scores, stream),
-                          "score launch");
-    }
-    st = hip_status(aba::launch_pool(k, p->dtype, B, H, N, NP, D, NB, kbar, stream), "pool launch");
+    const int NBk = p->n_key_blocks;
+    st = hip_status(fine ? aba::launch_fine_pool(k, p->dtype, B, H, N, NP, D, NBk, kbar, stream)
+                         : aba::launch_pool(k, p->dtype, B, H, N, NP, D, NB, kbar, stream),
+                    "pool launch");
     if (st != ABA_OK) return st;
-    return hip_status(aba::launch_score(cent, wgt, kbar, B, H, NB, p->n_clusters, D, p->softmax_scale, scores, stream),
+    return hip_status(aba::launch_fine_score(cent, wgt, kbar, B, H, NB, NBk, p->n_clusters, D, p->softmax_scale,
+                                             ws + lay.fine, scores, stream),
                       "score launch");
 }
 

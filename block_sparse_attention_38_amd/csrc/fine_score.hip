@@ -1,13 +1,15 @@
-// fine_score.hip -- IBCS pooling and scoring for 4-token key blocks (gfx950).
+// fine_score.hip -- IBCS block scoring on the matrix cores, and pooling of
+// 4-token key blocks (gfx950).
 //
-// AB-Attention page, section "Три приёма AB-Attention": key/value blocks of
-// only 4 tokens are selected while queries stay in 128-token blocks (kernel
-// paragraph), and every key block is scored by the cluster-weighted attention
-// of the query block's centroids to its averaged keys (IBCS paragraph):
-//     S[b', j] = sum_m w_m softmax_j(s c_m . kbar_j),  j over all 4-token blocks.
-// With 4-token blocks a query block scores N/4 key blocks (8190 at 32K
-// tokens), so the centroid x pooled-key contraction is a real matrix product
-// (2 * C * N/4 * D flops per query block) and runs on the bf16 MFMA.
+// AB-Attention page, section "Три приёма AB-Attention": every key block is
+// scored by the cluster-weighted attention of the query block's centroids to
+// its averaged keys (IBCS paragraph),
+//     S[b', j] = sum_m w_m softmax_j(s c_m . kbar_j),
+// and key/value blocks may be only 4 tokens while queries stay in 128-token
+// blocks (kernel paragraph).  With 4-token blocks a query block scores N/4 key
+// blocks (8190 at 32K tokens), so the centroid x pooled-key contraction is a
+// real matrix product (2 * C * N/4 * D flops per query block); the same
+// kernels score 128-token key blocks (NB of them per row).
 //
 // Precision.  Scores must stay within 1e-4 relative of an fp64 evaluation, which
 // bf16 operands (2^-9) cannot give.  Both operands are split into two bf16

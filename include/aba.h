@@ -90,8 +90,8 @@ typedef struct aba_plan {
     int32_t key_block;      /* tokens per key block: ABA_BLOCK or ABA_FINE_BLOCK */
     int32_t n_key_blocks;   /* NBk = ceil(N / key_block) */
     int32_t reserved;
-    uint64_t workspace_bytes; /* device scratch for aba_score (when its optional
-                                 outputs are NULL), aba_attend and aba_attend_full;
+    uint64_t workspace_bytes; /* device scratch for aba_score, aba_attend and
+                                 aba_attend_full;
                                  every call uses it from offset 0 and only while it
                                  runs, so one buffer serves all calls ordered on a
                                  stream (calls that overlap in time need their own) */
@@ -125,9 +125,8 @@ aba_status aba_plan(aba_plan_t *p, int32_t batch, int32_t heads, int32_t seq_len
  *   centroids  : out, nullable, float32 [B,H,NB,C,D]
  *   cluster_w  : out, nullable, float32 [B,H,NB,C]
  *   pooled_k   : out, nullable, float32 [B,H,NBk,D]
- *   workspace  : at least p->workspace_bytes of device memory (may be NULL only
- *                for 128-token key blocks when all three optional outputs are
- *                given) */
+ *   workspace  : at least p->workspace_bytes of device memory (required: the
+ *                two scoring passes keep per-chunk softmax statistics there) */
 aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *scores, float *centroids,
                      float *cluster_w, float *pooled_k, void *workspace, hipStream_t stream);
 

@@ -144,11 +144,12 @@ def test_tampered_plan_is_rejected(aba):
     assert lib.aba_attend_full(ctypes.byref(p.raw), fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
 
 
-def test_fine_scores_always_need_a_workspace(aba):
+@pytest.mark.parametrize("key_block", [128, 4])
+def test_scores_always_need_a_workspace(aba, key_block):
     lib = aba.load_library()
-    p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 64, key_block=4)
+    p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 2 if key_block == 128 else 64, key_block=key_block)
     fake = ctypes.c_void_p(1)
-    # every optional output given, still no workspace: the two-pass scoring keeps its statistics there
+    # every optional output given, still no workspace: the two scoring passes keep their statistics there
     assert lib.aba_score(ctypes.byref(p.raw), fake, fake, fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
     assert b"workspace" in lib.aba_last_error()
 
