@@ -151,4 +151,11 @@ template <int n> __device__ __forceinline__ void wait_loads_and_sync()
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
 }
 
+// The same for code that also writes LDS with ordinary stores before the
+// barrier: those must land (lgkmcnt) before another wavefront reads them.
+template <int n> __device__ __forceinline__ void wait_loads_lds_and_sync()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+
 }  // namespace aba

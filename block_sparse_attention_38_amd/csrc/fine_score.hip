@@ -200,11 +200,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         if (write && wave == 0) load_lds4(rs, 4 * lane, ct * kTileSlots * (int)sizeof(float2), (char *)st_ring[sl]);
     };
-    // wait for everything but the next-next tile's loads (or for everything)
+    // wait for everything but the next-next tile's loads (or for everything);
+    // the statistics pass has also written its partials to LDS before the barrier
     auto wait_tile = [&](bool more) __attribute__((always_inline)) {
-        if (!more) wait_loads_and_sync<0>();
-        else if (write && wave == 0) wait_loads_and_sync<WL + 1>();
-        else wait_loads_and_sync<WL>();
+        if (!more) wait_loads_lds_and_sync<0>();
+        else if (write && wave == 0) wait_loads_lds_and_sync<WL + 1>();
+        else wait_loads_lds_and_sync<WL>();
     };
 
     if (n_my > 0) issue(0, sp);

@@ -114,3 +114,32 @@ def test_wide_head_densest_sampled(aba):
     err = np.abs(gpu_rows(L["out"], items) - ref).max()
     print(f"[wide_head] K={p.budget}: lists bit-exact, attend {len(items)} query blocks max abs err {err:.3g}")
     assert err <= att_tol(w)
+
+
+def test_high_res_scores_are_run_to_run_identical(aba, highres):
+    """Scoring the same layer again gives bit-identical scores (its passes exchange
+    partial statistics between wavefronts through LDS; every such value must be in
+    place before it is read)."""
+    L, p = highres, highres["p"]
+    qd, kd, _ = L["gpu"]
+    ws = aba.workspace(p, qd.device)
+    for _ in range(3):
+        s2 = aba.score(p, qd, kd, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(s2, L["s"])
+
+
+def test_wide_fine_scores_are_run_to_run_identical(aba):
+    """The same with 4-token key blocks on the 40-head layer (32 chunks of key
+    blocks per head, 64 centroid tiles)."""
+    from block_sparse_attention_38_amd.workloads import FINE_BLOCK
+
+    w = WIDE
+    (_, _, _), (qd, kd, _) = inputs(w, 1005)
+    p = aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, 8, 10, w.fine_budget(0.1), key_block=FINE_BLOCK)
+    ws = aba.workspace(p, qd.device)
+    first = aba.score(p, qd, kd, ws=ws).clone()
+    for _ in range(3):
+        again = aba.score(p, qd, kd, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again, first)
