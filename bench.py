@@ -45,7 +45,8 @@ METRIC = "ms/call and effective TFLOP/s of sparse attention, 32K-token video lay
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 ATTEND_SRC = os.path.join(ROOT, "block_sparse_attention_38_amd", "csrc", "attend.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_single_layer_traffic.json")
+TRAFFIC_FILES = {128: os.path.join(ROOT, "profiles", "attend_single_layer_traffic.json"),
+                 4: os.path.join(ROOT, "profiles", "attend_single_layer_4token_traffic.json")}
 
 
 def log(msg: str):
@@ -71,16 +72,18 @@ def source_digest(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_entry():
-    """HBM traffic per attend launch from the committed rocprofv3 counter runs, if the
-    kernel source has not changed since they were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_entry(key_block: int = 128):
+    """HBM traffic per attend call (bytes) of the 32K bf16 layer from the committed
+    rocprofv3 counter runs for that key block size, if the kernel source has not
+    changed since they were taken."""
+    path = TRAFFIC_FILES.get(key_block)
+    if path is None or not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("attend_src_sha256_16") != source_digest(ATTEND_SRC):
+    if rec.get("attend_src_sha256_16") != source_digest(ATTEND_SRC) or rec.get("key_block", 128) != key_block:
         return None
     return rec.get("bytes_per_launch")
 
@@ -266,6 +269,7 @@ def fine_leg(args, w, sets, density, coarse_plan, coarse_lists, dense_ms, n_diag
         "mean_kept_blocks": float(np.mean(kept)), "realised_density": float(np.mean(kept)) / NBk,
         "kept_tflop_per_call": kflops / 1e12, "attend_kept_tflops": kflops / (st["attend"] * 1e-3) / 1e12,
         "attend_kept_mfma_frac": kflops / (st["attend"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "attend_traffic_bytes": traffic_entry(aba.FINE_BLOCK) if w.name == "single_layer" else None,
         "speedup_vs_dense": {"layer": dense_ms / ms, "attention": dense_ms / st["attend"]} if dense_ms else None,
     }
     log(f"[bench] 4-token key blocks: {ms:.3f} ms/step (score {st['score']:.3f}, sample {st['sample']:.3f}, "
@@ -589,7 +593,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attend_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None if fine_main else traffic_entry(),
+            "traffic": traffic_entry(p.key_block) if w.name == "single_layer" and w.dtype == "bf16" else None,
         },
         "diagnostics": diagnostics,
         "fine_key_blocks": None,
