@@ -195,8 +195,11 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
     constexpr int KS = D / 16;          // k-steps over the head dimension
     constexpr int DCH = D / 8;          // 16-byte chunks per row of D bf16
     __shared__ uint4 xt_s[D * 16];      // X^T: row d holds 128 queries (16 chunks), chunk swizzle c ^ (d & 15)
-    __shared__ uint4 cs_s[32 * DCH];    // split centroids: row 8p + m, chunk swizzle c ^ (row & (DCH - 1))
-    __shared__ float cent[kMaxClusters][D];
+    // split centroids: row 8p + m holds part p of cluster m (chunk swizzle c ^
+    // (row & (DCH - 1))); the three parts sum exactly to the fp32 centroid, so
+    // no separate fp32 copy is kept (that keeps the block under 40 KB of LDS:
+    // four workgroups per CU)
+    __shared__ uint4 cs_s[24 * DCH];
     __shared__ __align__(16) uint8_t asg[kBlock];
     __shared__ int cnt_part[4][kMaxClusters];
     __shared__ float cn_part[4][kMaxClusters];   // per-wavefront shares of |c_m|^2
@@ -248,52 +251,45 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
         }
     }
 
-    // strided initial centroids; clusters >= C stay zero and are never chosen
-    for (int i = tid; i < kMaxClusters * D; i += 256) {
-        const int m = i / D, d = i % D;
-        cent[m][d] = m < C ? bf16_bits_to_f32(src[(m * n / C) * D + d]) : 0.f;
-    }
-    for (int i = tid; i < 8 * DCH; i += 256) cs_s[(24 + i / DCH) * DCH + i % DCH] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
-
-    // split centroids into three bf16 parts and refresh |c|^2 (threads (m, chunk))
-    auto refresh = [&]() {
-        if (tid < kMaxClusters * DCH) {
-            const int m = tid / DCH, c = tid % DCH;
-            uint32_t hi[4], mid[4], lo[4];
-            float nrm = 0.f;
+    // strided initial centroids q[floor(m n / C)]: bf16 values, so the high
+    // part is the row itself and the other two are zero; clusters >= C stay
+    // zero and are never chosen.  Threads (m, chunk) also form |c_m|^2.
+    if (tid < kMaxClusters * DCH) {
+        const int m = tid / DCH, c = tid % DCH;
+        uint4 hi = make_uint4(0, 0, 0, 0);
+        if (m < C) hi = *reinterpret_cast<const uint4 *>(src + (long)(m * n / C) * D + 8 * c);
+        const uint32_t *h = reinterpret_cast<const uint32_t *>(&hi);
+        float nrm = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                float x0 = cent[m][8 * c + e], x1 = cent[m][8 * c + e + 1];
-                nrm = fmaf(x0, x0, nrm);
-                nrm = fmaf(x1, x1, nrm);
-                const uint16_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
-                const float r0 = x0 - bf16_bits_to_f32(h0), r1 = x1 - bf16_bits_to_f32(h1);
-                const uint16_t m0 = f32_to_bf16_bits(r0), m1 = f32_to_bf16_bits(r1);
-                const uint16_t l0 = f32_to_bf16_bits(r0 - bf16_bits_to_f32(m0));
-                const uint16_t l1 = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m1));
-                hi[e / 2] = h0 | ((uint32_t)h1 << 16);
-                mid[e / 2] = m0 | ((uint32_t)m1 << 16);
-                lo[e / 2] = l0 | ((uint32_t)l1 << 16);
-            }
-#pragma unroll
-            for (int pp = 0; pp < 3; ++pp) {
-                const int r = 8 * pp + m;
-                const uint32_t *src4 = pp == 0 ? hi : (pp == 1 ? mid : lo);
-                cs_s[r * DCH + (c ^ (r & (DCH - 1)))] = make_uint4(src4[0], src4[1], src4[2], src4[3]);
-            }
-            // reduce |c_m|^2 over the DCH consecutive lanes of cluster m
-#pragma unroll
-            for (int o = 1; o < DCH; o <<= 1) nrm += __shfl_xor(nrm, o, 64);
-            if (c == 0) {
-                cn_part[0][m] = nrm;
-                cn_part[1][m] = cn_part[2][m] = cn_part[3][m] = 0.f;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const float x0 = bf16_lo(h[e]), x1 = bf16_hi(h[e]);
+            nrm = fmaf(x0, x0, nrm);
+            nrm = fmaf(x1, x1, nrm);
         }
-    };
-    refresh();
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+            const int r = 8 * pp + m;
+            cs_s[r * DCH + (c ^ (r & (DCH - 1)))] = pp == 0 ? hi : make_uint4(0, 0, 0, 0);
+        }
+        // reduce |c_m|^2 over the DCH consecutive lanes of cluster m
+#pragma unroll
+        for (int o = 1; o < DCH; o <<= 1) nrm += __shfl_xor(nrm, o, 64);
+        if (c == 0) {
+            cn_part[0][m] = nrm;
+            cn_part[1][m] = cn_part[2][m] = cn_part[3][m] = 0.f;
+        }
+    }
     __syncthreads();
     uint16_t *cs16 = reinterpret_cast<uint16_t *>(cs_s);
+    // element d of cluster m's part p, and the fp32 centroid element (exact sum of the parts)
+    auto part_at = [&](int p, int m, int d) __attribute__((always_inline)) -> uint16_t & {
+        const int rr = 8 * p + m;
+        return cs16[(rr * DCH + ((d >> 3) ^ (rr & (DCH - 1)))) * 8 + (d & 7)];
+    };
+    auto centroid = [&](int m, int d) __attribute__((always_inline)) {
+        return (bf16_bits_to_f32(part_at(0, m, d)) + bf16_bits_to_f32(part_at(1, m, d))) +
+               bf16_bits_to_f32(part_at(2, m, d));
+    };
 
     const int rounds = T_iters > 0 ? T_iters : 1;
     int prev = -1;
@@ -304,7 +300,10 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const uint4 a = cs_s[l32 * DCH + ((2 * ks + half) ^ (l32 & (DCH - 1)))];
+            // rows 24..31 of the A operand only feed accumulator rows that are
+            // never read: any stored row serves
+            const int ar = l32 < 24 ? l32 : l32 - 8;
+            const uint4 a = cs_s[ar * DCH + ((2 * ks + half) ^ (ar & (DCH - 1)))];
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), xf[ks], acc, 0, 0, 0);
         }
         // lane half h holds clusters 4h .. 4h+3: accumulator row 8p + m is r = 4p + (m & 3)
@@ -362,19 +361,18 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
             for (int r = 0; r < 4; ++r) {
                 const int m = 4 * half + r;
                 const int cn = cnt_part[0][m] + cnt_part[1][m] + cnt_part[2][m] + cnt_part[3][m];
-                float cv = cent[m][d];
+                float cv;
                 if (m < C && cn > 0) {
                     cv = sum[r] / (float)cn;
-                    cent[m][d] = cv;
                     const uint16_t hb = f32_to_bf16_bits(cv);
                     const float r1 = cv - bf16_bits_to_f32(hb);
                     const uint16_t mb = f32_to_bf16_bits(r1);
                     const uint16_t lb = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mb));
-#pragma unroll
-                    for (int pp = 0; pp < 3; ++pp) {
-                        const int rr = 8 * pp + m;
-                        cs16[(rr * DCH + ((d >> 3) ^ (rr & (DCH - 1)))) * 8 + (d & 7)] = pp == 0 ? hb : (pp == 1 ? mb : lb);
-                    }
+                    part_at(0, m, d) = hb;
+                    part_at(1, m, d) = mb;
+                    part_at(2, m, d) = lb;
+                } else {
+                    cv = centroid(m, d);   // an empty cluster keeps its centroid
                 }
                 sq[r] = cv * cv;
             }
@@ -393,7 +391,7 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
     }
 
     float *co = cent_out + (long)row * C * D;
-    for (int i = tid; i < C * D; i += 256) co[i] = cent[i / D][i % D];
+    for (int i = tid; i < C * D; i += 256) co[i] = centroid(i / D, i % D);
     if (tid < C) {
         const int cn = cnt_part[0][tid] + cnt_part[1][tid] + cnt_part[2][tid] + cnt_part[3][tid];
         w_out[(long)row * C + tid] = (float)((double)cn / (double)n);
