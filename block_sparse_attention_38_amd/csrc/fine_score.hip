@@ -38,6 +38,11 @@
 // rows in each half of the wavefront, one permlane32 swap apart).  Both
 // passes evaluate identical MFMA sequences, so every logit of the write pass
 // is bitwise the one the stats pass saw and 2^(x - M) <= 1.
+//
+// Short rows (at most kRowMaxBlocks key blocks, e.g. the 256 128-token blocks
+// of a 32K sequence) take one pass instead: row_score_kernel gives a
+// workgroup one tile of 32 centroid slots and every key block of the head,
+// keeps all its logits in LDS, and reduces, normalises and writes from there.
 #include "aba_internal.h"
 
 namespace aba {
@@ -363,6 +368,113 @@ __global__ __launch_bounds__(256) void fine_merge_kernel(const float2 *__restric
     stat[i] = make_float2(M, coef);
 }
 
+// ---------------------------------------------------------------------------
+// One-pass scoring of short rows.  Workgroup (b, h, centroid tile ct): the 32
+// slots' split centroids are the A operand, held in registers; wavefront w
+// computes the logit tiles of key blocks [32t, 32t + 32) for t = w, w + 4, ...
+// (three split-bf16 MFMA terms per k-step, as in the two-pass kernels, in S
+// orientation: rows = slots, columns = key blocks) and stores them, in the
+// log2 domain, to LDS rows of one slot each.  Then 8 threads per slot reduce
+// its row to the maximum M and the normaliser Z (coefficient w_m / Z), and
+// every (query block, key block) score is summed over the block's centroids.
+// ---------------------------------------------------------------------------
+constexpr int kRowMaxBlocks = 1024;
+
+// LDS row pitch (floats) of one slot's logits: whole 32-block tiles plus 8, so
+// that the 8 slots one wavefront of the reduction reads start on different banks.
+__host__ __device__ constexpr int row_pitch(int NBk) { return 32 * ((NBk + 31) / 32) + 8; }
+
+template <int D>
+__global__ __launch_bounds__(256) void row_score_kernel(const float *__restrict__ cent,
+                                                        const float *__restrict__ weight,
+                                                        const float *__restrict__ kbar, int NBq, int NBk, int C,
+                                                        float scale_log2, float *__restrict__ scores)
+{
+    constexpr int KS = D / 16;
+    extern __shared__ float xs[];              // logits [32 slots][pitch]
+    __shared__ float2 st[kTileSlots];          // (M, coefficient) per slot
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, half = lane >> 5;
+    const int NT = (NBq + kTileBlocks - 1) / kTileBlocks;
+    const int ct = blockIdx.x % NT;
+    const long bh = blockIdx.x / NT;
+    const int pitch = row_pitch(NBk);
+
+    // A operand: slot l32 (query block 4ct + l32/8, centroid l32%8), elements
+    // 16ks + 8half .. +7; slots past C or past the last query block are zero
+    const int qb_s = kTileBlocks * ct + l32 / kSlots, m_s = l32 % kSlots;
+    const bool slot_ok = qb_s < NBq && m_s < C;
+    const float *crow = cent + ((bh * NBq + qb_s) * C + m_s) * D;
+    bf16x8 chi[KS], clo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (slot_ok) load8(crow + 16 * ks + 8 * half, x);
+        split8(x, chi[ks], clo[ks]);
+    }
+
+    const int n_tiles = (NBk + 31) / 32;
+    for (int t = wave; t < n_tiles; t += 4) {
+        const int j = 32 * t + l32;
+        const float *krow = kbar + (bh * NBk + j) * D;
+        float kx[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kx[ks][e] = 0.f;
+            if (j < NBk) load8(krow + 16 * ks + 8 * half, kx[ks]);
+        }
+        floatx16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 khi, klo;
+            split8(kx[ks], khi, klo);
+            acc = mfma32(chi[ks], khi, acc);
+            acc = mfma32(chi[ks], klo, acc);
+            acc = mfma32(clo[ks], khi, acc);
+        }
+        // lane (l32, half) element r: slot 8(r/4) + 4half + r%4, key block j
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            xs[(8 * (r >> 2) + 4 * half + (r & 3)) * pitch + j] = j < NBk ? acc[r] * scale_log2 : -INFINITY;
+    }
+    __syncthreads();
+
+    {   // per-slot maximum and normaliser: 8 consecutive threads per slot
+        const int sl = tid >> 3, sub = tid & 7;
+        const float *row = xs + sl * pitch;
+        float M = -INFINITY;
+        for (int j = sub; j < NBk; j += 8) M = fmaxf(M, row[j]);
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        float Z = 0.f;
+        for (int j = sub; j < NBk; j += 8) Z += __builtin_amdgcn_exp2f(row[j] - M);
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) Z += __shfl_xor(Z, o, 64);
+        if (sub == 0) {
+            const int qb = kTileBlocks * ct + sl / kSlots, m = sl % kSlots;
+            float coef = 0.f;
+            if (qb < NBq && m < C && Z > 0.f) coef = weight[(bh * NBq + qb) * C + m] / Z;
+            st[sl] = make_float2(M, coef);
+        }
+    }
+    __syncthreads();
+
+    // scores of the tile's query blocks: consecutive threads, consecutive key blocks
+    const int n_qb = min(kTileBlocks, NBq - kTileBlocks * ct);
+    for (int i = tid; i < n_qb * NBk; i += 256) {
+        const int p = i / NBk, j = i - p * NBk;
+        float a = 0.f;
+        for (int m = 0; m < C; ++m) {
+            const float2 sv = st[kSlots * p + m];
+            a += sv.y * __builtin_amdgcn_exp2f(xs[(kSlots * p + m) * pitch + j] - sv.x);
+        }
+        scores[(bh * NBq + kTileBlocks * ct + p) * (long)NBk + j] = a;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_fine_pool(const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NBk, float *kbar,
@@ -416,6 +528,25 @@ hipError_t launch_fine_score(const float *cent, const float *weight, const float
 {
     if (C < 1 || C > kSlots) return hipErrorInvalidValue;
     const int NT = (NBq + kTileBlocks - 1) / kTileBlocks;
+    const float sl2 = scale * kLog2e;
+    if (NBk <= kRowMaxBlocks) {   // short rows: one pass, logits in LDS
+        const size_t lds = (size_t)kTileSlots * row_pitch(NBk) * sizeof(float);
+        const dim3 grid((unsigned)((long)B * H * NT)), block(256);
+        if (D == 128) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&row_score_kernel<128>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            row_score_kernel<128><<<grid, block, lds, s>>>(cent, weight, kbar, NBq, NBk, C, sl2, scores);
+        } else if (D == 64) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&row_score_kernel<64>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            row_score_kernel<64><<<grid, block, lds, s>>>(cent, weight, kbar, NBq, NBk, C, sl2, scores);
+        } else {
+            return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     const int n_chunks = (NBk + kChunk - 1) / kChunk;
     const size_t part_bytes = (size_t)B * H * n_chunks * NT * kTileSlots * sizeof(float2);
     const size_t stat_bytes = (size_t)B * H * NT * kTileSlots * sizeof(float2);
@@ -426,7 +557,6 @@ hipError_t launch_fine_score(const float *cent, const float *weight, const float
     const long base = (long)B * H * n_chunks;
     const int splits = fine_splits(base, NT);
     const dim3 grid((unsigned)(base * splits)), block(256);
-    const float sl2 = scale * kLog2e;
     const long slots = (long)B * H * NT * kTileSlots;
     const dim3 merge_grid((unsigned)((slots + 255) / 256));
     if (D == 128) {
