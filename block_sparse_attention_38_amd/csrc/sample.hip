@@ -23,12 +23,19 @@ namespace {
 constexpr uint64_t kOne = 1ull << 32;
 constexpr int kIdxBits = 10;   // kMaxBlocks = 2^10: block index packed under sigma
 
+// clamp(floor(s * 2^32), 1, 2^32), exactly, from the bits of s: a positive
+// float below 1 is m * 2^(e - 150) with m its 24-bit significand (e the biased
+// exponent; subnormals: e = 1 and no hidden bit), so s * 2^32 = m * 2^(e - 118)
+// and the floor is a shift.  (Equal to the fp64 evaluation for every float.)
 __device__ __forceinline__ uint64_t fixed_point(float s)
 {
     if (!(s > 0.f)) return 1;                       // zero, negative, NaN
-    const double v = floor((double)s * 4294967296.0);
-    if (v >= 4294967296.0) return kOne;
-    const uint64_t r = (uint64_t)v;
+    const uint32_t b = __float_as_uint(s);
+    const int e = (int)(b >> 23);
+    if (e >= 127) return kOne;                      // s >= 1, inf
+    const uint32_t m = e ? ((b & 0x7FFFFFu) | 0x800000u) : (b & 0x7FFFFFu);
+    const int sh = (e ? e : 1) - 118;
+    const uint64_t r = sh >= 0 ? ((uint64_t)m << sh) : (sh > -32 ? (uint64_t)(m >> -sh) : 0);
     return r < 1 ? 1 : r;
 }
 
@@ -236,6 +243,7 @@ __global__ __launch_bounds__(256) void sample_kernel(const float *__restrict__ s
 constexpr int kKeyIdxBits = 15;                       // key blocks per row < 2^15
 constexpr uint32_t kKeyIdxMask = (1u << kKeyIdxBits) - 1;
 constexpr int kFastTop = 64;                          // sorted top tried first (one wavefront)
+constexpr int kCandMax = 512;                         // blocks ranked directly for the fast top
 constexpr int kMaxQuadSteps = kMaxFineBlocks / 4 / 256;   // quads per lane at most
 
 __device__ __forceinline__ uint64_t pack_key(uint32_t sig_m1, int j)
@@ -290,13 +298,20 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
     uint64_t *top = reinterpret_cast<uint64_t *>(dyn);                          // P keys
     uint32_t *sig = reinterpret_cast<uint32_t *>(dyn + 16 * (((size_t)P + 1) / 2));   // 4 * NB4 values
     __shared__ uint32_t red[2][4][4];
-    __shared__ int hist[4][256];
+    __shared__ __align__(16) int hist[4][256];
+    // the fast top's candidates share the histograms' space (the radix select
+    // that uses them runs only when the candidates did not fit)
+    uint64_t *const cand = reinterpret_cast<uint64_t *>(&hist[0][0]);
+    static_assert(sizeof(hist) >= kCandMax * sizeof(uint64_t), "candidates fit in the histogram space");
     __shared__ int sel_s[3];
     __shared__ uint64_t ured[4];
     __shared__ uint32_t mm_s[2][4];
     __shared__ int wtot[4];
     __shared__ int top_n, t_s;
     __shared__ uint64_t r_s, cut_s;
+    __shared__ uint32_t lmax_s[256];   // largest sigma - 1 of each thread's blocks
+    __shared__ uint32_t lo_s;
+    __shared__ int cand_n;
 
     const int row = blockIdx.x;
     const int qb = row % NBq, h = (row / NBq) % H, b = row / (NBq * H);
@@ -334,6 +349,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         *reinterpret_cast<uint4 *>(sig + 4 * q) = make_uint4(x[0], x[1], x[2], x[3]);
     }
     part = wave_sum_t<uint64_t>(part);
+    lmax_s[tid] = vmax;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         vmin = min(vmin, (uint32_t)__shfl_xor((int)vmin, o, 64));
@@ -344,7 +360,10 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         mm_s[0][wave] = vmin;
         mm_s[1][wave] = vmax;
     }
-    if (tid == 0) top_n = 0;
+    if (tid == 0) {
+        top_n = 0;
+        cand_n = 0;
+    }
     __syncthreads();
     const uint64_t total = ured[0] + ured[1] + ured[2] + ured[3];
     vmin = min(min(mm_s[0][0], mm_s[0][1]), min(mm_s[0][2], mm_s[0][3]));
@@ -395,8 +414,67 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         return std::array<int, 7>{out[0], out[1], out[2], out[3], out[4], out[5], out[6]};
     };
 
-    // 2. gathers the top T (unsorted) into top[0 .. T), pads top[T .. PT) with 0
+    // the T-th largest of the threads' maxima (T <= 256, wavefront 0, into
+    // lo_s): a lower bound on the T-th largest value, since T threads each hold
+    // a block at least that large
+    auto threads_bound = [&](int T) {
+        if (wave == 0) {
+            const uint32_t a0 = lmax_s[lane], a1 = lmax_s[lane + 64], a2 = lmax_s[lane + 128], a3 = lmax_s[lane + 192];
+            uint32_t v = 0;
+            for (int bit = 31; bit >= 0; --bit) {   // largest v with >= T maxima >= v
+                const uint32_t c = v | (1u << bit);
+                const int n = __popcll(__ballot(a0 >= c)) + __popcll(__ballot(a1 >= c)) +
+                              __popcll(__ballot(a2 >= c)) + __popcll(__ballot(a3 >= c));
+                if (n >= T) v = c;
+            }
+            if (lane == 0) lo_s = v > vmin ? v : vmin;
+        }
+        __syncthreads();
+        return lo_s;
+    };
+
+    // 2. gathers the top T into top[0 .. T), pads top[T .. PT) with 0.  For a
+    // small T the blocks at or above the bound are collected first; when they
+    // are few, each one's rank among them (by the packed key, which orders
+    // sigma descending and index ascending) places the top T directly, sorted.
+    // Otherwise the radix select below finds the T-th value and the top is
+    // gathered unsorted.
     auto gather_top = [&](int T, int PT) {
+        if (T <= kFastTop) {
+            const uint32_t lo = threads_bound(T);
+            for (int k = 0; k < steps; ++k) {
+                const int q = quad(k);
+                uint4 xv = make_uint4(0, 0, 0, 0);
+                if (q < NB4) xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+                const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * q + e;
+                    const bool sel = q < NB4 && j < NB && xs[e] >= lo;
+                    const uint64_t bal = __ballot(sel);
+                    if (bal) {
+                        int base = 0;
+                        if (lane == __builtin_ctzll(bal)) base = atomicAdd(&cand_n, __popcll(bal));
+                        base = __shfl(base, __builtin_ctzll(bal), 64);
+                        const int at = base + __popcll(bal & ((1ull << lane) - 1));
+                        if (sel && at < kCandMax) cand[at] = pack_key(xs[e], j);
+                    }
+                }
+            }
+            __syncthreads();
+            const int C = cand_n;
+            if (C <= kCandMax) {
+                for (int i = tid; i < C; i += 256) {
+                    const uint64_t key = cand[i];
+                    int rank = 0;
+                    for (int m = 0; m < C; ++m) rank += cand[m] > key;
+                    if (rank < T) top[rank] = key;
+                }
+                for (int i = T + tid; i < PT; i += 256) top[i] = 0;
+                __syncthreads();
+                return;
+            }
+        }
         // v: the T-th largest sigma - 1; need: how many blocks equal to v are in the top; n_eq: blocks equal to v
         uint32_t v;
         int need, n_eq;
@@ -421,10 +499,12 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
                 need = T - above;
                 n_eq = NB - above;
             } else {
-                // radix select over [vmin, vmax], 8 bits per pass from the top of the range
-                uint32_t base = vmin;
+                // blocks below the threads' bound are never counted
+                const uint32_t lo = T <= 256 ? threads_bound(T) : vmin;
+                // radix select over [lo, vmax], 8 bits per pass from the top of the range
+                uint32_t base = lo;
                 int bits = 0;
-                while (bits < 32 && ((uint64_t)(vmax - vmin) >> bits) != 0) ++bits;   // range < 2^bits
+                while (bits < 32 && ((uint64_t)(vmax - lo) >> bits) != 0) ++bits;   // range < 2^bits
                 int rem = T;   // blocks still needed from the current range [base, base + 2^bits)
                 int cnt_bin = 0;
                 for (;;) {
@@ -444,12 +524,14 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
                             const uint64_t off = (uint64_t)xs[e] - base;
                             const bool in = q < NB4 && 4 * q + e < NB && xs[e] >= base && (off >> bits) == 0;
                             const int bin = in ? (int)(off >> shift) : -1;
-                            const int b0 = __builtin_amdgcn_readfirstlane(bin);
-                            const uint64_t same = __ballot(bin == b0);
-                            if (same == ~0ull) {   // the whole wavefront in one bin: one atomic
-                                if (lane == 0 && b0 >= 0) atomicAdd(&hist[wave][b0], 64);
-                            } else if (in) {
-                                atomicAdd(&hist[wave][bin], 1);
+                            // one atomic per distinct bin among the wavefront's blocks
+                            uint64_t pending = __ballot(in);
+                            while (pending) {
+                                const int leader = __builtin_ctzll(pending);
+                                const int b0 = __builtin_amdgcn_readlane(bin, leader);
+                                const uint64_t same = __ballot(bin == b0) & pending;
+                                if (lane == leader) atomicAdd(&hist[wave][b0], (int)__popcll(same));
+                                pending &= ~same;
                             }
                         }
                     }
