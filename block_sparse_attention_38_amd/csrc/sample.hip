@@ -62,8 +62,10 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
-        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        // each 32 x 32 -> 64-bit product is one instruction (v_mad_u64_u32)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
+        const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+        const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
         c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
@@ -327,26 +329,41 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
     auto quad = [&](int k) { return q0 + 64 * k + lane; };   // valid if < NB4
 
     // 1. fixed-point scores, row total, min and max of sigma - 1
+    // (the scores of 8 steps are loaded before any is used, so that their
+    // latencies overlap)
     uint64_t part = 0;
     uint32_t vmin = 0xFFFFFFFFu, vmax = 0;
-#pragma unroll 8
-    for (int k = 0; k < steps; ++k) {
-        const int q = quad(k);
-        if (q >= NB4) continue;
-        uint32_t x[4];
+    constexpr int kLoadBatch = 8;
+    for (int k0 = 0; k0 < steps; k0 += kLoadBatch) {
+        float sv[kLoadBatch][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = 4 * q + e;
-            x[e] = 0;
-            if (j < NB) {
-                const uint64_t sg = fixed_point(srow[j]);
-                part += sg;
-                x[e] = (uint32_t)(sg - 1);
-                vmin = min(vmin, x[e]);
-                vmax = max(vmax, x[e]);
+        for (int kk = 0; kk < kLoadBatch; ++kk) {
+            const int q = quad(k0 + kk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * q + e;
+                sv[kk][e] = (k0 + kk < steps && j < NB) ? srow[j] : 0.f;
             }
         }
-        *reinterpret_cast<uint4 *>(sig + 4 * q) = make_uint4(x[0], x[1], x[2], x[3]);
+#pragma unroll
+        for (int kk = 0; kk < kLoadBatch; ++kk) {
+            const int q = quad(k0 + kk);
+            if (k0 + kk >= steps || q >= NB4) continue;
+            uint32_t x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * q + e;
+                x[e] = 0;
+                if (j < NB) {
+                    const uint64_t sg = fixed_point(sv[kk][e]);
+                    part += sg;
+                    x[e] = (uint32_t)(sg - 1);
+                    vmin = min(vmin, x[e]);
+                    vmax = max(vmax, x[e]);
+                }
+            }
+            *reinterpret_cast<uint4 *>(sig + 4 * q) = make_uint4(x[0], x[1], x[2], x[3]);
+        }
     }
     part = wave_sum_t<uint64_t>(part);
     lmax_s[tid] = vmax;
@@ -729,6 +746,27 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         kept_total += wtot[i];
     }
     const double inv_r = R > 0 ? 1.0 / (double)R : 0.0;
+    // weight 2^32 / theta of kept block j (sigma - 1 = x)
+    auto weight_of = [&](int j, uint32_t x) __attribute__((always_inline)) {
+        uint64_t th;
+        if (pack_key(x, j) >= cut) {
+            th = kOne;
+        } else if (Kt == 0) {
+            th = 1;
+        } else {
+            const uint64_t xx = Kt * ((uint64_t)x + 1);
+            th = (xx >= R) ? kOne : ceil_ratio_shift32(xx, R, inv_r);
+            th = th < 1 ? 1 : (th > kOne ? kOne : th);
+        }
+        return (float)(4294967296.0 / (double)th);
+    };
+    // Positions in index order; the kept indices go to LDS (the space of the
+    // sorted top, no longer needed), and all threads then form the weights of
+    // consecutive positions: balanced work and coalesced stores.  A list
+    // longer than that space is written directly, each thread its own blocks.
+    const int n_out = kept_total < cap ? kept_total : cap;
+    uint32_t *const lst = reinterpret_cast<uint32_t *>(top);
+    const bool staged = n_out <= 2 * P;
     for (int k = 0; k < steps; ++k) {
         const uint32_t nib = (bits[k >> 3] >> (4 * (k & 7))) & 15u;
         const int c = __popc(nib);
@@ -743,20 +781,22 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
             const int e = __builtin_ctz(rest);
             const int j = 4 * q + e;
             if (pos < cap) {
-                uint64_t th;
-                if (pack_key(xs[e], j) >= cut) {
-                    th = kOne;
-                } else if (Kt == 0) {
-                    th = 1;
+                if (staged) {
+                    lst[pos] = (uint32_t)j;
                 } else {
-                    const uint64_t xx = Kt * ((uint64_t)xs[e] + 1);
-                    th = (xx >= R) ? kOne : ceil_ratio_shift32(xx, R, inv_r);
-                    th = th < 1 ? 1 : (th > kOne ? kOne : th);
+                    irow[pos] = j;
+                    wrow[pos] = weight_of(j, xs[e]);
                 }
-                irow[pos] = j;
-                wrow[pos] = (float)(4294967296.0 / (double)th);
             }
             ++pos;
+        }
+    }
+    if (staged) {
+        __syncthreads();
+        for (int p = tid; p < n_out; p += 256) {
+            const int j = (int)lst[p];
+            irow[p] = j;
+            wrow[p] = weight_of(j, sig[j]);
         }
     }
     if (tid == 0) cnt[row] = kept_total < cap ? kept_total : cap;
