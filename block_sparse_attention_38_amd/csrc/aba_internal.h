@@ -25,8 +25,7 @@ hipError_t launch_pool(const void *k, int dtype, int B, int H, int N, int N_pad,
                        hipStream_t s);
 hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int cap,
                          int32_t *idx, int32_t *cnt, float *w, hipStream_t s);
-// Dynamic LDS the sampler needs for rows of NB key blocks and budget K (0: the
-// short-row kernel, whose LDS is static).
+// Dynamic LDS the sampler needs for rows of NB key blocks and budget K.
 size_t sample_lds_bytes(int NB, int K);
 // 4-token key pooling, and the two-pass MFMA scoring of either key block size
 // (workspace: per-chunk partial statistics, per-centroid coefficients and the

@@ -6,13 +6,13 @@
 // important blocks always, every other block with a non-zero chance; a kept
 // block counts 1/pi times (Horvitz-Thompson: 25% counts as four).
 //
-// One workgroup per (b, h, query block) row.  All decisions are integer so
-// that they are bit-reproducible:
+// One workgroup per (b, h, query block) row, for rows of any length (256
+// 128-token blocks or N/4 4-token blocks).  All decisions are integer so that
+// they are bit-reproducible:
 //   sigma_j = clamp(floor(S_j * 2^32), 1, 2^32)     (uint64, exact)
-//   bitonic sort of (sigma desc, j asc) in LDS; water-filling over the sorted
-//   prefix by one lane (at most K steps); thresholds by exact 96/64-bit long
-//   division; draws from Philox4x32-10 addressed by (seed, b, h, qb, j);
-//   kept blocks compacted in ascending order with a workgroup prefix sum.
+//   water-filling over the order (sigma desc, j asc); thresholds by exact
+//   128-bit comparisons; draws from Philox4x32-10 addressed by (seed, b, h,
+//   qb, j); kept blocks compacted in ascending order.
 #include "aba_internal.h"
 
 #include <array>
@@ -21,7 +21,6 @@ namespace aba {
 namespace {
 
 constexpr uint64_t kOne = 1ull << 32;
-constexpr int kIdxBits = 10;   // kMaxBlocks = 2^10: block index packed under sigma
 
 // clamp(floor(s * 2^32), 1, 2^32), exactly, from the bits of s: a positive
 // float below 1 is m * 2^(e - 150) with m its 24-bit significand (e the biased
@@ -37,22 +36,6 @@ __device__ __forceinline__ uint64_t fixed_point(float s)
     const int sh = (e ? e : 1) - 118;
     const uint64_t r = sh >= 0 ? ((uint64_t)m << sh) : (sh > -32 ? (uint64_t)(m >> -sh) : 0);
     return r < 1 ? 1 : r;
-}
-
-// ceil(x * 2^32 / r) for x < r, by restoring long division (32 quotient bits).
-__device__ __forceinline__ uint64_t ceil_scaled_ratio(uint64_t x, uint64_t r)
-{
-    uint64_t rem = x, quo = 0;
-#pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
-        rem <<= 1;
-        quo <<= 1;
-        if (rem >= r) {
-            rem -= r;
-            quo |= 1;
-        }
-    }
-    return quo + (rem != 0 ? 1 : 0);
 }
 
 // Philox4x32-10 block function (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds,
@@ -73,159 +56,26 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
     return c;
 }
 
-__global__ __launch_bounds__(256) void sample_kernel(const float *__restrict__ scores, int H, int NBq, int NB, int K,
-                                                     uint64_t seed, int cap, int32_t *__restrict__ idx,
-                                                     int32_t *__restrict__ cnt, float *__restrict__ w)
-{
-    __shared__ uint64_t keys[kMaxBlocks];
-    __shared__ uint8_t capped[kMaxBlocks];
-    __shared__ uint64_t red[4];
-    __shared__ int scan[256];
-    __shared__ int t_s;
-    __shared__ uint64_t r_s;
-
-    const int row = blockIdx.x;
-    const int qb = row % NBq, h = (row / NBq) % H, b = row / (NBq * H);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float *srow = scores + (long)row * NB;
-
-    int P = 1;
-    while (P < NB) P <<= 1;
-
-    // fixed-point scores, packed sort keys, row total
-    uint64_t part = 0;
-    for (int j = tid; j < P; j += 256) {
-        if (j < NB) {
-            const uint64_t sg = fixed_point(srow[j]);
-            part += sg;
-            keys[j] = (sg << kIdxBits) | (uint64_t)(kMaxBlocks - 1 - j);
-            capped[j] = 0;
-        } else {
-            keys[j] = 0;   // below every real key
-        }
-    }
-    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-    if (lane == 0) red[wave] = part;
-    __syncthreads();
-    const uint64_t total = red[0] + red[1] + red[2] + red[3];
-
-    // bitonic sort, descending
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < P / 2; i += 256) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = ((lo & size) == 0);
-                const uint64_t a = keys[lo], c = keys[hi];
-                if ((a < c) == desc) {
-                    keys[lo] = c;
-                    keys[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
-
-    // water-filling over the sorted order (the first block is always kept)
-    if (tid == 0) {
-        int t = 1;
-        uint64_t R = total - (keys[0] >> kIdxBits);
-        while (t < NB && K - t > 0) {
-            const uint64_t sg = keys[t] >> kIdxBits;
-            if ((uint64_t)(K - t) * sg < R) break;
-            R -= sg;
-            ++t;
-        }
-        t_s = t;
-        r_s = R;
-    }
-    __syncthreads();
-    const int t = t_s;
-    const uint64_t R = r_s;
-    for (int p = tid; p < t; p += 256) capped[kMaxBlocks - 1 - (int)(keys[p] & (kMaxBlocks - 1))] = 1;
-    __syncthreads();
-
-    // draws: thread g owns key blocks 4g .. 4g+3 (one Philox block)
-    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-    const int groups = (NB + 3) / 4;
-    int32_t *irow = idx + (long)row * cap;
-    float *wrow = w + (long)row * cap;
-    int base = 0;
-    for (int g0 = 0; g0 < groups; g0 += 256) {
-        const int g = g0 + tid;
-        uint32_t keep = 0;
-        uint64_t theta[4] = {0, 0, 0, 0};
-        if (g < groups) {
-            const uint4 r = philox4x32_10(make_uint4((uint32_t)g, (uint32_t)qb, (uint32_t)h, (uint32_t)b), k0, k1);
-            const uint32_t draw[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 4 * g + e;
-                if (j >= NB) break;
-                uint64_t th;
-                if (capped[j]) {
-                    th = kOne;
-                } else if (K - t <= 0) {
-                    th = 1;
-                } else {
-                    const uint64_t x = (uint64_t)(K - t) * fixed_point(srow[j]);
-                    th = (x >= R) ? kOne : ceil_scaled_ratio(x, R);
-                    th = th < 1 ? 1 : (th > kOne ? kOne : th);
-                }
-                theta[e] = th;
-                if ((uint64_t)draw[e] < th) keep |= 1u << e;
-            }
-        }
-        // exclusive prefix sum of the kept counts over the workgroup
-        const int mine = __popc(keep);
-        scan[tid] = mine;
-        __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {
-            const int v = tid >= o ? scan[tid - o] : 0;
-            __syncthreads();
-            scan[tid] += v;
-            __syncthreads();
-        }
-        int pos = base + scan[tid] - mine;
-        const int chunk_total = scan[255];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (keep & (1u << e)) {
-                if (pos < cap) {
-                    irow[pos] = 4 * g + e;
-                    wrow[pos] = (float)(4294967296.0 / (double)theta[e]);
-                }
-                ++pos;
-            }
-        }
-        base += chunk_total;
-        __syncthreads();
-    }
-    if (tid == 0) cnt[row] = base < cap ? base : cap;
-}
-
-
 // ---------------------------------------------------------------------------
-// Long rows (more than kMaxBlocks key blocks: 4-token key blocks give N/4 per
-// row).  The decisions are the ones above, bit for bit, without sorting the
-// row: the water-filling loop stops at the first position p >= 1 of the sorted
-// order where (K - p) sigma_p < R_p (R_p = total - sum of the first p), and
-// never looks past position min(K, NB) - 1, so only a sorted top of the row is
-// needed.
+// The row is never sorted: the water-filling loop stops at the first position
+// p >= 1 of the sorted order where (K - p) sigma_p < R_p (R_p = total - sum of
+// the first p), and never looks past position min(K, NB) - 1, so only a sorted
+// top of the row is needed.
 //
 // Work is split in "quads" of 4 consecutive blocks (one Philox call, one
 // 16-byte LDS read): wavefront w owns a contiguous run of quads and its lane l
 // takes quad q0 + 64k + l at step k, so reads are conflict-free and every
 // ordered pass runs in index order.
 //   1. sigma - 1 of every block into LDS (uint32), the row total, min and max;
-//   2. top(T): the T-th largest sigma - 1, v, by a radix select over the row's
-//      own range [min, max] (8 bits per pass from the top of the range:
-//      per-wavefront LDS histograms, one atomic per wavefront when all its lanes
-//      fall in one bin; v = min directly when fewer than T blocks exceed it);
-//      when more blocks equal v than the top has room for, the lowest indices
-//      among them are taken (an 8-way bisection on the index).  The top T is
-//      gathered with wavefront-aggregated LDS atomics (order does not matter: it
-//      is sorted next, by the packed key (sigma - 1) << 15 | ~j);
+//   2. top(T), ordered by the packed key (sigma - 1) << 15 | ~j: for T <= 64
+//      the blocks at or above a bound (the T-th largest of the threads'
+//      maxima) are collected, and when at most 512 of them, each one's rank
+//      among them places it; otherwise the T-th largest sigma - 1, v, comes
+//      from a radix select over [bound, max] (8 bits per pass from the top of
+//      the range, per-wavefront LDS histograms with one atomic per distinct
+//      bin; v = min directly when fewer than T blocks exceed it), the lowest
+//      indices are taken when more blocks equal v than the top has room for
+//      (an 8-way bisection on the index), and the top is gathered unsorted;
 //   3. the stopping point: first with T = min(K, 64), sorted and scanned inside
 //      one wavefront with shuffles; when the loop stops inside that top (fewer
 //      than 64 blocks capped, the usual case) nothing more is needed;
@@ -236,9 +86,10 @@ __global__ __launch_bounds__(256) void sample_kernel(const float *__restrict__ s
 //      (K - t) sigma, which for an integer draw is draw * R < x * 2^32, an
 //      exact 128-bit comparison.  theta itself (for the weight) is formed only
 //      for kept blocks: an fp64 estimate (x 2^32 times 1/R), corrected to the
-//      exact ceiling with two 128-bit products.  Kept blocks are compacted in index order (a
-//      count pass, a scan over wavefronts, a write pass with a shuffle scan
-//      per step).
+//      exact ceiling with two 128-bit products.  Kept blocks are compacted in
+//      index order (a count pass, a scan over wavefronts, a pass with a shuffle
+//      scan per step that places the indices in LDS), then every thread forms
+//      the weights of consecutive list positions.
 // K >= NB caps every block (the loop then ends at t = NB), so that case keeps
 // everything with weight 1 and skips 2-4.
 // ---------------------------------------------------------------------------
@@ -815,7 +666,6 @@ static int topk_pad(int NB, int K)
 
 size_t sample_lds_bytes(int NB, int K)
 {
-    if (NB <= kMaxBlocks) return 0;
     const size_t P = (size_t)topk_pad(NB, K);
     return 16 * ((P + 1) / 2) + 16 * (((size_t)NB + 3) / 4);
 }
@@ -824,10 +674,6 @@ hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int
                          int32_t *idx, int32_t *cnt, float *w, hipStream_t s)
 {
     const dim3 grid((unsigned)((long)B * H * NBq)), block(256);
-    if (NB <= kMaxBlocks) {
-        sample_kernel<<<grid, block, 0, s>>>(scores, H, NBq, NB, K, seed, cap, idx, cnt, w);
-        return hipGetLastError();
-    }
     if (NB > kMaxFineBlocks) return hipErrorInvalidValue;
     const size_t lds = sample_lds_bytes(NB, K);
     if (lds > kSampleLdsLimit) return hipErrorInvalidValue;
