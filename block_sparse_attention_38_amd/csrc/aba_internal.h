@@ -19,8 +19,10 @@ constexpr int kMaxClusters = 8;
 enum Dtype : int { kF32 = 0, kBF16 = 1 };
 
 // Host launchers; each returns the HIP status of its launch.
-hipError_t launch_kmeans(const void *q, int dtype, int B, int H, int N, int N_pad, int D, int NB, int C, int T,
-                         float *cent, float *weight, hipStream_t s);
+// k-means of every query block; for bf16 the same kernel also pools the keys
+// into kbar (key blocks of kb tokens, NBk of them) and sets *pooled.
+hipError_t launch_kmeans(const void *q, const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB, int C,
+                         int T, int kb, int NBk, float *cent, float *weight, float *kbar, bool *pooled, hipStream_t s);
 hipError_t launch_pool(const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB, float *kbar,
                        hipStream_t s);
 hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int cap,

@@ -166,14 +166,18 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
     float *kbar = pooled_k ? pooled_k : reinterpret_cast<float *>(ws + lay.kbar);
 
     const int B = p->batch, H = p->heads, N = p->seq_len, NP = p->seq_pad, D = p->head_dim, NB = p->n_blocks;
-    st = hip_status(aba::launch_kmeans(q, p->dtype, B, H, N, NP, D, NB, p->n_clusters, p->kmeans_iters, cent, wgt, stream),
+    const int NBk = p->n_key_blocks;
+    bool pooled = false;
+    st = hip_status(aba::launch_kmeans(q, k, p->dtype, B, H, N, NP, D, NB, p->n_clusters, p->kmeans_iters,
+                                       p->key_block, NBk, cent, wgt, kbar, &pooled, stream),
                     "kmeans launch");
     if (st != ABA_OK) return st;
-    const int NBk = p->n_key_blocks;
-    st = hip_status(fine ? aba::launch_fine_pool(k, p->dtype, B, H, N, NP, D, NBk, kbar, stream)
-                         : aba::launch_pool(k, p->dtype, B, H, N, NP, D, NB, kbar, stream),
-                    "pool launch");
-    if (st != ABA_OK) return st;
+    if (!pooled) {
+        st = hip_status(fine ? aba::launch_fine_pool(k, p->dtype, B, H, N, NP, D, NBk, kbar, stream)
+                             : aba::launch_pool(k, p->dtype, B, H, N, NP, D, NB, kbar, stream),
+                        "pool launch");
+        if (st != ABA_OK) return st;
+    }
     return hip_status(aba::launch_fine_score(cent, wgt, kbar, B, H, NB, NBk, p->n_clusters, D, p->softmax_scale,
                                              ws + lay.fine, scores, stream),
                       "score launch");

@@ -345,24 +345,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // Per (b, h, slot): maximum and normaliser over all chunks, and the slot's
 // coefficient w_m / Z (0 for slots >= C and for query blocks past the end).
-__global__ __launch_bounds__(256) void fine_merge_kernel(const float2 *__restrict__ partial,
+__global__ __launch_bounds__(64) void fine_merge_kernel(const float2 *__restrict__ partial,
                                                          const float *__restrict__ weight, int NBq, int C,
                                                          int n_chunks, long total, float2 *__restrict__ stat)
 {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    const long i = (long)blockIdx.x * 64 + threadIdx.x;
     if (i >= total) return;
     const int NT = (NBq + kTileBlocks - 1) / kTileBlocks;
     const int slot = (int)(i % ((long)NT * kTileSlots));
     const long bh = i / ((long)NT * kTileSlots);
     const int qb = slot / kSlots, m = slot % kSlots;
     const float2 *p = partial + bh * n_chunks * (long)NT * kTileSlots + slot;
-    float M = -INFINITY;
-    for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, p[(long)c * NT * kTileSlots].x);
-    float Z = 0.f;
-    for (int c = 0; c < n_chunks; ++c) {
-        const float2 r = p[(long)c * NT * kTileSlots];
-        if (r.x > -INFINITY) Z += r.y * __builtin_amdgcn_exp2f(r.x - M);
+    const long stride = (long)NT * kTileSlots;
+    // (M, Z) of two chunks combined into one: exact in the max, one rounding per sum
+    auto combine = [](float2 a, float2 b) {
+        const float M = fmaxf(a.x, b.x);
+        float Z = 0.f;
+        if (a.x > -INFINITY) Z += a.y * __builtin_amdgcn_exp2f(a.x - M);
+        if (b.x > -INFINITY) Z += b.y * __builtin_amdgcn_exp2f(b.x - M);
+        return make_float2(M, Z);
+    };
+    // chunks are read eight at a time, all loads in flight together
+    float2 acc = make_float2(-INFINITY, 0.f);
+    for (int c0 = 0; c0 < n_chunks; c0 += 8) {
+        float2 r[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r[u] = c0 + u < n_chunks ? p[(c0 + u) * stride] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = combine(acc, r[u]);
     }
+    const float M = acc.x, Z = acc.y;
     float coef = 0.f;
     if (qb < NBq && m < C && Z > 0.f) coef = weight[(bh * NBq + qb) * C + m] / Z;
     stat[i] = make_float2(M, coef);
@@ -558,13 +570,13 @@ hipError_t launch_fine_score(const float *cent, const float *weight, const float
     const int splits = fine_splits(base, NT);
     const dim3 grid((unsigned)(base * splits)), block(256);
     const long slots = (long)B * H * NT * kTileSlots;
-    const dim3 merge_grid((unsigned)((slots + 255) / 256));
+    const dim3 merge_grid((unsigned)((slots + 63) / 64)), merge_block(64);   // many small groups: latency-bound
     if (D == 128) {
         const long tt = (long)B * H * NT * kTileSlots * CentTile<128>::chunks;
         fine_cent_kernel<128><<<dim3((unsigned)((tt + 255) / 256)), block, 0, s>>>(cent, NBq, C, NT, tt, tiles);
         fine_score_kernel<128, false><<<grid, block, 0, s>>>(tiles, kbar, nullptr, NBq, NBk, n_chunks, splits, sl2,
                                                              partial, nullptr);
-        fine_merge_kernel<<<merge_grid, block, 0, s>>>(partial, weight, NBq, C, n_chunks, slots, stat);
+        fine_merge_kernel<<<merge_grid, merge_block, 0, s>>>(partial, weight, NBq, C, n_chunks, slots, stat);
         fine_score_kernel<128, true><<<grid, block, 0, s>>>(tiles, kbar, stat, NBq, NBk, n_chunks, splits, sl2,
                                                             nullptr, scores);
     } else if (D == 64) {
@@ -572,7 +584,7 @@ hipError_t launch_fine_score(const float *cent, const float *weight, const float
         fine_cent_kernel<64><<<dim3((unsigned)((tt + 255) / 256)), block, 0, s>>>(cent, NBq, C, NT, tt, tiles);
         fine_score_kernel<64, false><<<grid, block, 0, s>>>(tiles, kbar, nullptr, NBq, NBk, n_chunks, splits, sl2,
                                                             partial, nullptr);
-        fine_merge_kernel<<<merge_grid, block, 0, s>>>(partial, weight, NBq, C, n_chunks, slots, stat);
+        fine_merge_kernel<<<merge_grid, merge_block, 0, s>>>(partial, weight, NBq, C, n_chunks, slots, stat);
         fine_score_kernel<64, true><<<grid, block, 0, s>>>(tiles, kbar, stat, NBq, NBk, n_chunks, splits, sl2,
                                                            nullptr, scores);
     } else {

@@ -187,10 +187,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// The same workgroup then pools the keys of its 128 tokens (IBCS paragraph:
+// a key block is represented by its averaged keys): one 128-token key block
+// (kb = 128) or 32 4-token ones (kb = 4), into kbar [B, H, NBk, D].  The key
+// reads overlap the rounds of the other workgroups on the CU, and the separate
+// pooling pass over k disappears.
 template <int D>
 __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__restrict__ q, int N, int N_pad, int NB,
                                                           int C, int T_iters, float *__restrict__ cent_out,
-                                                          float *__restrict__ w_out)
+                                                          float *__restrict__ w_out, const uint16_t *__restrict__ k,
+                                                          int kb, int NBk, float *__restrict__ kbar)
 {
     constexpr int KS = D / 16;          // k-steps over the head dimension
     constexpr int DCH = D / 8;          // 16-byte chunks per row of D bf16
@@ -396,18 +402,68 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
         const int cn = cnt_part[0][tid] + cnt_part[1][tid] + cnt_part[2][tid] + cnt_part[3][tid];
         w_out[(long)row * C + tid] = (float)((double)cn / (double)n);
     }
+
+    // ---- key pooling of this block's 128 tokens (n valid)
+    const uint16_t *ksrc = k + (bh * N_pad + (long)qb * kBlock) * D;
+    if (kb == kBlock) {
+        // thread (group g, chunk c) sums rows g, g + G, ..; the G partial rows are
+        // then added in order through LDS (the X^T space, free after the rounds)
+        constexpr int G = 256 / DCH;
+        float *part = reinterpret_cast<float *>(xt_s);
+        static_assert(G * D * sizeof(float) <= sizeof(xt_s), "partial rows fit in the X^T space");
+        const int c = tid % DCH, g = tid / DCH;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int r = g; r < n; r += G) {
+            float x[8];
+            load8(ksrc + (long)r * D + 8 * c, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += x[e];
+        }
+        __syncthreads();   // every wavefront is past its last X^T read
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[g * D + 8 * c + e] = acc[e];
+        __syncthreads();
+        if (tid < D) {
+            float sum = 0.f;
+            for (int gg = 0; gg < G; ++gg) sum += part[gg * D + tid];
+            kbar[((long)bh * NBk + qb) * D + tid] = sum / (float)n;
+        }
+    } else {
+        // 4-token blocks 32 qb .. 32 qb + 31: thread (block, chunk)
+        constexpr int kFine = kBlock / kFineBlock;
+        for (int i = tid; i < kFine * DCH; i += 256) {
+            const int g = i / DCH, c = i % DCH;
+            const int j = qb * kFine + g;
+            if (j >= NBk) continue;
+            const int nr = min(kFineBlock, N - kFineBlock * j);
+            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int r = 0; r < nr; ++r) {
+                float x[8];
+                load8(ksrc + (long)(kFineBlock * g + r) * D + 8 * c, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += x[e];
+            }
+            const float fn = (float)nr;
+            float4 *dst = reinterpret_cast<float4 *>(kbar + ((long)bh * NBk + j) * D + 8 * c);
+            dst[0] = make_float4(acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn);
+            dst[1] = make_float4(acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn);
+        }
+    }
 }
 
 }  // namespace
 
-hipError_t launch_kmeans(const void *q, int dtype, int B, int H, int N, int N_pad, int D, int NB, int C, int T,
-                         float *cent, float *weight, hipStream_t s)
+hipError_t launch_kmeans(const void *q, const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB, int C,
+                         int T, int kb, int NBk, float *cent, float *weight, float *kbar, bool *pooled, hipStream_t s)
 {
     const dim3 grid((unsigned)((long)B * H * NB)), block(256);
+    *pooled = dtype == kBF16;
     if (dtype == kBF16 && D == 128)
-        kmeans_mfma_kernel<128><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight);
+        kmeans_mfma_kernel<128><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight,
+                                                       (const uint16_t *)k, kb, NBk, kbar);
     else if (dtype == kBF16 && D == 64)
-        kmeans_mfma_kernel<64><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight);
+        kmeans_mfma_kernel<64><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight,
+                                                      (const uint16_t *)k, kb, NBk, kbar);
     else if (dtype == kF32 && D == 64)
         kmeans_kernel<float, 64><<<grid, block, 0, s>>>((const float *)q, N, N_pad, NB, C, T, cent, weight);
     else
