@@ -219,13 +219,18 @@ __device__ __forceinline__ Entry list_entry(const int32_t *lrow, const float *wr
 // contiguous range of query blocks per XCD.  A query block's cost is its kept
 // count, which varies several-fold between blocks, so every range is
 // reordered by decreasing count (longest first), which keeps the tail of the
-// launch short.  One workgroup per XCD range: an LDS histogram of the counts,
-// a scan over the counts from high to low, and an atomic scatter.  The order
-// inside one count is arbitrary; results do not depend on it (each query
-// block is computed by one workgroup, independently of the others).
+// launch short.  The reordering stays inside windows of kOrderWindow
+// consecutive query blocks when the histogram has room for it (128-token key
+// blocks): the workgroups an XCD runs at once then come from neighbouring query
+// blocks of one head, whose lists overlap, and share more of its L2.  One
+// workgroup per XCD range: an LDS histogram of (window, count), a scan from
+// high counts to low, and an atomic scatter.  The order inside one count is
+// arbitrary; results do not depend on it (each query block is computed by one
+// workgroup, independently of the others).
 // ---------------------------------------------------------------------------
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderBins = kMaxFineBlocks / (kSub / kFineBlock) + 1;   // cost ranks: 0 .. ceil(cap / unit)
+constexpr int kOrderWindow = 128;
 
 // cnt[i] entries cost ceil(cnt[i] / unit) units of work (unit = 1 for 128-token
 // key blocks, 16 for 4-token key blocks: one 64-key sub-tile).
@@ -238,11 +243,13 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *__r
     const int x = blockIdx.x, per = G / kXcds, extra = G % kXcds;
     const int start = x * per + (x < extra ? x : extra), n = per + (x < extra ? 1 : 0);
     const int capu = (cap + unit - 1) / unit;
-    const int nb = capu + 1, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    auto key = [&](int i) {   // cost rank: 0 for the largest possible cost
+    const int wins = (n + kOrderWindow - 1) / kOrderWindow;
+    const bool windowed = (long)wins * (capu + 1) <= kOrderBins;
+    const int nb = (windowed ? wins : 1) * (capu + 1), tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto key = [&](int i) {   // window, then cost rank (0 for the largest possible cost)
         const int c = cnt[start + i];
         const int u = c <= 0 ? 0 : (c >= cap ? capu : (c + unit - 1) / unit);
-        return capu - u;
+        return (windowed ? (i / kOrderWindow) * (capu + 1) : 0) + capu - u;
     };
     for (int b = tid; b < nb; b += kOrderThreads) bins[b] = 0;
     __syncthreads();
