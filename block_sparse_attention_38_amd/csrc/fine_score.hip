@@ -419,6 +419,21 @@ __global__ __launch_bounds__(256) void row_score_kernel(const float *__restrict_
     const int qb_s = kTileBlocks * ct + l32 / kSlots, m_s = l32 % kSlots;
     const bool slot_ok = qb_s < NBq && m_s < C;
     const float *crow = cent + ((bh * NBq + qb_s) * C + m_s) * D;
+    // pooled keys of key tile t (block 32t + l32), elements 16ks + 8half .. +7
+    const int n_tiles = (NBk + 31) / 32;
+    auto load_keys = [&](int t, float (&kx)[KS][8]) __attribute__((always_inline)) {
+        const int j = 32 * t + l32;
+        const float *krow = kbar + (bh * NBk + j) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kx[ks][e] = 0.f;
+            if (t < n_tiles && j < NBk) load8(krow + 16 * ks + 8 * half, kx[ks]);
+        }
+    };
+    // the first key tile's loads go out with the centroids'
+    float kx[KS][8];
+    load_keys(wave, kx);
     bf16x8 chi[KS], clo[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -427,17 +442,9 @@ __global__ __launch_bounds__(256) void row_score_kernel(const float *__restrict_
         split8(x, chi[ks], clo[ks]);
     }
 
-    const int n_tiles = (NBk + 31) / 32;
     for (int t = wave; t < n_tiles; t += 4) {
         const int j = 32 * t + l32;
-        const float *krow = kbar + (bh * NBk + j) * D;
-        float kx[KS][8];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kx[ks][e] = 0.f;
-            if (j < NBk) load8(krow + 16 * ks + 8 * half, kx[ks]);
-        }
+        if (t != wave) load_keys(t, kx);
         floatx16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {

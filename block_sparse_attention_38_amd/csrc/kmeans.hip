@@ -412,12 +412,23 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
         float *part = reinterpret_cast<float *>(xt_s);
         static_assert(G * D * sizeof(float) <= sizeof(xt_s), "partial rows fit in the X^T space");
         const int c = tid % DCH, g = tid / DCH;
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int r = g; r < n; r += G) {
-            float x[8];
-            load8(ksrc + (long)r * D + 8 * c, x);
+        constexpr int RPT = kBlock / G;   // rows per thread; all loads issued before the sums
+        uint4 raw[RPT];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += x[e];
+        for (int i = 0; i < RPT; ++i) {
+            const int r = g + G * i;
+            raw[i] = r < n ? *reinterpret_cast<const uint4 *>(ksrc + (long)r * D + 8 * c) : make_uint4(0, 0, 0, 0);
+        }
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            if (g + G * i >= n) break;
+            const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += bf16_lo(w4[e]);
+                acc[2 * e + 1] += bf16_hi(w4[e]);
+            }
         }
         __syncthreads();   // every wavefront is past its last X^T read
 #pragma unroll
@@ -431,17 +442,35 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
     } else {
         // 4-token blocks 32 qb .. 32 qb + 31: thread (block, chunk)
         constexpr int kFine = kBlock / kFineBlock;
-        for (int i = tid; i < kFine * DCH; i += 256) {
-            const int g = i / DCH, c = i % DCH;
+        constexpr int IPT = kFine * DCH / 256;   // (block, chunk) items per thread
+        static_assert(kFine * DCH % 256 == 0, "whole items per thread");
+        uint4 raw[IPT][kFineBlock];               // all loads issued before the sums
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int i = tid + 256 * it, g = i / DCH, c = i % DCH;
+            const int j = qb * kFine + g;
+#pragma unroll
+            for (int r = 0; r < kFineBlock; ++r)
+                raw[it][r] = (j < NBk && kFineBlock * j + r < N)
+                                 ? *reinterpret_cast<const uint4 *>(ksrc + (long)(kFineBlock * g + r) * D + 8 * c)
+                                 : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int i = tid + 256 * it, g = i / DCH, c = i % DCH;
             const int j = qb * kFine + g;
             if (j >= NBk) continue;
             const int nr = min(kFineBlock, N - kFineBlock * j);
             float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            for (int r = 0; r < nr; ++r) {
-                float x[8];
-                load8(ksrc + (long)(kFineBlock * g + r) * D + 8 * c, x);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += x[e];
+            for (int r = 0; r < kFineBlock; ++r) {
+                if (r >= nr) break;
+                const uint32_t w4[4] = {raw[it][r].x, raw[it][r].y, raw[it][r].z, raw[it][r].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += bf16_lo(w4[e]);
+                    acc[2 * e + 1] += bf16_hi(w4[e]);
+                }
             }
             const float fn = (float)nr;
             float4 *dst = reinterpret_cast<float4 *>(kbar + ((long)bh * NBk + j) * D + 8 * c);
