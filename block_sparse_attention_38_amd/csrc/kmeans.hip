@@ -200,7 +200,11 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
 {
     constexpr int KS = D / 16;          // k-steps over the head dimension
     constexpr int DCH = D / 8;          // 16-byte chunks per row of D bf16
-    __shared__ uint4 xt_s[D * 16];      // X^T: row d holds 128 queries (16 chunks), chunk swizzle c ^ (d & 15)
+    // X^T: row d holds 128 queries (16 chunks of 8), chunk c stored at c ^ xt_swz(d): 16
+    // consecutive rows (the update's reads) and the rows 8c + j of the 16 chunks c of
+    // one transposing write both land on 16 different chunks, so neither conflicts
+    __shared__ uint4 xt_s[D * 16];
+    auto xt_swz = [](int d) __attribute__((always_inline)) { return (d & 15) ^ ((d >> 4) & 7); };
     // split centroids: row 8p + m holds part p of cluster m (chunk swizzle c ^
     // (row & (DCH - 1))); the three parts sum exactly to the fp32 centroid, so
     // no separate fp32 copy is kept (that keeps the block under 40 KB of LDS:
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
                 const int d = 8 * c + 2 * p + hl;
                 const uint32_t a = hl ? ((r0[p] >> 16) | (r1[p] & 0xFFFF0000u)) : ((r0[p] & 0xFFFFu) | (r1[p] << 16));
                 const uint32_t b = hl ? ((r2[p] >> 16) | (r3[p] & 0xFFFF0000u)) : ((r2[p] & 0xFFFFu) | (r3[p] << 16));
-                xt2[d * 32 + (((quad >> 1) ^ (d & 15)) << 1) + (quad & 1)] = make_uint2(a, b);
+                xt2[d * 32 + (((quad >> 1) ^ xt_swz(d)) << 1) + (quad & 1)] = make_uint2(a, b);
             }
         }
     }
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
                     const uint32_t byte = ((e < 4 ? ab.x : ab.y) >> (8 * (e & 3))) & 0xFFu;
                     oh[e] = (byte == (uint32_t)l32) ? (__bf16)1.0f : (__bf16)0.0f;
                 }
-                const uint4 b = xt_s[d * 16 + ((2 * ks + half) ^ (d & 15))];
+                const uint4 b = xt_s[d * 16 + ((2 * ks + half) ^ xt_swz(d))];
                 sum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oh, __builtin_bit_cast(bf16x8, b), sum, 0, 0, 0);
             }
             // lane holds the sums of clusters 4half .. 4half+3 for dim d
@@ -409,8 +413,9 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
         // thread (group g, chunk c) sums rows g, g + G, ..; the G partial rows are
         // then added in order through LDS (the X^T space, free after the rounds)
         constexpr int G = 256 / DCH;
+        constexpr int PP = D + 4;   // partial row pitch: the G rows start on different banks
         float *part = reinterpret_cast<float *>(xt_s);
-        static_assert(G * D * sizeof(float) <= sizeof(xt_s), "partial rows fit in the X^T space");
+        static_assert(G * PP * sizeof(float) <= sizeof(xt_s), "partial rows fit in the X^T space");
         const int c = tid % DCH, g = tid / DCH;
         constexpr int RPT = kBlock / G;   // rows per thread; all loads issued before the sums
         uint4 raw[RPT];
@@ -432,11 +437,11 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
         }
         __syncthreads();   // every wavefront is past its last X^T read
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part[g * D + 8 * c + e] = acc[e];
+        for (int e = 0; e < 8; ++e) part[g * PP + 8 * c + e] = acc[e];
         __syncthreads();
         if (tid < D) {
             float sum = 0.f;
-            for (int gg = 0; gg < G; ++gg) sum += part[gg * D + tid];
+            for (int gg = 0; gg < G; ++gg) sum += part[gg * PP + tid];
             kbar[((long)bh * NBk + qb) * D + tid] = sum / (float)n;
         }
     } else {
