@@ -260,3 +260,37 @@ def test_single_layer_fine_attention_sampled(aba, single_fine):
     err = np.abs(gpu_rows(L["out"], items) - ref).max()
     print(f"[single fine] attend: {len(items)} query blocks, max abs err {err:.3g}")
     assert err <= att_tol(w), f"max abs err {err:.3g}"
+
+
+@pytest.mark.parametrize("key_block,n_tokens,heads", [(4, 4096, 2), (4, 4097, 2), (4, 4100, 2), (128, 131072, 1),
+                                                      (128, 130945, 1)])
+def test_scores_at_the_one_pass_limit(aba, key_block, n_tokens, heads):
+    """Rows of exactly 1024 key blocks take the one-pass scorer with its largest LDS
+    rows; 1025 or more take the two-pass scorer; both against the oracle, re-scored
+    from the GPU's own centroids, weights and pooled keys."""
+    g = torch.Generator().manual_seed(n_tokens + key_block)
+    NB = (n_tokens + 127) // 128
+    shape = (1, heads, 128 * NB, 128)
+    centres = torch.randn(heads, 16, 128, generator=g)
+    z = torch.randint(0, 16, (n_tokens,), generator=g)
+    base = torch.zeros(shape)
+    base[0, :, :n_tokens] = centres[:, z, :]
+    q = (base + 0.5 * torch.randn(shape, generator=g)).to(torch.bfloat16)
+    k = (base + torch.randn(shape, generator=g)).to(torch.bfloat16)
+    q[0, :, n_tokens:] = 0
+    k[0, :, n_tokens:] = 0
+    p = aba.plan(1, heads, n_tokens, 128, "bf16", 8, 10, 8, key_block=key_block)
+    NBk = p.n_key_blocks
+    assert NBk == (n_tokens + key_block - 1) // key_block
+    s, cent, wgt, kbar = aba.score(p, q.to(device()), k.to(device()), return_parts=True)
+    torch.cuda.synchronize()
+    ref = oracle.score(cent.cpu().double().numpy(), wgt.cpu().double().numpy(), kbar.cpu().double().numpy(),
+                       p.softmax_scale)
+    got = s.cpu().double().numpy()
+    rel = (np.abs(got - ref) / ref).max()
+    sums = got.sum(-1)
+    print(f"[one-pass limit kb={key_block} N={n_tokens} NBk={NBk}] max rel err {rel:.3g}; "
+          f"row sums {sums.min():.6f}..{sums.max():.6f}")
+    assert rel <= SCORE_RTOL
+    ref_kbar = oracle.pool(k.float().numpy(), n_tokens, blk=key_block)
+    assert np.abs(kbar.cpu().double().numpy() - ref_kbar).max() / np.abs(ref_kbar).max() <= POOL_RTOL
