@@ -282,3 +282,41 @@ def test_single_layer_dense_sampled(aba, single):
     err = np.abs(gpu_rows(dense, items) - ref).max()
     print(f"[single] attend_full: {len(items)} query blocks, max abs err {err:.3g}")
     assert err <= att_tol(w), f"max abs err {err:.3g}"
+
+
+@pytest.mark.parametrize("key_block", [128, 4])
+def test_padding_rows_are_ignored(aba, key_block):
+    """Rows >= N of q, k and v may hold anything (NaN, inf, huge values): scores,
+    lists, sparse and dense outputs are bitwise those of zero padding."""
+    w = RAGGED
+    (q, k, v), (qd, kd, vd) = inputs(w, 17)
+    N = w.seq_len
+    p = aba.plan(w.batch, w.heads, N, w.head_dim, w.dtype, 8, 10, w.budget() if key_block == 128 else 64,
+                 key_block=key_block)
+
+    def run(qx, kx, vx):
+        s = aba.score(p, qx, kx)
+        lists = aba.sample(p, s, 5)
+        o = aba.attend(p, qx, kx, vx, *lists)
+        of = aba.attend_full(p, qx, kx, vx)
+        torch.cuda.synchronize()
+        return [x.cpu() for x in (s, *lists, o, of)]
+
+    clean = run(qd, kd, vd)
+    dirty = []
+    for x in (qd, kd, vd):
+        y = x.clone()
+        y[:, :, N:] = float("nan")
+        y[:, :, N::2] = float("inf")
+        y[:, 1:, N:] = -3.0e38
+        dirty.append(y)
+    got = run(*dirty)
+    names = ("scores", "idx", "cnt", "w", "attend", "attend_full")
+    for name, a, b in zip(names, clean, got):
+        if name == "idx" or name == "w":   # entries past cnt are unspecified
+            cnt = clean[2]
+            for r in np.ndindex(*cnt.shape):
+                n = int(cnt[r])
+                assert torch.equal(a[r][:n], b[r][:n]), f"{name} differs in row {r}"
+            continue
+        assert torch.equal(a, b), f"{name} differs with garbage padding rows"
