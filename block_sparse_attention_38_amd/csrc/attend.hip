@@ -9,22 +9,21 @@
 // with no permutation and no copies (third paragraph).  The dense path is the
 // same kernel over every key block with unit weights.
 //
-// bf16 path (the hot path), two kernels:
-//   vt_kernel     writes V once per call as 64-key V^T tiles (see "V^T
-//                 staging" below), so that the PV operand is one 16-byte LDS
-//                 read (a transposing read of row-major V runs at half the
-//                 LDS rate on gfx950);
+// bf16 path (the hot path):
 //   attend_bf16   one workgroup of 4 wavefronts per (b, h, query block), two
 //                 workgroups per CU (two wavefronts per SIMD); wavefront w owns
 //                 query rows [32w, 32w + 32).  A kept key block is two 64-key
-//                 sub-tiles, each copied by buffer->LDS direct loads into one of
-//                 two LDS stages while the other stage is computed; one barrier
-//                 per sub-tile.  Per sub-tile:
+//                 sub-tiles of K and V rows, each copied by buffer->LDS direct
+//                 loads into LDS slots while earlier ones are computed; one
+//                 barrier per sub-tile.  Per sub-tile:
 //   S^T = K Q^T      32x32x16 bf16 MFMA, K from LDS, Q fragments in registers
 //   online softmax   in the exp2 domain; the block's log2(w_j) is added to its
 //                    logits, so the weight enters numerator and normaliser; the
 //                    running max moves only when it grows by more than 2^8
-//   O^T += V^T P^T   32x32x16 bf16 MFMA, P^T straight from the S^T accumulators
+//   O^T += V^T P^T   32x32x16 bf16 MFMA, P^T straight from the S^T accumulators,
+//                    the V^T operand by transposing LDS reads of the row-major
+//                    V tile (ds_read_b64_tr_b16, head_dim 128); at head_dim 64
+//                    a pre-pass (vt_kernel) writes V^T tiles instead.
 // Computing the transposed products makes every lane own one query column, so
 // row statistics need a single cross-half exchange (v_permlane32_swap) and the
 // rescale of O is a per-lane scalar multiply.  LDS fragment reads are issued
@@ -45,6 +44,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -65,15 +66,16 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
 // ---------------------------------------------------------------------------
-// V^T staging.  The PV product contracts over keys, so its MFMA operand wants
-// each lane's 8 keys of one head dimension contiguous.  A pre-pass writes V
-// once per call as, for every (b, h) and 64-key sub-tile s, a [D][64] bf16
-// tile whose row d holds v[64s + .][d] with key order vt_key(): inside each
-// group of 16 keys, positions 4..7 and 8..11 are exchanged.  Lane half h of
-// an MFMA then finds its keys 8(e/4) + 4h + e%4 (e = 0..7, the order in which
-// the S^T accumulators hand over P^T) at positions 8h .. 8h+7: one 16-byte
-// LDS read.  Keys >= N are written as zero.  The tiles occupy the same
-// B*H*N_pad*D elements as v.
+// V^T staging (head_dim 64).  The PV product contracts over keys, so its MFMA
+// operand wants each lane's 8 keys of one head dimension contiguous.  A
+// pre-pass writes V once per call as, for every (b, h) and 64-key sub-tile s,
+// a [D][64] bf16 tile whose row d holds v[64s + .][d] with key order vt_key():
+// inside each group of 16 keys, positions 4..7 and 8..11 are exchanged.  Lane
+// half h of an MFMA then finds its keys 8(e/4) + 4h + e%4 (e = 0..7, the order
+// in which the S^T accumulators hand over P^T) at positions 8h .. 8h+7: one
+// 16-byte LDS read.  Keys >= N are written as zero.  The tiles occupy the same
+// B*H*N_pad*D elements as v.  At head_dim 128 the kernels read v itself (see
+// "Transposing reads of V" below).
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
@@ -119,12 +121,27 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t *__restrict__ v,
 // rows), with XOR swizzles of the 16-byte chunks:
 //   K   [64 keys][D]:  chunk c of row r at c ^ (r % 16), so the 16 rows one
 //       16-lane phase of a 128-bit read touches hit 16 different chunks;
-//   V^T [D][64 keys]:  chunk c of row r at c ^ ((r / 2) % 8); with 128-byte
-//       rows, 16 consecutive rows then cover every bank once.
-// Three K slots and two V^T slots: K sub-tiles are loaded two sub-tiles
-// ahead of their use and V^T tiles one and a half (the PV product comes after
-// the softmax), which hides the latency of key blocks gathered from beyond the
-// L2.  80 KB at D = 128, so two workgroups fill the 160 KB of a CU.
+//   V   [64 keys][D] (head_dim 128): chunk c of row r at c ^ 4 (r % 4), which
+//       keeps the transposing reads below free of bank conflicts;
+//   V^T [D][64 keys] (head_dim 64): chunk c of row r at c ^ ((r / 2) % 8);
+//       with 128-byte rows, 16 consecutive rows then cover every bank once.
+// Three K slots and two V slots: K sub-tiles are loaded two sub-tiles ahead of
+// their use and V one and a half (the PV product comes after the softmax),
+// which hides the latency of key blocks gathered from beyond the L2.  80 KB at
+// D = 128, so two workgroups fill the 160 KB of a CU.
+//
+// Transposing reads of V (head_dim 128).  ds_read_b64_tr_b16 works in groups of
+// 16 lanes: lane m of a group points at 4 consecutive bf16 values, and lane i
+// receives value i % 4 of the pieces of lanes 4j + i / 4, j = 0..3 (measured
+// with an in-bounds probe).  So if lane m points at row 4 (g / 2) + m / 4 and
+// dimensions 32 dt + 16 (g % 2) + 4 (m % 4) (g = lane / 16), lane i receives
+// rows 4 (g / 2) + j of dimension 32 dt + 16 (g % 2) + i: for MFMA lane (l32,
+// half) the keys 4 half + j of dimension 32 dt + l32, and a second read 8 rows
+// further gives keys 8 + 4 half + j -- the order of P^T in the accumulators.
+// The row offsets of a k-step are immediates; the swizzle depends only on row
+// % 4, which those offsets keep.  Rows of v past N are read through a buffer
+// descriptor that ends at row N (the row offset in the range-checked per-lane
+// offset), so they arrive as zeros.  No V^T copy of v is made.
 template <int D> struct Lds {
     static constexpr int pitch = D * 2;        // K row bytes
     static constexpr int chunks = D / 8;
@@ -136,20 +153,33 @@ template <int D> struct Lds {
 };
 template <int D> __device__ __forceinline__ int k_swz(int r) { return r & (Lds<D>::chunks - 1); }
 __device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
+// row-major V tiles read by transposing LDS reads (D = 128): chunk c of row r at c ^ 4 (r % 4)
+__device__ __forceinline__ int vr_swz(int r) { return 4 * (r & 3); }
+template <int D> constexpr bool v_rows() { return D == 128; }
+
+// One PV operand (8 bf16) from a row-major V tile: two transposing reads, keys
+// p and p + 8 rows below (see the lane layout where the offsets are formed).
+template <int D> __device__ __forceinline__ bf16x8 v_frag_tr(const char *p)
+{
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 8 * 2 * D));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // Direct loads of one 64-key sub-tile: K rows key0 .. key0+63 into a K slot,
-// the matching V^T tile into a V slot.  Every load moves 1024 bytes: whole K
-// rows (4 at D = 128) or 8 V^T rows.  The per-lane byte offsets inside a
-// sub-tile are precomputed, the sub-tile's own offset is a scalar.  Rows of K
-// past N are read as they are (they lie inside the padded sequence) and
-// masked after the product.  A slot is read only after a vmcnt wait and a
-// barrier.
+// the matching V rows (D = 128) or V^T tile (D = 64) into a V slot.  Every load
+// moves 1024 bytes: whole rows (4 at D = 128) or 8 V^T rows.  The per-lane byte
+// offsets inside a sub-tile are precomputed; the sub-tile's own offset is a
+// scalar for K and V^T, and part of the range-checked per-lane offset for V
+// rows (so rows >= N read as 0).  Rows of K past N are read as they are (they
+// lie inside the padded sequence) and masked after the product.  A slot is
+// read only after a vmcnt wait and a barrier.
 template <int D> struct Dma {
     static constexpr int loads = Lds<D>::kBytes / 1024 / kWaves;   // per tensor and wavefront
     static constexpr int k_rows = 1024 / Lds<D>::pitch;             // K rows per load
     static constexpr int k_period = 16 / k_rows;                    // loads per K swizzle period
     int k[k_period];
-    int v[2];                                                       // V^T swizzle period: 2 loads
+    int v[2];                                                       // V rows: one period; V^T: 2 loads
 };
 
 template <int D>
@@ -164,16 +194,23 @@ __device__ __forceinline__ Dma<D> dma_offsets(int wave, int lane)
         const int r = k0 + O::k_rows * t + lane / L::chunks, pc = lane % L::chunks;
         off.k[t] = r * L::pitch + 16 * (pc ^ k_swz<D>(r));
     }
+    if (v_rows<D>()) {
+        // a load fills 4 rows: lane L row L / 16 (row % 4 == L / 16), LDS chunk L % 16
+        const int r = O::loads * 4 * wave + lane / 16, pc = lane % 16;
+        off.v[0] = r * L::pitch + 16 * (pc ^ vr_swz(r));
+        off.v[1] = off.v[0];
+    } else {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int r = v0 + 8 * t + lane / 8, pc = lane % 8;
-        off.v[t] = r * L::vPitch + 16 * (pc ^ vt_swz(r));
+        for (int t = 0; t < 2; ++t) {
+            const int r = v0 + 8 * t + lane / 8, pc = lane % 8;
+            off.v[t] = r * L::vPitch + 16 * (pc ^ vt_swz(r));
+        }
     }
     return off;
 }
 
 // Issue the direct loads of K rows key0 .. key0+63 into a K slot, or of the
-// matching V^T tile into a V slot (wavefront w fills its share of either).
+// matching V rows or V^T tile into a V slot (wavefront w fills its share).
 template <int D>
 __device__ __forceinline__ void issue_k(int4v rk, int key0, char *slot, int wave, const Dma<D> &off)
 {
@@ -193,8 +230,15 @@ __device__ __forceinline__ void issue_v(int4v rv, int key0, char *slot, int wave
     using O = Dma<D>;
     const int base = key0 * D * 2;   // a V^T tile sits where its keys' rows of v do
     char *dst = slot + O::loads * 1024 * wave;
+    if (v_rows<D>()) {
+        // rows of v itself; the row offset goes in the per-lane offset, which the
+        // buffer range check covers, so rows >= N (past the descriptor) read as 0
 #pragma unroll
-    for (int t = 0; t < O::loads; ++t) load_lds16(rv, off.v[t % 2], base + (t / 2) * 16 * L::vPitch, dst + 1024 * t);
+        for (int t = 0; t < O::loads; ++t) load_lds16(rv, off.v[0] + base + t * 4 * L::pitch, 0, dst + 1024 * t);
+    } else {
+#pragma unroll
+        for (int t = 0; t < O::loads; ++t) load_lds16(rv, off.v[t % 2], base + (t / 2) * 16 * L::vPitch, dst + 1024 * t);
+    }
 }
 
 // One list entry: key block j with log2 weight lw; j < 0 marks an entry to skip.
@@ -352,7 +396,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const long bh = blk / NB;
     const uint16_t *qh = q + bh * N_pad * D;
     const int4v rk = head_rsrc(k + bh * N_pad * D, N_pad * D * 2);
-    const int4v rv = head_rsrc(vt + bh * N_pad * D, N_pad * D * 2);
+    const int4v rv = head_rsrc(vt + bh * N_pad * D, (v_rows<D>() ? N : N_pad) * D * 2);
 
     // this lane's query row (the MFMA column l32 of wavefront's tile); padding rows read as zero
     const int qrow = qb * kBlock + 32 * wave + l32;
@@ -388,17 +432,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int k_rd[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) k_rd[ks] = l32 * L::pitch + 16 * ((2 * ks + half) ^ k_swz<D>(l32));
-    // V^T fragment i = (kt, sub, dt): row 32dt + l32 (the dimension), logical chunk
-    // 4kt + 2sub + half, i.e. positions 32kt + 16sub + 8half .. +7; (row / 2) % 8 ==
-    // (l32 / 2) % 8, so the tile row 32dt is an immediate offset.
-    int v_rd[KT * 2];
+    // V operand i = (ksub = 2 kt + sub, dt).  Row-major V (D = 128): two transposing
+    // reads from per-lane bases of each dt (the lane layout above), k-step rows as
+    // immediates.  V^T tiles (D = 64): one 16-byte read at row 32dt + l32 (the
+    // dimension), logical chunk 4kt + 2sub + half, i.e. positions 32kt + 16sub +
+    // 8half .. +7; (row / 2) % 8 == (l32 / 2) % 8, so the tile row 32dt is an
+    // immediate offset.
+    int v_rd[v_rows<D>() ? DT : KT * 2];
+    if (v_rows<D>()) {
+        const int g = lane >> 4, m = lane & 15, row0 = 4 * (g >> 1) + (m >> 2);
 #pragma unroll
-    for (int i = 0; i < KT * 2; ++i) v_rd[i] = l32 * L::vPitch + 16 * ((2 * i + half) ^ vt_swz(l32));
+        for (int dt = 0; dt < DT; ++dt) {
+            const int chunk = 4 * dt + 2 * (g & 1) + ((m & 3) >> 1);
+            v_rd[dt] = row0 * L::pitch + 16 * (chunk ^ vr_swz(row0)) + 8 * (m & 1);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < KT * 2; ++i) v_rd[i] = l32 * L::vPitch + 16 * ((2 * i + half) ^ vt_swz(l32));
+    }
     auto k_frag = [&](const char *st, int i) __attribute__((always_inline)) {
         return __builtin_bit_cast(bf16x8,
                                   *reinterpret_cast<const uint4 *>(st + k_rd[i % KS] + (i / KS) * 32 * L::pitch));
     };
     auto v_frag = [&](const char *st, int i) __attribute__((always_inline)) {
+        if (v_rows<D>()) return v_frag_tr<D>(st + v_rd[i % DT] + 16 * (i / DT) * L::pitch);
         return __builtin_bit_cast(bf16x8,
                                   *reinterpret_cast<const uint4 *>(st + v_rd[i / DT] + (i % DT) * 32 * L::vPitch));
     };
@@ -578,12 +635,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // address a scalar (block index x 1024) taken from the list window with
 // v_readlane.
 //
-// V^T is staged block-major here (vtg_kernel): block g of a head is a [D][4]
-// bf16 tile at byte offset 1024 g, so a gathered block lands in LDS as one
-// contiguous 1 KB piece.  The PV operand of lane half h (keys 8(e/4) + 4h + e%4
-// of its S^T accumulators, e = 0..7) is then the 4 keys of block slot ga at
-// dimension d followed by the 4 keys of slot ga + 2: two 8-byte LDS reads, one
-// per 256 contiguous bytes in each half-wavefront.
+// V is gathered the same way (a block's 4 rows are also 1 KB) into the
+// row-major, swizzled V layout of the 128-token kernel, and read with the same
+// transposing reads: the PV operand of lane half h (keys 8(e/4) + 4h + e%4 of
+// its S^T accumulators) is the 4 keys of block slot 4 ksub + h at dimension d
+// followed by the 4 keys of slot 4 ksub + h + 2.  The partial last block reads
+// its rows past N as zeros (range-checked offset, as above).
 //
 // Weights: an S^T element in row 8(r/4) + 4h + r%4 of 32-key tile kt belongs
 // to block slot 8kt + 2(r/4) + h, so each lane needs 8 log2 weights per
@@ -599,28 +656,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // ---------------------------------------------------------------------------
 constexpr int kFineSub = kSub / kFineBlock;   // 4-token key blocks per sub-tile
 
-template <int D>
-__global__ __launch_bounds__(256) void vtg_kernel(const uint16_t *__restrict__ v, int N, int N_pad, int NBk, long total,
-                                                  uint16_t *__restrict__ vt)
-{
-    // one thread per (b, h, key block g, dimension pair p): reads 4 B of each
-    // of the block's 4 rows, writes dims 2p and 2p + 1 x 4 keys (16 B)
-    constexpr int PAIRS = D / 2;
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    const int p = (int)(i % PAIRS);
-    const long row = i / PAIRS;
-    const int g = (int)(row % NBk);
-    const long bh = row / NBk;
-    const long t0 = (long)g * kFineBlock;
-    const uint16_t *src = v + (bh * N_pad + t0) * D + 2 * p;
-    uint32_t x[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) x[t] = (t0 + t < N) ? *reinterpret_cast<const uint32_t *>(src + (long)t * D) : 0u;
-    const uint4 o = make_uint4((x[0] & 0xFFFFu) | (x[1] << 16), (x[2] & 0xFFFFu) | (x[3] << 16),
-                               (x[0] >> 16) | (x[1] & 0xFFFF0000u), (x[2] >> 16) | (x[3] & 0xFFFF0000u));
-    *reinterpret_cast<uint4 *>(vt + (bh * N_pad + t0) * D + 8 * p) = o;
-}
 
 // 64 list entries held lane-distributed: lane i has entry 64m + i as the block
 // to load (0 for invalid entries and entries past the list) and its log2
@@ -667,12 +702,12 @@ __device__ __forceinline__ FineWindow make_fine_window(const RawWindow &raw, int
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_fine_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
     const int32_t *__restrict__ order, uint16_t *__restrict__ out, int N, int N_pad, int NBq, int NBk, int cap,
     float scale_log2)
 {
-    static_assert(D == 128, "a 4-token key block of K or V^T is one 1024-byte direct load at D = 128");
+    static_assert(D == 128, "a 4-token key block of K or V is one 1024-byte direct load at D = 128");
     using L = Lds<D>;
     constexpr int KS = D / 16, DT = D / 32, KT = kSub / 32, NK = KT * KS, NV = KT * 2 * DT, PF = 4;
     constexpr int GB = kFineBlock * D * 2;   // bytes of one 4-token block of K or V^T
@@ -689,7 +724,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const long bh = blk / NBq;
     const uint16_t *qh = q + bh * N_pad * D;
     const int4v rk = head_rsrc(k + bh * N_pad * D, N_pad * D * 2);
-    const int4v rv = head_rsrc(vt + bh * N_pad * D, N_pad * D * 2);
+    const int4v rv = head_rsrc(v + bh * N_pad * D, N * D * 2);   // rows >= N read as 0
 
     const int qrow = qb * kBlock + 32 * wave + l32;
     const bool qvalid = qrow < N;
@@ -723,14 +758,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         return __builtin_bit_cast(bf16x8,
                                   *reinterpret_cast<const uint4 *>(st + k_rd[i % KS] + (i / KS) * 32 * L::pitch));
     };
-    // V^T fragment i = (ksub = 2 kt + sub, dt): block slots ga = 8kt + 4sub + half and ga + 2, dimension 32dt + l32
-    const int v_rd = half * GB + l32 * 8;
+    // V fragment i = (ksub, dt): the keys of block slots 4 ksub + half and
+    // 4 ksub + half + 2 at dimension 32 dt + l32, by transposing reads of the
+    // row-major V tile (the same addressing as the 128-token kernel)
+    int v_rd[DT];
+    {
+        const int g = lane >> 4, m = lane & 15, row0 = 4 * (g >> 1) + (m >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int chunk = 4 * dt + 2 * (g & 1) + ((m & 3) >> 1);
+            v_rd[dt] = row0 * L::pitch + 16 * (chunk ^ vr_swz(row0)) + 8 * (m & 1);
+        }
+    }
     auto v_frag = [&](const char *st, int i) __attribute__((always_inline)) {
-        const int ksub = i / DT, dt = i % DT;
-        const int ga = 8 * (ksub >> 1) + 4 * (ksub & 1);
-        const uint2 a = *reinterpret_cast<const uint2 *>(st + v_rd + ga * GB + dt * 32 * 8);
-        const uint2 b = *reinterpret_cast<const uint2 *>(st + v_rd + (ga + 2) * GB + dt * 32 * 8);
-        return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+        return v_frag_tr<D>(st + v_rd[i % DT] + 16 * (i / DT) * L::pitch);
     };
 
     // direct-load source offsets inside a 4-token block of K: lane L fills row
@@ -752,9 +793,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int t = 0; t < KL; ++t) load_lds16(rk, koff[t], block_of(u, t) * GB, dst + (KL * wave + t) * 1024);
     };
+    // V rows of a block: LDS row % 4 = L / 16, chunk L % 16 holds logical chunk
+    // (L % 16) ^ vr_swz(row); the block's offset goes in the range-checked
+    // per-lane offset, so rows >= N (the partial last block) read as 0
+    const int voff = (lane >> 4) * L::pitch + 16 * ((lane & 15) ^ vr_swz(lane >> 4));
     auto issue_v = [&](char *dst, int u) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < KL; ++t) load_lds16(rv, 16 * lane, block_of(u, t) * GB, dst + (KL * wave + t) * 1024);
+        for (int t = 0; t < KL; ++t) load_lds16(rv, voff + block_of(u, t) * GB, 0, dst + (KL * wave + t) * 1024);
     };
 
     auto tile = [&](const char *kst, const char *vst, int u) __attribute__((always_inline)) {
@@ -1110,8 +1155,13 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const float *__restrict
 
 }  // namespace
 
-// V^T copy, then the work order (sparse lists only), in the workspace.
-size_t vt_bytes(int B, int H, int N_pad, int D) { return ((size_t)B * H * N_pad * D * sizeof(uint16_t) + 255) & ~(size_t)255; }
+// Workspace of the bf16 attention calls: the V^T copy (head_dim 64 only; at 128
+// the kernels read v itself), then the work order (sparse lists only).
+size_t vt_bytes(int B, int H, int N_pad, int D)
+{
+    if (v_rows<128>() && D == 128) return 0;
+    return ((size_t)B * H * N_pad * D * sizeof(uint16_t) + 255) & ~(size_t)255;
+}
 
 template <bool full>
 hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtype, int B, int H, int N, int N_pad,
@@ -1122,7 +1172,6 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
     const dim3 grid((unsigned)G), block(256);
     const float sl2 = scale * kLog2e;
     if (dtype == kBF16 && (D == 128 || D == 64)) {
-        const dim3 vt_grid((unsigned)((long)B * H * (N_pad / kSub)));
         uint16_t *vt = static_cast<uint16_t *>(ws);
         int32_t *order = nullptr;
         if (!full) {
@@ -1130,11 +1179,12 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
             order_kernel<<<dim3(8), dim3(kOrderThreads), 0, s>>>(cnt, G, cap, 1, order);
         }
         if (D == 128) {
-            vt_kernel<128><<<vt_grid, block, 0, s>>>((const uint16_t *)v, N, N_pad, vt);
             attend_bf16_kernel<128, full><<<grid, dim3(kThreads), 0, s>>>(
-                (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, order, (uint16_t *)out, N, N_pad, NB, cap, sl2);
+                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, cnt, w, order, (uint16_t *)out, N,
+                N_pad, NB, cap, sl2);
         } else {
-            vt_kernel<64><<<vt_grid, block, 0, s>>>((const uint16_t *)v, N, N_pad, vt);
+            vt_kernel<64><<<dim3((unsigned)((long)B * H * (N_pad / kSub))), block, 0, s>>>((const uint16_t *)v, N, N_pad,
+                                                                                        vt);
             attend_bf16_kernel<64, full><<<grid, dim3(kThreads), 0, s>>>(
                 (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, order, (uint16_t *)out, N, N_pad, NB, cap, sl2);
         }
@@ -1155,15 +1205,11 @@ hipError_t launch_attend_fine(const void *q, const void *k, const void *v, int d
     const int G = B * H * NBq;
     const float sl2 = scale * kLog2e;
     if (dtype == kBF16 && D == 128) {
-        uint16_t *vt = static_cast<uint16_t *>(ws);
         int32_t *order = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + vt_bytes(B, H, N_pad, D));
         order_kernel<<<dim3(8), dim3(kOrderThreads), 0, s>>>(cnt, G, cap, kFineSub, order);
-        const long total = (long)B * H * NBk * (D / 2);
-        vtg_kernel<128><<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>((const uint16_t *)v, N, N_pad, NBk,
-                                                                                   total, vt);
         attend_fine_kernel<128><<<dim3((unsigned)G), dim3(kThreads), 0, s>>>(
-            (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, order, (uint16_t *)out, N, N_pad, NBq, NBk, cap,
-            sl2);
+            (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, cnt, w, order, (uint16_t *)out, N,
+            N_pad, NBq, NBk, cap, sl2);
     } else if (dtype == kF32 && D == 64) {
         attend_f32_fine_kernel<64><<<dim3((unsigned)G), dim3(256), 0, s>>>((const float *)q, (const float *)k,
                                                                           (const float *)v, idx, cnt, w, (float *)out,

@@ -52,7 +52,9 @@ def test_plan_fills_the_layer_sizes(aba):
     assert abs(p.softmax_scale - 128 ** -0.5) < 1e-7
     rows = 12 * 256
     assert p.workspace_bytes >= 4 * rows * (8 * 128 + 8 + 128)
-    assert p.workspace_bytes >= 12 * 32768 * 128 * 2          # the transposed copy of v
+    assert p.workspace_bytes >= 4 * rows                       # the attention work order
+    p64 = aba.plan(1, 12, 32760, 64, "bf16", 8, 10, 26)
+    assert p64.workspace_bytes >= 12 * 32768 * 64 * 2         # head_dim 64: the transposed copy of v
     p = aba.plan(1, 24, 118800, 128, "bf16", 8, 10, 74)
     assert (p.n_blocks, p.seq_pad) == (929, 118912)
     p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 2, softmax_scale=0.5)
