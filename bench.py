@@ -584,9 +584,9 @@ def main():
         "score_stage_gbs": score_bytes / (score_ms * 1e-3) / 1e9,
         "score_stage_hbm_frac": score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "roofline": {
-            # the whole aba_attend call: the V^T copy and the work order are part of it
-            "kernel": (("aba_attend: vtg_kernel<128> + order_kernel + attend_fine_kernel<128>" if fine_main else
-                        "aba_attend: vt_kernel<128> + order_kernel + attend_bf16_kernel<128,false>")
+            # the whole aba_attend call: the work order is part of it
+            "kernel": (("aba_attend: order_kernel + attend_fine_kernel<128>" if fine_main else
+                        "aba_attend: order_kernel + attend_bf16_kernel<128,false>")
                        if w.dtype == "bf16" else "aba_attend: attend_f32_kernel<64,false>"),
             "bound": "mfma",
             "achieved": attend_tflops,

@@ -162,8 +162,9 @@ aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, i
  *   q, k, v   : [B,H,N_pad,D];  idx, cnt, w : as produced by aba_sample
  *   out       : out, [B,H,N_pad,D] in the plan's dtype
  *   workspace : at least p->workspace_bytes of device memory; required for
- *               ABA_BF16 (it holds a transposed copy of v), may be NULL for
- *               ABA_F32.  NULL where required -> ABA_E_INVALID. */
+ *               ABA_BF16 (it holds the work order, and at head_dim 64 a
+ *               transposed copy of v), may be NULL for ABA_F32.  NULL where
+ *               required -> ABA_E_INVALID. */
 aba_status aba_attend(const aba_plan_t *p, const void *q, const void *k, const void *v, const int32_t *idx,
                       const int32_t *cnt, const float *w, void *out, void *workspace, hipStream_t stream);
 
