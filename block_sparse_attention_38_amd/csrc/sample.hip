@@ -124,6 +124,33 @@ __device__ __forceinline__ uint64_t ceil_ratio_shift32(uint64_t x, uint64_t r, d
     return th;
 }
 
+// Whether block j (sigma - 1 = x) is kept: capped blocks always, any other iff
+// its draw is below theta = ceil((K - t) sigma 2^32 / R), i.e. draw R < x 2^32
+// with x = (K - t) sigma (exact 128-bit), or draw == 0 when K - t = 0.
+__device__ __forceinline__ bool keep_block(int j, uint32_t x, uint32_t draw, uint64_t cut, uint64_t Kt, uint64_t R)
+{
+    if (pack_key(x, j) >= cut) return true;
+    if (Kt == 0) return draw == 0;
+    return cmp_mul_shift32(draw, R, Kt * ((uint64_t)x + 1)) < 0;
+}
+
+// Horvitz-Thompson weight 2^32 / theta of kept block j (an fp64 division,
+// rounded to fp32); inv_r ~ 1/R for the exact ceiling of theta.
+__device__ __forceinline__ float kept_weight(int j, uint32_t x, uint64_t cut, uint64_t Kt, uint64_t R, double inv_r)
+{
+    uint64_t th;
+    if (pack_key(x, j) >= cut) {
+        th = kOne;
+    } else if (Kt == 0) {
+        th = 1;
+    } else {
+        const uint64_t xx = Kt * ((uint64_t)x + 1);
+        th = (xx >= R) ? kOne : ceil_ratio_shift32(xx, R, inv_r);
+        th = th < 1 ? 1 : (th > kOne ? kOne : th);
+    }
+    return (float)(4294967296.0 / (double)th);
+}
+
 template <typename T> __device__ __forceinline__ T wave_sum_t(T x)
 {
 #pragma unroll
@@ -578,11 +605,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         for (int e = 0; e < 4; ++e) {
             const int j = 4 * q + e;
             if (j >= NB) continue;
-            bool keep;
-            if (pack_key(xs[e], j) >= cut) keep = true;
-            else if (Kt == 0) keep = draw[e] == 0;                                     // theta = 1
-            else keep = cmp_mul_shift32(draw[e], R, Kt * ((uint64_t)xs[e] + 1)) < 0;   // draw R < x 2^32
-            nib |= (uint32_t)keep << e;
+            nib |= (uint32_t)keep_block(j, xs[e], draw[e], cut, Kt, R) << e;
         }
         bits[k >> 3] |= nib << (4 * (k & 7));
         mine += __popc(nib);
@@ -597,19 +620,8 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         kept_total += wtot[i];
     }
     const double inv_r = R > 0 ? 1.0 / (double)R : 0.0;
-    // weight 2^32 / theta of kept block j (sigma - 1 = x)
     auto weight_of = [&](int j, uint32_t x) __attribute__((always_inline)) {
-        uint64_t th;
-        if (pack_key(x, j) >= cut) {
-            th = kOne;
-        } else if (Kt == 0) {
-            th = 1;
-        } else {
-            const uint64_t xx = Kt * ((uint64_t)x + 1);
-            th = (xx >= R) ? kOne : ceil_ratio_shift32(xx, R, inv_r);
-            th = th < 1 ? 1 : (th > kOne ? kOne : th);
-        }
-        return (float)(4294967296.0 / (double)th);
+        return kept_weight(j, x, cut, Kt, R, inv_r);
     };
     // Positions in index order; the kept indices go to LDS (the space of the
     // sorted top, no longer needed), and all threads then form the weights of
@@ -653,6 +665,156 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
     if (tid == 0) cnt[row] = kept_total < cap ? kept_total : cap;
 }
 
+// ---------------------------------------------------------------------------
+// Rows of at most 1024 blocks (every 128-token row): one wavefront per row,
+// four rows per workgroup, no workgroup barriers.  The wavefront keeps sigma - 1
+// of its row in registers (quad 64k + lane at step k), sorts the packed keys of
+// the whole row in its own LDS region (bitonic, descending), finds the stopping
+// point of the water-filling with a scan over the sorted prefix, and draws,
+// keeps and compacts in index order as the long-row kernel does; the decisions
+// are the same, bit for bit.
+// ---------------------------------------------------------------------------
+constexpr int kWaveRowMax = 1024;
+
+template <int QPL>   // quads per lane: rows of up to 256 QPL blocks
+__global__ __launch_bounds__(256) void sample_wave_kernel(const float *__restrict__ scores, int H, int NBq, int NB,
+                                                          int K, uint64_t seed, int cap, int rows,
+                                                          int32_t *__restrict__ idx, int32_t *__restrict__ cnt,
+                                                          float *__restrict__ w)
+{
+    constexpr int kKeys = 256 * QPL;
+    __shared__ uint64_t keys_s[4][kKeys];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * 4 + wave;
+    if (row >= rows) return;   // the whole wavefront: nothing below waits for other wavefronts
+    uint64_t *keys = keys_s[wave];
+    const int qb = row % NBq, h = (row / NBq) % H, b = row / (NBq * H);
+    const float *srow = scores + (long)row * NB;
+    int32_t *irow = idx + (long)row * cap;
+    float *wrow = w + (long)row * cap;
+    const int NB4 = (NB + 3) / 4;
+
+    // sigma - 1 of the row (all loads in flight together) and the row total
+    float sv[QPL][4];
+#pragma unroll
+    for (int k = 0; k < QPL; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * (64 * k + lane) + e;
+            sv[k][e] = j < NB ? srow[j] : 0.f;
+        }
+    uint32_t x[QPL][4];
+    uint64_t part = 0;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * (64 * k + lane) + e;
+            x[k][e] = 0;
+            if (j < NB) {
+                const uint64_t sg = fixed_point(sv[k][e]);
+                part += sg;
+                x[k][e] = (uint32_t)(sg - 1);
+            }
+        }
+    const uint64_t total = wave_sum_t<uint64_t>(part);
+
+    if (K >= NB) {   // every block capped: keep all, weight 1
+        for (int j = lane; j < NB && j < cap; j += 64) {
+            irow[j] = j;
+            wrow[j] = 1.0f;
+        }
+        if (lane == 0) cnt[row] = NB < cap ? NB : cap;
+        return;
+    }
+
+    // packed keys (sigma desc, index asc when sorted descending); padding 0 sorts last
+    int P = 64;
+    while (P < NB) P <<= 1;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * (64 * k + lane) + e;
+            if (j < P) keys[j] = j < NB ? pack_key(x[k][e], j) : 0;
+        }
+    // bitonic sort of keys[0 .. P) by this wavefront: LDS operations of one
+    // wavefront complete in order, so each stage sees the previous one's writes
+    for (int size = 2; size <= P; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            __builtin_amdgcn_wave_barrier();
+            for (int i = lane; i < P / 2; i += 64) {
+                const int a = 2 * i - (i & (stride - 1)), c = a + stride;
+                const bool desc = (a & size) == 0;
+                const uint64_t ka = keys[a], kc = keys[c];
+                if ((ka < kc) == desc) {
+                    keys[a] = kc;
+                    keys[c] = ka;
+                }
+            }
+        }
+    __builtin_amdgcn_wave_barrier();
+
+    // stopping point: the first position p >= 1 with (K - p) sigma_p < total - sum of
+    // the first p, else K; R = total - sum of the first t; cut = the key at t - 1
+    int t = K;
+    uint64_t before = 0;   // sum of sigma over the positions before the current chunk
+    uint64_t pre_t = 0;
+    bool found = false;
+    for (int c0 = 0; c0 < K && !found; c0 += 64) {
+        const int p = c0 + lane;
+        const uint64_t sg = p < K ? (keys[p] >> kKeyIdxBits) + 1 : 0;
+        const uint64_t incl = before + wave_incl_scan<uint64_t>(sg, lane);
+        const bool fail = p >= 1 && p < K && (uint64_t)(K - p) * sg < total - (incl - sg);
+        const uint64_t fb = __ballot(fail);
+        if (fb) {
+            const int tt = __builtin_ctzll(fb);   // >= 1 in the first chunk
+            t = c0 + tt;
+            pre_t = tt > 0 ? __shfl(incl, tt - 1, 64) : before;
+            found = true;
+        } else {
+            before = __shfl(incl, 63, 64);
+        }
+    }
+    if (!found) pre_t = before;
+    const uint64_t R = total - pre_t, cut = keys[t - 1];
+    const uint64_t Kt = (uint64_t)(K - t);
+    const double inv_r = R > 0 ? 1.0 / (double)R : 0.0;
+
+    // draws, keep decisions and the compaction in index order
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    int base = 0;
+#pragma unroll
+    for (int k = 0; k < QPL; ++k) {
+        const int q = 64 * k + lane;
+        uint32_t nib = 0;
+        if (q < NB4) {
+            const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)qb, (uint32_t)h, (uint32_t)b), k0, k1);
+            const uint32_t draw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * q + e;
+                if (j < NB) nib |= (uint32_t)keep_block(j, x[k][e], draw[e], cut, Kt, R) << e;
+            }
+        }
+        const int c = __popc(nib);
+        const int incl = wave_incl_scan<int>(c, lane);
+        int pos = base + incl - c;
+        base += __shfl(incl, 63, 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (!((nib >> e) & 1u)) continue;
+            const int j = 4 * q + e;
+            if (pos < cap) {
+                irow[pos] = j;
+                wrow[pos] = kept_weight(j, x[k][e], cut, Kt, R, inv_r);
+            }
+            ++pos;
+        }
+    }
+    if (lane == 0) cnt[row] = base < cap ? base : cap;
+}
+
 }  // namespace
 
 // Keys of the sorted top (P of them, P = 2^ceil(log2 K) when K < NB, else 1)
@@ -673,8 +835,19 @@ size_t sample_lds_bytes(int NB, int K)
 hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int cap,
                          int32_t *idx, int32_t *cnt, float *w, hipStream_t s)
 {
-    const dim3 grid((unsigned)((long)B * H * NBq)), block(256);
+    const long rows = (long)B * H * NBq;
+    const dim3 grid((unsigned)rows), block(256);
     if (NB > kMaxFineBlocks) return hipErrorInvalidValue;
+    if (NB <= kWaveRowMax) {   // one wavefront per row
+        const dim3 wgrid((unsigned)((rows + 3) / 4));
+        if (NB <= 256)
+            sample_wave_kernel<1><<<wgrid, block, 0, s>>>(scores, H, NBq, NB, K, seed, cap, (int)rows, idx, cnt, w);
+        else if (NB <= 512)
+            sample_wave_kernel<2><<<wgrid, block, 0, s>>>(scores, H, NBq, NB, K, seed, cap, (int)rows, idx, cnt, w);
+        else
+            sample_wave_kernel<4><<<wgrid, block, 0, s>>>(scores, H, NBq, NB, K, seed, cap, (int)rows, idx, cnt, w);
+        return hipGetLastError();
+    }
     const size_t lds = sample_lds_bytes(NB, K);
     if (lds > kSampleLdsLimit) return hipErrorInvalidValue;
     const int P = topk_pad(NB, K);
