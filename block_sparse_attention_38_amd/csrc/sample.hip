@@ -97,7 +97,6 @@ constexpr int kKeyIdxBits = 15;                       // key blocks per row < 2^
 constexpr uint32_t kKeyIdxMask = (1u << kKeyIdxBits) - 1;
 constexpr int kFastTop = 64;                          // sorted top tried first (one wavefront)
 constexpr int kCandMax = 512;                         // blocks ranked directly for the fast top
-constexpr int kMaxQuadSteps = kMaxFineBlocks / 4 / 256;   // quads per lane at most
 
 __device__ __forceinline__ uint64_t pack_key(uint32_t sig_m1, int j)
 {
@@ -169,27 +168,28 @@ template <typename T> __device__ __forceinline__ T wave_incl_scan(T x, int lane)
     return x;
 }
 
-__global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restrict__ scores, int H, int NBq, int NB,
+template <int W, int STEPS>   // wavefronts per workgroup, quad steps per thread: rows of up to 256 W STEPS blocks
+__global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__restrict__ scores, int H, int NBq, int NB,
                                                           int K, uint64_t seed, int cap, int P,
                                                           int32_t *__restrict__ idx, int32_t *__restrict__ cnt,
                                                           float *__restrict__ w)
 {
+    constexpr int NT = 64 * W;
     extern __shared__ __align__(16) char dyn[];
     uint64_t *top = reinterpret_cast<uint64_t *>(dyn);                          // P keys
-    uint32_t *sig = reinterpret_cast<uint32_t *>(dyn + 16 * (((size_t)P + 1) / 2));   // 4 * NB4 values
-    __shared__ uint32_t red[2][4][4];
-    __shared__ __align__(16) int hist[4][256];
+    __shared__ uint32_t red[2][W][4];
+    __shared__ __align__(16) int hist[W][256];
     // the fast top's candidates share the histograms' space (the radix select
     // that uses them runs only when the candidates did not fit)
     uint64_t *const cand = reinterpret_cast<uint64_t *>(&hist[0][0]);
     static_assert(sizeof(hist) >= kCandMax * sizeof(uint64_t), "candidates fit in the histogram space");
     __shared__ int sel_s[3];
-    __shared__ uint64_t ured[4];
-    __shared__ uint32_t mm_s[2][4];
-    __shared__ int wtot[4];
+    __shared__ uint64_t ured[W];
+    __shared__ uint32_t mm_s[2][W];
+    __shared__ int wtot[W];
     __shared__ int top_n, t_s;
     __shared__ uint64_t r_s, cut_s;
-    __shared__ uint32_t lmax_s[256];   // largest sigma - 1 of each thread's blocks
+    __shared__ uint32_t lmax_s[NT];   // largest sigma - 1 of each thread's blocks
     __shared__ uint32_t lo_s;
     __shared__ int cand_n;
 
@@ -201,10 +201,15 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
     float *wrow = w + (long)row * cap;
 
     const int NB4 = (NB + 3) / 4;
-    const int Qw = ((NB4 + 3) / 4 + 63) / 64 * 64;   // quads per wavefront
+    const int Qw = ((NB4 + W - 1) / W + 63) / 64 * 64;   // quads per wavefront
     const int steps = Qw / 64;
     const int q0 = wave * Qw;
-    auto quad = [&](int k) { return q0 + 64 * k + lane; };   // valid if < NB4
+    auto quad = [&](int k) __attribute__((always_inline)) { return q0 + 64 * k + lane; };   // valid if < NB4
+    // sigma - 1 of this thread's quads, quad(k) in xr[k] (zero past the row): every
+    // pass below reads registers, and the LDS holds only the sorted top
+    uint4 xr[STEPS];
+#pragma unroll
+    for (int k = 0; k < STEPS; ++k) xr[k] = make_uint4(0, 0, 0, 0);
 
     // 1. fixed-point scores, row total, min and max of sigma - 1
     // (the scores of 8 steps are loaded before any is used, so that their
@@ -212,10 +217,13 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
     uint64_t part = 0;
     uint32_t vmin = 0xFFFFFFFFu, vmax = 0;
     constexpr int kLoadBatch = 8;
-    for (int k0 = 0; k0 < steps; k0 += kLoadBatch) {
+    static_assert(STEPS % kLoadBatch == 0 || STEPS < kLoadBatch, "whole load batches");
+#pragma unroll
+    for (int k0 = 0; k0 < STEPS; k0 += kLoadBatch) {
+        if (k0 >= steps) break;
         float sv[kLoadBatch][4];
 #pragma unroll
-        for (int kk = 0; kk < kLoadBatch; ++kk) {
+        for (int kk = 0; kk < kLoadBatch && k0 + kk < STEPS; ++kk) {
             const int q = quad(k0 + kk);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
             }
         }
 #pragma unroll
-        for (int kk = 0; kk < kLoadBatch; ++kk) {
+        for (int kk = 0; kk < kLoadBatch && k0 + kk < STEPS; ++kk) {
             const int q = quad(k0 + kk);
             if (k0 + kk >= steps || q >= NB4) continue;
             uint32_t x[4];
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
                     vmax = max(vmax, x[e]);
                 }
             }
-            *reinterpret_cast<uint4 *>(sig + 4 * q) = make_uint4(x[0], x[1], x[2], x[3]);
+            xr[k0 + kk] = make_uint4(x[0], x[1], x[2], x[3]);
         }
     }
     part = wave_sum_t<uint64_t>(part);
@@ -260,12 +268,18 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         cand_n = 0;
     }
     __syncthreads();
-    const uint64_t total = ured[0] + ured[1] + ured[2] + ured[3];
-    vmin = min(min(mm_s[0][0], mm_s[0][1]), min(mm_s[0][2], mm_s[0][3]));
-    vmax = max(max(mm_s[1][0], mm_s[1][1]), max(mm_s[1][2], mm_s[1][3]));
+    uint64_t total = 0;
+    vmin = 0xFFFFFFFFu;
+    vmax = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        total += ured[i];
+        vmin = min(vmin, mm_s[0][i]);
+        vmax = max(vmax, mm_s[1][i]);
+    }
 
     if (K >= NB) {   // every block capped: keep all, weight 1
-        for (int j = tid; j < NB; j += 256)
+        for (int j = tid; j < NB; j += NT)
             if (j < cap) {
                 irow[j] = j;
                 wrow[j] = 1.0f;
@@ -276,13 +290,14 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
 
     // Workgroup counts of a per-block predicate at 7 pivots (16-bit fields), one barrier.
     int parity = 0;
-    auto count7 = [&](auto pred) {
+    auto count7 = [&](auto pred) __attribute__((always_inline)) {
         uint32_t c[4] = {0, 0, 0, 0};
-#pragma unroll 4
-        for (int k = 0; k < steps; ++k) {
+#pragma unroll
+        for (int k = 0; k < STEPS; ++k) {
+            if (k >= steps) break;
             const int q = quad(k);
             if (q >= NB4) continue;
-            const uint4 xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+            const uint4 xv = xr[k];
             const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -301,25 +316,29 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         int out[7];
 #pragma unroll
         for (int i = 0; i < 7; ++i) {
-            const uint32_t s4 = red[parity][0][i >> 1] + red[parity][1][i >> 1] + red[parity][2][i >> 1] +
-                                red[parity][3][i >> 1];
+            uint32_t s4 = 0;
+#pragma unroll
+            for (int v = 0; v < W; ++v) s4 += red[parity][v][i >> 1];
             out[i] = (int)((s4 >> (16 * (i & 1))) & 0xFFFFu);
         }
         parity ^= 1;
         return std::array<int, 7>{out[0], out[1], out[2], out[3], out[4], out[5], out[6]};
     };
 
-    // the T-th largest of the threads' maxima (T <= 256, wavefront 0, into
+    // the T-th largest of the threads' maxima (T <= 64 W, wavefront 0, into
     // lo_s): a lower bound on the T-th largest value, since T threads each hold
     // a block at least that large
-    auto threads_bound = [&](int T) {
+    auto threads_bound = [&](int T) __attribute__((always_inline)) {
         if (wave == 0) {
-            const uint32_t a0 = lmax_s[lane], a1 = lmax_s[lane + 64], a2 = lmax_s[lane + 128], a3 = lmax_s[lane + 192];
+            uint32_t a[W];
+#pragma unroll
+            for (int i = 0; i < W; ++i) a[i] = lmax_s[lane + 64 * i];
             uint32_t v = 0;
             for (int bit = 31; bit >= 0; --bit) {   // largest v with >= T maxima >= v
                 const uint32_t c = v | (1u << bit);
-                const int n = __popcll(__ballot(a0 >= c)) + __popcll(__ballot(a1 >= c)) +
-                              __popcll(__ballot(a2 >= c)) + __popcll(__ballot(a3 >= c));
+                int n = 0;
+#pragma unroll
+                for (int i = 0; i < W; ++i) n += __popcll(__ballot(a[i] >= c));
                 if (n >= T) v = c;
             }
             if (lane == 0) lo_s = v > vmin ? v : vmin;
@@ -334,13 +353,14 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
     // sigma descending and index ascending) places the top T directly, sorted.
     // Otherwise the radix select below finds the T-th value and the top is
     // gathered unsorted.
-    auto gather_top = [&](int T, int PT) {
+    auto gather_top = [&](int T, int PT) __attribute__((always_inline)) {
         if (T <= kFastTop) {
             const uint32_t lo = threads_bound(T);
-            for (int k = 0; k < steps; ++k) {
+            #pragma unroll
+for (int k = 0; k < STEPS; ++k) {
+    if (k >= steps) break;
                 const int q = quad(k);
-                uint4 xv = make_uint4(0, 0, 0, 0);
-                if (q < NB4) xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+                const uint4 xv = xr[k];
                 const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -359,13 +379,13 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
             __syncthreads();
             const int C = cand_n;
             if (C <= kCandMax) {
-                for (int i = tid; i < C; i += 256) {
+                for (int i = tid; i < C; i += NT) {
                     const uint64_t key = cand[i];
                     int rank = 0;
                     for (int m = 0; m < C; ++m) rank += cand[m] > key;
                     if (rank < T) top[rank] = key;
                 }
-                for (int i = T + tid; i < PT; i += 256) top[i] = 0;
+                for (int i = T + tid; i < PT; i += NT) top[i] = 0;
                 __syncthreads();
                 return;
             }
@@ -376,10 +396,12 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         {
             // shortcut: fewer than T blocks above the minimum (rows whose scores mostly underflow)
             int above = 0;
-            for (int k = 0; k < steps; ++k) {
+            #pragma unroll
+for (int k = 0; k < STEPS; ++k) {
+    if (k >= steps) break;
                 const int q = quad(k);
                 if (q >= NB4) continue;
-                const uint4 xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+                const uint4 xv = xr[k];
                 const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) above += (4 * q + e < NB) && xs[e] > vmin;
@@ -387,7 +409,9 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
             above = wave_sum_t<int>(above);
             if (lane == 0) wtot[wave] = above;
             __syncthreads();
-            above = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+            above = 0;
+#pragma unroll
+            for (int i = 0; i < W; ++i) above += wtot[i];
             __syncthreads();
             if (above < T) {
                 v = vmin;
@@ -395,7 +419,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
                 n_eq = NB - above;
             } else {
                 // blocks below the threads' bound are never counted
-                const uint32_t lo = T <= 256 ? threads_bound(T) : vmin;
+                const uint32_t lo = T <= NT ? threads_bound(T) : vmin;
                 // radix select over [lo, vmax], 8 bits per pass from the top of the range
                 uint32_t base = lo;
                 int bits = 0;
@@ -409,10 +433,11 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
                     hist[wave][lane + 128] = 0;
                     hist[wave][lane + 192] = 0;
                     __syncthreads();
-                    for (int k = 0; k < steps; ++k) {
+                    #pragma unroll
+for (int k = 0; k < STEPS; ++k) {
+    if (k >= steps) break;
                         const int q = quad(k);
-                        uint4 xv = make_uint4(0, 0, 0, 0);
-                        if (q < NB4) xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+                        const uint4 xv = xr[k];
                         const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -431,8 +456,11 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
                         }
                     }
                     __syncthreads();
-                    const int bb = 255 - tid;   // bins from the top
-                    const int c = hist[0][bb] + hist[1][bb] + hist[2][bb] + hist[3][bb];
+                    const int bb = 255 - tid;   // bins from the top (the first 256 threads)
+                    int c = 0;
+                    if (bb >= 0)
+#pragma unroll
+                        for (int v = 0; v < W; ++v) c += hist[v][bb];
                     const int incl = wave_incl_scan<int>(c, lane);
                     if (lane == 63) wtot[wave] = incl;
                     __syncthreads();
@@ -475,10 +503,11 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
             }
             jcut = jh;
         }
-        for (int k = 0; k < steps; ++k) {
+        #pragma unroll
+for (int k = 0; k < STEPS; ++k) {
+    if (k >= steps) break;
             const int q = quad(k);
-            uint4 xv = make_uint4(0, 0, 0, 0);
-            if (q < NB4) xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
+            const uint4 xv = xr[k];
             const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -493,7 +522,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
                 }
             }
         }
-        for (int i = T + tid; i < PT; i += 256) top[i] = 0;   // below every real key (or equal, decoding alike)
+        for (int i = T + tid; i < PT; i += NT) top[i] = 0;   // below every real key (or equal, decoding alike)
         __syncthreads();
     };
 
@@ -539,7 +568,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         gather_top(K, PT);
         for (int size = 2; size <= PT; size <<= 1) {
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < PT / 2; i += 256) {
+                for (int i = tid; i < PT / 2; i += NT) {
                     const int a = 2 * i - (i & (stride - 1));
                     const int c = a + stride;
                     const bool desc = ((a & size) == 0);
@@ -554,7 +583,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
         }
         // first failure at a position 1 .. K-1, else K
         if (tid == 0) t_s = K;
-        const int qn = (K + 255) / 256;
+        const int qn = (K + NT - 1) / NT;
         const int p0 = min(K, tid * qn), p1 = min(K, p0 + qn);
         uint64_t local = 0;
         for (int p = p0; p < p1; ++p) local += (top[p] >> kKeyIdxBits) + 1;
@@ -590,32 +619,31 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
 
     // 4. keep decisions (4 bits per quad step), then the compaction in index order
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-    uint32_t bits[(kMaxQuadSteps + 7) / 8] = {};
+    uint32_t bits[(STEPS + 7) / 8] = {};
     int mine = 0;
-#pragma unroll 2
-    for (int k = 0; k < steps; ++k) {
-        const int q = quad(k);
-        if (q >= NB4) continue;
-        const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)qb, (uint32_t)h, (uint32_t)b), k0, k1);
-        const uint32_t draw[4] = {r.x, r.y, r.z, r.w};
-        const uint4 xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
-        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-        uint32_t nib = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = 4 * q + e;
-            if (j >= NB) continue;
-            nib |= (uint32_t)keep_block(j, xs[e], draw[e], cut, Kt, R) << e;
+    for (int k = 0; k < STEPS; ++k) {
+        const int q = quad(k);
+        if (k < steps && q < NB4) {
+            const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)qb, (uint32_t)h, (uint32_t)b), k0, k1);
+            const uint32_t draw[4] = {r.x, r.y, r.z, r.w};
+            const uint32_t xs[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+            uint32_t nib = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * q + e;
+                if (j < NB) nib |= (uint32_t)keep_block(j, xs[e], draw[e], cut, Kt, R) << e;
+            }
+            bits[k >> 3] |= nib << (4 * (k & 7));
+            mine += __popc(nib);
         }
-        bits[k >> 3] |= nib << (4 * (k & 7));
-        mine += __popc(nib);
     }
     mine = wave_sum_t<int>(mine);
     if (lane == 0) wtot[wave] = mine;
     __syncthreads();
     int running = 0, kept_total = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < W; ++i) {
         if (i < wave) running += wtot[i];
         kept_total += wtot[i];
     }
@@ -628,45 +656,49 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
     // consecutive positions: balanced work and coalesced stores.  A list
     // longer than that space is written directly, each thread its own blocks.
     const int n_out = kept_total < cap ? kept_total : cap;
-    uint32_t *const lst = reinterpret_cast<uint32_t *>(top);
-    const bool staged = n_out <= 2 * P;
-    for (int k = 0; k < steps; ++k) {
-        const uint32_t nib = (bits[k >> 3] >> (4 * (k & 7))) & 15u;
-        const int c = __popc(nib);
-        const int incl = wave_incl_scan<int>(c, lane);
-        int pos = running + incl - c;
-        running += __shfl(incl, 63, 64);
-        if (!nib) continue;
-        const int q = quad(k);
-        const uint4 xv = *reinterpret_cast<const uint4 *>(sig + 4 * q);
-        const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
-        for (uint32_t rest = nib; rest; rest &= rest - 1) {
-            const int e = __builtin_ctz(rest);
-            const int j = 4 * q + e;
-            if (pos < cap) {
-                if (staged) {
-                    lst[pos] = (uint32_t)j;
-                } else {
-                    irow[pos] = j;
-                    wrow[pos] = weight_of(j, xs[e]);
+    uint32_t *const lst = reinterpret_cast<uint32_t *>(top);   // P indices, then their sigma - 1
+    const bool staged = n_out <= P;
+#pragma unroll
+    for (int k = 0; k < STEPS; ++k) {
+        if (k < steps) {
+            const uint32_t nib = (bits[k >> 3] >> (4 * (k & 7))) & 15u;
+            const int c = __popc(nib);
+            const int incl = wave_incl_scan<int>(c, lane);
+            int pos = running + incl - c;
+            running += __shfl(incl, 63, 64);
+            const int q = quad(k);
+            const uint32_t xs[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if ((nib >> e) & 1u) {
+                    const int j = 4 * q + e;
+                    if (pos < cap) {
+                        if (staged) {
+                            lst[pos] = (uint32_t)j;
+                            lst[P + pos] = xs[e];
+                        } else {
+                            irow[pos] = j;
+                            wrow[pos] = weight_of(j, xs[e]);
+                        }
+                    }
+                    ++pos;
                 }
             }
-            ++pos;
         }
     }
     if (staged) {
         __syncthreads();
-        for (int p = tid; p < n_out; p += 256) {
+        for (int p = tid; p < n_out; p += NT) {
             const int j = (int)lst[p];
             irow[p] = j;
-            wrow[p] = weight_of(j, sig[j]);
+            wrow[p] = weight_of(j, lst[P + p]);
         }
     }
     if (tid == 0) cnt[row] = kept_total < cap ? kept_total : cap;
 }
 
 // ---------------------------------------------------------------------------
-// Rows of at most 1024 blocks (every 128-token row): one wavefront per row,
+// Rows of at most 256 blocks (128-token rows up to 32K tokens): one wavefront per row,
 // four rows per workgroup, no workgroup barriers.  The wavefront keeps sigma - 1
 // of its row in registers (quad 64k + lane at step k), sorts the packed keys of
 // the whole row in its own LDS region (bitonic, descending), finds the stopping
@@ -674,7 +706,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const float *__restric
 // keeps and compacts in index order as the long-row kernel does; the decisions
 // are the same, bit for bit.
 // ---------------------------------------------------------------------------
-constexpr int kWaveRowMax = 1024;
+constexpr int kWaveRowMax = 256;   // longer rows: a whole-row sort per wavefront costs more than the top-K kernel
 
 template <int QPL>   // quads per lane: rows of up to 256 QPL blocks
 __global__ __launch_bounds__(256) void sample_wave_kernel(const float *__restrict__ scores, int H, int NBq, int NB,
@@ -828,8 +860,8 @@ static int topk_pad(int NB, int K)
 
 size_t sample_lds_bytes(int NB, int K)
 {
-    const size_t P = (size_t)topk_pad(NB, K);
-    return 16 * ((P + 1) / 2) + 16 * (((size_t)NB + 3) / 4);
+    if (NB <= kWaveRowMax) return 0;   // the wavefront-per-row kernel: static LDS only
+    return 8 * (size_t)topk_pad(NB, K);
 }
 
 hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int cap,
@@ -840,23 +872,28 @@ hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int
     if (NB > kMaxFineBlocks) return hipErrorInvalidValue;
     if (NB <= kWaveRowMax) {   // one wavefront per row
         const dim3 wgrid((unsigned)((rows + 3) / 4));
-        if (NB <= 256)
-            sample_wave_kernel<1><<<wgrid, block, 0, s>>>(scores, H, NBq, NB, K, seed, cap, (int)rows, idx, cnt, w);
-        else if (NB <= 512)
-            sample_wave_kernel<2><<<wgrid, block, 0, s>>>(scores, H, NBq, NB, K, seed, cap, (int)rows, idx, cnt, w);
-        else
-            sample_wave_kernel<4><<<wgrid, block, 0, s>>>(scores, H, NBq, NB, K, seed, cap, (int)rows, idx, cnt, w);
+        sample_wave_kernel<1><<<wgrid, block, 0, s>>>(scores, H, NBq, NB, K, seed, cap, (int)rows, idx, cnt, w);
         return hipGetLastError();
     }
     const size_t lds = sample_lds_bytes(NB, K);
     if (lds > kSampleLdsLimit) return hipErrorInvalidValue;
     const int P = topk_pad(NB, K);
-    // allow more than the default dynamic LDS (a host-side attribute of the current device)
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&sample_topk_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSampleLdsLimit);
-    if (e != hipSuccess) return e;
-    sample_topk_kernel<<<grid, block, lds, s>>>(scores, H, NBq, NB, K, seed, cap, P, idx, cnt, w);
-    return hipGetLastError();
+    // as few quad steps per thread as the row needs: 1 to 8 on 4 wavefronts, 8 or 16 on 8
+    auto launch = [&](auto kernel, int threads) {
+        // allow more than the default dynamic LDS (a host-side attribute of the current device);
+        // exactly this launch's size, which with the kernel's static LDS stays within a CU's
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        kernel<<<grid, dim3(threads), lds, s>>>(scores, H, NBq, NB, K, seed, cap, P, idx, cnt, w);
+        return hipGetLastError();
+    };
+    if (NB <= 256 * 4 * 1) return launch(&sample_topk_kernel<4, 1>, 256);
+    if (NB <= 256 * 4 * 2) return launch(&sample_topk_kernel<4, 2>, 256);
+    if (NB <= 256 * 4 * 4) return launch(&sample_topk_kernel<4, 4>, 256);
+    if (NB <= 256 * 4 * 8) return launch(&sample_topk_kernel<4, 8>, 256);
+    if (NB <= 256 * 8 * 8) return launch(&sample_topk_kernel<8, 8>, 512);
+    return launch(&sample_topk_kernel<8, 16>, 512);
 }
 
 }  // namespace aba

@@ -106,8 +106,8 @@ typedef struct aba_plan {
  * than 128 or 4, or a null p, and ABA_E_UNSUPPORTED for a head_dim/dtype pair
  * without kernels (4-token key blocks: bf16 with head_dim 128, or fp32 with
  * 64), more than ABA_MAX_BLOCKS query blocks, more than ABA_MAX_CLUSTERS
- * clusters, or a 4-token budget whose sampling state exceeds the LDS of a CU
- * (8 * 2^ceil(log2 K) + 4 * NBk bytes > 155648 when K < NBk). */
+ * clusters, or a 4-token budget whose sorted top exceeds the LDS of a CU
+ * (8 * 2^ceil(log2 K) bytes > 155648, when 1024 < NBk and K < NBk). */
 aba_status aba_plan(aba_plan_t *p, int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
                     aba_dtype dtype, int32_t n_clusters, int32_t kmeans_iters, int32_t budget, int32_t key_block,
                     float softmax_scale);
