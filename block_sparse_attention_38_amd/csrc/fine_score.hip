@@ -381,14 +381,16 @@ __global__ __launch_bounds__(64) void fine_merge_kernel(const float2 *__restrict
 }
 
 // ---------------------------------------------------------------------------
-// One-pass scoring of short rows.  Workgroup (b, h, centroid tile ct): the 32
-// slots' split centroids are the A operand, held in registers; wavefront w
-// computes the logit tiles of key blocks [32t, 32t + 32) for t = w, w + 4, ...
-// (three split-bf16 MFMA terms per k-step, as in the two-pass kernels, in S
-// orientation: rows = slots, columns = key blocks) and stores them, in the
-// log2 domain, to LDS rows of one slot each.  Then 8 threads per slot reduce
-// its row to the maximum M and the normaliser Z (coefficient w_m / Z), and
-// every (query block, key block) score is summed over the block's centroids.
+// One-pass scoring of short rows.  Workgroup (b, h, centroid tile ct): the
+// workgroup loads the 32 slots' centroids once and splits them into bf16 hi and
+// lo parts in LDS, from where every wavefront takes its A operand into registers;
+// wavefront w computes the logit tiles of key blocks [32t, 32t + 32) for
+// t = w, w + 4, ... (three split-bf16 MFMA terms per k-step, as in the
+// two-pass kernels, in S orientation: rows = slots, columns = key blocks) and
+// stores them, in the log2 domain, to LDS rows of one slot each.  Then 8 threads
+// per slot reduce its row to the maximum M and the normaliser Z (coefficient
+// w_m / Z), and every (query block, key block) score is summed over the block's
+// centroids.
 // ---------------------------------------------------------------------------
 constexpr int kRowMaxBlocks = 1024;
 
@@ -402,9 +404,12 @@ __global__ __launch_bounds__(256) void row_score_kernel(const float *__restrict_
                                                         const float *__restrict__ kbar, int NBq, int NBk, int C,
                                                         float scale_log2, float *__restrict__ scores)
 {
-    constexpr int KS = D / 16;
+    constexpr int KS = D / 16, DCH = D / 8;
     extern __shared__ float xs[];              // logits [32 slots][pitch]
     __shared__ float2 st[kTileSlots];          // (M, coefficient) per slot
+    // split centroid tile: chunk c (8 elements) of slot r at r * DCH + (c ^ (r % DCH)),
+    // so the 16 slots one phase of a fragment read touches sit on different banks
+    __shared__ bf16x8 c_hi[kTileSlots * DCH], c_lo[kTileSlots * DCH];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -413,14 +418,10 @@ __global__ __launch_bounds__(256) void row_score_kernel(const float *__restrict_
     const int ct = blockIdx.x % NT;
     const long bh = blockIdx.x / NT;
     const int pitch = row_pitch(NBk);
+    const int n32 = 32 * ((NBk + 31) / 32);    // logit columns written (-inf past NBk)
 
-    // A operand: slot l32 (query block 4ct + l32/8, centroid l32%8), elements
-    // 16ks + 8half .. +7; slots past C or past the last query block are zero
-    const int qb_s = kTileBlocks * ct + l32 / kSlots, m_s = l32 % kSlots;
-    const bool slot_ok = qb_s < NBq && m_s < C;
-    const float *crow = cent + ((bh * NBq + qb_s) * C + m_s) * D;
     // pooled keys of key tile t (block 32t + l32), elements 16ks + 8half .. +7
-    const int n_tiles = (NBk + 31) / 32;
+    const int n_tiles = n32 / 32;
     auto load_keys = [&](int t, float (&kx)[KS][8]) __attribute__((always_inline)) {
         const int j = 32 * t + l32;
         const float *krow = kbar + (bh * NBk + j) * D;
@@ -434,12 +435,26 @@ __global__ __launch_bounds__(256) void row_score_kernel(const float *__restrict_
     // the first key tile's loads go out with the centroids'
     float kx[KS][8];
     load_keys(wave, kx);
+    // slot r = query block 4ct + r/8, centroid r%8; slots past C or past the last
+    // query block are zero
+#pragma unroll
+    for (int i = 0; i < kTileSlots * DCH / 256; ++i) {
+        const int q = tid + 256 * i, r = q / DCH, c = q % DCH;
+        const int qb = kTileBlocks * ct + r / kSlots, m = r % kSlots;
+        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (qb < NBq && m < C) load8(cent + ((bh * NBq + qb) * C + m) * D + 8 * c, x);
+        bf16x8 hi, lo;
+        split8(x, hi, lo);
+        c_hi[r * DCH + (c ^ (r % DCH))] = hi;
+        c_lo[r * DCH + (c ^ (r % DCH))] = lo;
+    }
+    __syncthreads();
+    // A operand: slot l32, elements 16ks + 8half .. +7 (chunk 2ks + half)
     bf16x8 chi[KS], clo[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (slot_ok) load8(crow + 16 * ks + 8 * half, x);
-        split8(x, chi[ks], clo[ks]);
+        chi[ks] = c_hi[l32 * DCH + ((2 * ks + half) ^ (l32 % DCH))];
+        clo[ks] = c_lo[l32 * DCH + ((2 * ks + half) ^ (l32 % DCH))];
     }
 
     for (int t = wave; t < n_tiles; t += 4) {
@@ -461,15 +476,23 @@ __global__ __launch_bounds__(256) void row_score_kernel(const float *__restrict_
     }
     __syncthreads();
 
-    {   // per-slot maximum and normaliser: 8 consecutive threads per slot
+    {   // per-slot maximum and normaliser: 8 consecutive threads per slot, four
+        // independent chains each so that the LDS reads overlap (columns past NBk
+        // hold -inf and add nothing)
         const int sl = tid >> 3, sub = tid & 7;
         const float *row = xs + sl * pitch;
-        float M = -INFINITY;
-        for (int j = sub; j < NBk; j += 8) M = fmaxf(M, row[j]);
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        for (int j = sub; j < n32; j += 32)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) m4[u] = fmaxf(m4[u], row[j + 8 * u]);
+        float M = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-        float Z = 0.f;
-        for (int j = sub; j < NBk; j += 8) Z += __builtin_amdgcn_exp2f(row[j] - M);
+        float z4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j = sub; j < n32; j += 32)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) z4[u] += __builtin_amdgcn_exp2f(row[j + 8 * u] - M);
+        float Z = (z4[0] + z4[1]) + (z4[2] + z4[3]);
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) Z += __shfl_xor(Z, o, 64);
         if (sub == 0) {
@@ -481,12 +504,14 @@ __global__ __launch_bounds__(256) void row_score_kernel(const float *__restrict_
     }
     __syncthreads();
 
-    // scores of the tile's query blocks: consecutive threads, consecutive key blocks
+    // scores of the tile's query blocks: consecutive threads, consecutive key
+    // blocks; slots past C have coefficient 0 and finite logits (zero centroids)
     const int n_qb = min(kTileBlocks, NBq - kTileBlocks * ct);
     for (int i = tid; i < n_qb * NBk; i += 256) {
         const int p = i / NBk, j = i - p * NBk;
         float a = 0.f;
-        for (int m = 0; m < C; ++m) {
+#pragma unroll
+        for (int m = 0; m < kSlots; ++m) {
             const float2 sv = st[kSlots * p + m];
             a += sv.y * __builtin_amdgcn_exp2f(xs[(kSlots * p + m) * pitch + j] - sv.x);
         }
