@@ -168,9 +168,12 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T *__restrict__ q, in
 //               clusters for its query and adds them locally; the argmin needs
 //               one exchange between the two lane halves.
 //   update      sums = onehot^T X with X^T staged once per block in LDS; new
-//               centroids are sums / counts (counts from wavefront ballots);
-//               the lanes that form a centroid element also write its three
-//               bf16 parts and its share of |c|^2, so a round has two barriers.
+//               centroids are sums / counts.  The one-hot operand comes from
+//               the assignment bytes with a few bit operations per four
+//               queries, and the same flags give the counts (popcounts), so
+//               no separate counting pass runs per round; the lanes that form
+//               a centroid element also write its three bf16 parts and its
+//               share of |c|^2, so a round has two barriers.
 // A round whose assignment equals the previous round's leaves every later
 // round unchanged bit for bit (same rows, same sums), so the loop stops there:
 // the result is exactly that of all T rounds.
@@ -186,6 +189,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Bit 7 of byte i set iff byte i of x equals byte i of pat, all other bits clear:
+// t = x ^ pat is zero exactly in the matching bytes; (t & 0x7f) + 0x7f carries
+// into bit 7 iff the low seven bits are not all zero, and no byte carries into
+// the next.
+__device__ __forceinline__ uint32_t match_bytes(uint32_t x, uint32_t pat)
+{
+    const uint32_t t = x ^ pat;
+    return ~(((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t) & 0x80808080u;
+}
+
+// Eight bf16 values from the flags of eight bytes (f0: elements 0..3, f1: 4..7):
+// 4.0 (0x4080: low byte 0x80, high byte 0x40) for a set flag, else 0.  Byte
+// permutes interleave each flag byte (0x80 / 0) with itself shifted right by one
+// (0x40 / 0).
+__device__ __forceinline__ uint4 onehot4(uint32_t f0, uint32_t f1)
+{
+    const uint32_t g0 = f0 >> 1, g1 = f1 >> 1;
+    // selector bytes 0..3 pick bytes of the second operand, 4..7 of the first
+    return make_uint4(__builtin_amdgcn_perm(g0, f0, 0x05010400u), __builtin_amdgcn_perm(g0, f0, 0x07030602u),
+                      __builtin_amdgcn_perm(g1, f1, 0x05010400u), __builtin_amdgcn_perm(g1, f1, 0x07030602u));
+}
 
 // The same workgroup then pools the keys of its 128 tokens (IBCS paragraph:
 // a key block is represented by its averaged keys): one 128-token key block
@@ -211,7 +236,6 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
     // four workgroups per CU)
     __shared__ uint4 cs_s[24 * DCH];
     __shared__ __align__(16) uint8_t asg[kBlock];
-    __shared__ int cnt_part[4][kMaxClusters];
     __shared__ float cn_part[4][kMaxClusters];   // per-wavefront shares of |c_m|^2
 
     const int row = blockIdx.x;                           // (b*H + h) * NB + query block
@@ -337,11 +361,6 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
             bm = om;
         }
         if (half == 0) asg[my_q] = qv ? (uint8_t)bm : (uint8_t)0xFF;
-#pragma unroll
-        for (int m = 0; m < kMaxClusters; ++m) {
-            const unsigned long long b = __ballot(qv && half == 0 && bm == m);
-            if (lane == 0) cnt_part[wave][m] = __popcll(b);
-        }
         const int changed = (half == 0 && qv && bm != prev) ? 1 : 0;
         prev = bm;
         const int any_changed = __syncthreads_or(changed);
@@ -353,27 +372,33 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
 #pragma unroll
             for (int r = 0; r < 16; ++r) sum[r] = 0.f;
             const int d = wave * 32 + l32;
+            // A operand row l32 is cluster l32 % 8 (rows >= 8 only feed accumulator
+            // rows that are never read); its entries are 4.0 (bf16 0x4080) where the
+            // query's assignment byte equals the cluster, so the sums are 4x the
+            // cluster sums, exactly
+            const uint32_t pat = 0x01010101u * (uint32_t)(l32 & 7);
+            int cnt = 0;
 #pragma unroll
             for (int ks = 0; ks < kBlock / 16; ++ks) {
                 const uint2 ab = *reinterpret_cast<const uint2 *>(&asg[16 * ks + 8 * half]);
-                bf16x8 oh;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t byte = ((e < 4 ? ab.x : ab.y) >> (8 * (e & 3))) & 0xFFu;
-                    oh[e] = (byte == (uint32_t)l32) ? (__bf16)1.0f : (__bf16)0.0f;
-                }
+                const uint32_t f0 = match_bytes(ab.x, pat), f1 = match_bytes(ab.y, pat);
+                cnt += __popc(f0) + __popc(f1);
+                const uint4 oh = onehot4(f0, f1);
                 const uint4 b = xt_s[d * 16 + ((2 * ks + half) ^ xt_swz(d))];
-                sum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oh, __builtin_bit_cast(bf16x8, b), sum, 0, 0, 0);
+                sum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, oh),
+                                                              __builtin_bit_cast(bf16x8, b), sum, 0, 0, 0);
             }
+            // lane m < 8 (either half) counted cluster m over its half of the queries
+            cnt += __shfl_xor(cnt, 32, 64);
             // lane holds the sums of clusters 4half .. 4half+3 for dim d
             float sq[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = 4 * half + r;
-                const int cn = cnt_part[0][m] + cnt_part[1][m] + cnt_part[2][m] + cnt_part[3][m];
+                const int cn = __shfl(cnt, m, 64);
                 float cv;
                 if (m < C && cn > 0) {
-                    cv = sum[r] / (float)cn;
+                    cv = sum[r] / (float)(4 * cn);   // (4 sum) / (4 n) rounds as sum / n
                     const uint16_t hb = f32_to_bf16_bits(cv);
                     const float r1 = cv - bf16_bits_to_f32(hb);
                     const uint16_t mb = f32_to_bf16_bits(r1);
@@ -402,8 +427,12 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
 
     float *co = cent_out + (long)row * C * D;
     for (int i = tid; i < C * D; i += 256) co[i] = centroid(i / D, i % D);
-    if (tid < C) {
-        const int cn = cnt_part[0][tid] + cnt_part[1][tid] + cnt_part[2][tid] + cnt_part[3][tid];
+    if (tid < C) {   // weights from the last assignment
+        const uint32_t pat = 0x01010101u * (uint32_t)tid;
+        const uint32_t *a4 = reinterpret_cast<const uint32_t *>(asg);
+        int cn = 0;
+#pragma unroll 8
+        for (int i = 0; i < kBlock / 4; ++i) cn += __popc(match_bytes(a4[i], pat));
         w_out[(long)row * C + tid] = (float)((double)cn / (double)n);
     }
 
