@@ -48,7 +48,7 @@ hipError_t launch_attend_fine(const void *q, const void *k, const void *v, int d
 // Attention mass per key block of kb tokens (128 or 4) for the listed query blocks.
 hipError_t launch_block_mass(const void *q, const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB,
                              int kb, float scale, const int32_t *items, int n_items, float *mass, hipStream_t s);
-// Device bytes launch_attend needs at ws (the V^T copy and the work order; 0 for fp32).
+// Device bytes launch_attend needs at ws (the work order, and at head_dim 64 the V^T copy; 0 for fp32).
 size_t attend_workspace_bytes(int dtype, int B, int H, int N_pad, int D);
 
 // ---------------------------------------------------------------------------

@@ -39,7 +39,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // the duration of the call: aba_score keeps centroids, weights and pooled keys
 // there when the caller does not ask for them (and, for 4-token key blocks, the
 // per-chunk softmax statistics of its two-pass scoring), aba_attend and
-// aba_attend_full the V^T staging copy of v and the work order.
+// aba_attend_full the work order (and at head_dim 64 a V^T staging copy of v).
 struct Workspace {
     size_t cent, weight, kbar, fine, score_total, attend_total, total;
 };

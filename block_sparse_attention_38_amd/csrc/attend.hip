@@ -553,9 +553,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 
     // Sub-tile u is half u % 2 of list entry u / 2; its K sits in K slot u % 3,
-    // its V^T in V slot u % 2.  Iteration u issues V^T(u + 1) and then K(u + 2),
-    // computes u, and waits for all but the K(u + 2) loads: K(u + 1) and
-    // V^T(u + 1) are then in LDS.  The entry loop is unrolled three times, so
+    // its V (rows, or the V^T tile at head_dim 64) in V slot u % 2.  Iteration u
+    // issues V(u + 1) and then K(u + 2), computes u, and waits for all but the
+    // K(u + 2) loads: K(u + 1) and V(u + 1) are then in LDS.  The entry loop is unrolled three times, so
     // every slot is a compile-time offset.  Branches are uniform over the
     // workgroup; invalid entries and sub-tiles past N load and compute nothing.
     constexpr int KL = Dma<D>::loads;
@@ -582,12 +582,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (!full && e2 < n_list && (e2 & 63) == 0) win = load_window<full>(lrow, wrow, e2 >> 6, n_list, NB, lane);
         const Entry nn = e2 < n_list ? window_entry<full>(win, e2) : none;
         const bool ce_hi = hi_valid(ce), ne_ok = ne.j >= 0, ne_hi = hi_valid(ne);
-        // first half: V^T of the second half, K of the next entry's first half
+        // first half: V of the second half, K of the next entry's first half
         if (ce_hi) issue_v<D>(rv, ce.j * kBlock + kSub, vptr(1), wave, dma);
         if (ne_ok) issue_k<D>(rk, ne.j * kBlock, kptr((2 * E3 + 2) % 3), wave, dma);
         if (ce.j >= 0) tile(kptr(k0), vptr(0), ce.j * kBlock, ce.lw);
         if (ne_ok) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
-        // second half: V^T of the next entry's first half, K of its second half
+        // second half: V of the next entry's first half, K of its second half
         if (ne_ok) issue_v<D>(rv, ne.j * kBlock, vptr(0), wave, dma);
         if (ne_hi) issue_k<D>(rk, ne.j * kBlock + kSub, kptr((2 * E3 + 3) % 3), wave, dma);
         if (ce_hi) tile(kptr(k1), vptr(1), ce.j * kBlock + kSub, ce.lw);
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // the compute tile).  A list entry is a key block of 4 tokens; 16 of them fill
 // a 64-key sub-tile, gathered by index with direct loads into the same LDS
 // ring as above, so the MFMA work per sub-tile is unchanged.  At D = 128 one
-// 4-token block of K (4 rows) or of V^T is exactly 1024 bytes, one direct load
+// 4-token block of K or V (4 rows) is exactly 1024 bytes, one direct load
 // of a wavefront: load t of wavefront w fills block slot 4w + t, its source
 // address a scalar (block index x 1024) taken from the list window with
 // v_readlane.
@@ -710,7 +710,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     static_assert(D == 128, "a 4-token key block of K or V is one 1024-byte direct load at D = 128");
     using L = Lds<D>;
     constexpr int KS = D / 16, DT = D / 32, KT = kSub / 32, NK = KT * KS, NV = KT * 2 * DT, PF = 4;
-    constexpr int GB = kFineBlock * D * 2;   // bytes of one 4-token block of K or V^T
+    constexpr int GB = kFineBlock * D * 2;   // bytes of one 4-token block of K or V
     constexpr int KL = kFineSub / kWaves;    // direct loads per wavefront and tensor per sub-tile
     __shared__ __align__(16) char ks0[L::kBytes], ks1[L::kBytes], ks2[L::kBytes];
     __shared__ __align__(16) char vs0[L::vBytes], vs1[L::vBytes];
@@ -903,8 +903,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // Sub-tile u: K in K slot u % 3, V^T in V slot u % 2.  Iteration u issues
-    // V^T(u + 1) and K(u + 2), computes u and waits for all but the K(u + 2)
+    // Sub-tile u: K in K slot u % 3, V in V slot u % 2.  Iteration u issues
+    // V(u + 1) and K(u + 2), computes u and waits for all but the K(u + 2)
     // loads.  Window m (sub-tiles 4m .. 4m+3) sits in win{m % 2}; the entries of
     // window m + 1 are loaded at iteration 4m and validated at 4m + 2, just
     // before their first use, so the wait the compiler puts before that use
