@@ -157,6 +157,17 @@ template <typename T> __device__ __forceinline__ T wave_sum_t(T x)
     return x;
 }
 
+// Maximum over the 64 lanes of a wavefront.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t y = __shfl_xor(x, o, 64);
+        x = y > x ? y : x;
+    }
+    return x;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 template <typename T> __device__ __forceinline__ T wave_incl_scan(T x, int lane)
 {
@@ -700,11 +711,12 @@ for (int k = 0; k < STEPS; ++k) {
 // ---------------------------------------------------------------------------
 // Rows of at most 256 blocks (128-token rows up to 32K tokens): one wavefront per row,
 // four rows per workgroup, no workgroup barriers.  The wavefront keeps sigma - 1
-// of its row in registers (quad 64k + lane at step k), sorts the packed keys of
-// the whole row in its own LDS region (bitonic, descending), finds the stopping
-// point of the water-filling with a scan over the sorted prefix, and draws,
-// keeps and compacts in index order as the long-row kernel does; the decisions
-// are the same, bit for bit.
+// of its row in registers (quad 64k + lane at step k).  The two largest packed
+// keys tell whether the water-filling stops right after the top block; only
+// when it does not does the wavefront sort the packed keys of the whole row in
+// its own LDS region (bitonic, descending) and find the stopping point with a
+// scan over the sorted prefix.  It then draws, keeps and compacts in index order
+// as the long-row kernel does; the decisions are the same, bit for bit.
 // ---------------------------------------------------------------------------
 constexpr int kWaveRowMax = 256;   // longer rows: a whole-row sort per wavefront costs more than the top-K kernel
 
@@ -760,56 +772,90 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(const float *__restric
         return;
     }
 
-    // packed keys (sigma desc, index asc when sorted descending); padding 0 sorts last
-    int P = 64;
-    while (P < NB) P <<= 1;
+    // The stopping point is 1 (only the top block forced) exactly when K = 1 or
+    // (K - 1) sigma_(2) < total - sigma_(1): the two largest keys decide it, and
+    // the sort is needed only otherwise.
+    int t = K;
+    uint64_t pre_t = 0, cut = 0;
+    bool sorted_path = true;
+    {
+        uint64_t k1 = 0, k2 = 0;   // this lane's largest and second largest keys
 #pragma unroll
-    for (int k = 0; k < QPL; ++k)
+        for (int k = 0; k < QPL; ++k)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = 4 * (64 * k + lane) + e;
-            if (j < P) keys[j] = j < NB ? pack_key(x[k][e], j) : 0;
-        }
-    // bitonic sort of keys[0 .. P) by this wavefront: LDS operations of one
-    // wavefront complete in order, so each stage sees the previous one's writes
-    for (int size = 2; size <= P; size <<= 1)
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            __builtin_amdgcn_wave_barrier();
-            for (int i = lane; i < P / 2; i += 64) {
-                const int a = 2 * i - (i & (stride - 1)), c = a + stride;
-                const bool desc = (a & size) == 0;
-                const uint64_t ka = keys[a], kc = keys[c];
-                if ((ka < kc) == desc) {
-                    keys[a] = kc;
-                    keys[c] = ka;
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * (64 * k + lane) + e;
+                if (j < NB) {
+                    const uint64_t kk = pack_key(x[k][e], j);
+                    if (kk > k1) {
+                        k2 = k1;
+                        k1 = kk;
+                    } else if (kk > k2) {
+                        k2 = kk;
+                    }
                 }
             }
-        }
-    __builtin_amdgcn_wave_barrier();
-
-    // stopping point: the first position p >= 1 with (K - p) sigma_p < total - sum of
-    // the first p, else K; R = total - sum of the first t; cut = the key at t - 1
-    int t = K;
-    uint64_t before = 0;   // sum of sigma over the positions before the current chunk
-    uint64_t pre_t = 0;
-    bool found = false;
-    for (int c0 = 0; c0 < K && !found; c0 += 64) {
-        const int p = c0 + lane;
-        const uint64_t sg = p < K ? (keys[p] >> kKeyIdxBits) + 1 : 0;
-        const uint64_t incl = before + wave_incl_scan<uint64_t>(sg, lane);
-        const bool fail = p >= 1 && p < K && (uint64_t)(K - p) * sg < total - (incl - sg);
-        const uint64_t fb = __ballot(fail);
-        if (fb) {
-            const int tt = __builtin_ctzll(fb);   // >= 1 in the first chunk
-            t = c0 + tt;
-            pre_t = tt > 0 ? __shfl(incl, tt - 1, 64) : before;
-            found = true;
-        } else {
-            before = __shfl(incl, 63, 64);
+        const uint64_t m1 = wave_max_u64(k1);
+        const uint64_t m2 = wave_max_u64(k1 == m1 ? k2 : k1);   // NB >= 2 here, so a real key
+        const uint64_t s1 = (m1 >> kKeyIdxBits) + 1, s2 = (m2 >> kKeyIdxBits) + 1;
+        if (K == 1 || (uint64_t)(K - 1) * s2 < total - s1) {
+            t = 1;
+            pre_t = s1;
+            cut = m1;
+            sorted_path = false;
         }
     }
-    if (!found) pre_t = before;
-    const uint64_t R = total - pre_t, cut = keys[t - 1];
+    if (sorted_path) {
+        // packed keys (sigma desc, index asc when sorted descending); padding 0 sorts last
+        int P = 64;
+        while (P < NB) P <<= 1;
+#pragma unroll
+        for (int k = 0; k < QPL; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * (64 * k + lane) + e;
+                if (j < P) keys[j] = j < NB ? pack_key(x[k][e], j) : 0;
+            }
+        // bitonic sort of keys[0 .. P) by this wavefront: LDS operations of one
+        // wavefront complete in order, so each stage sees the previous one's writes
+        for (int size = 2; size <= P; size <<= 1)
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                __builtin_amdgcn_wave_barrier();
+                for (int i = lane; i < P / 2; i += 64) {
+                    const int a = 2 * i - (i & (stride - 1)), c = a + stride;
+                    const bool desc = (a & size) == 0;
+                    const uint64_t ka = keys[a], kc = keys[c];
+                    if ((ka < kc) == desc) {
+                        keys[a] = kc;
+                        keys[c] = ka;
+                    }
+                }
+            }
+        __builtin_amdgcn_wave_barrier();
+
+        // stopping point: the first position p >= 1 with (K - p) sigma_p < total - sum of
+        // the first p, else K; R = total - sum of the first t; cut = the key at t - 1
+        uint64_t before = 0;   // sum of sigma over the positions before the current chunk
+        bool found = false;
+        for (int c0 = 0; c0 < K && !found; c0 += 64) {
+            const int p = c0 + lane;
+            const uint64_t sg = p < K ? (keys[p] >> kKeyIdxBits) + 1 : 0;
+            const uint64_t incl = before + wave_incl_scan<uint64_t>(sg, lane);
+            const bool fail = p >= 1 && p < K && (uint64_t)(K - p) * sg < total - (incl - sg);
+            const uint64_t fb = __ballot(fail);
+            if (fb) {
+                const int tt = __builtin_ctzll(fb);   // >= 1 in the first chunk
+                t = c0 + tt;
+                pre_t = tt > 0 ? __shfl(incl, tt - 1, 64) : before;
+                found = true;
+            } else {
+                before = __shfl(incl, 63, 64);
+            }
+        }
+        if (!found) pre_t = before;
+        cut = keys[t - 1];
+    }
+    const uint64_t R = total - pre_t;
     const uint64_t Kt = (uint64_t)(K - t);
     const double inv_r = R > 0 ? 1.0 / (double)R : 0.0;
 

@@ -103,8 +103,13 @@ def test_sampling_bit_exact_on_varied_rows(aba, NB, K, peak):
     sd = s.to(device())
     g = aba.sample(p, sd, 99)
     torch.cuda.synchronize()
-    o_idx, o_cnt, o_w, _ = oracle.sample(s.numpy(), K, 99)
+    o_idx, o_cnt, o_w, theta = oracle.sample(s.numpy(), K, 99)
     assert compare_lists(*g, o_idx, o_cnt, o_w) == 0
+    if 1 < K < NB and NB != 8:
+        # both ways of finding the stopping point t (the first t blocks capped) run:
+        # rows where only the top block is forced and rows with a longer capped top
+        t = (theta == 2**32).sum(axis=-1)
+        assert (t == 1).any() and (t > 1).any()
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
