@@ -203,6 +203,7 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
     __shared__ uint32_t lmax_s[NT];   // largest sigma - 1 of each thread's blocks
     __shared__ uint32_t lo_s;
     __shared__ int cand_n;
+    __shared__ uint64_t top2_s[2][W];   // each wavefront's two largest packed keys
 
     const int row = blockIdx.x;
     const int qb = row % NBq, h = (row / NBq) % H, b = row / (NBq * H);
@@ -367,9 +368,9 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
     auto gather_top = [&](int T, int PT) __attribute__((always_inline)) {
         if (T <= kFastTop) {
             const uint32_t lo = threads_bound(T);
-            #pragma unroll
-for (int k = 0; k < STEPS; ++k) {
-    if (k >= steps) break;
+#pragma unroll
+            for (int k = 0; k < STEPS; ++k) {
+                if (k >= steps) break;
                 const int q = quad(k);
                 const uint4 xv = xr[k];
                 const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -407,9 +408,9 @@ for (int k = 0; k < STEPS; ++k) {
         {
             // shortcut: fewer than T blocks above the minimum (rows whose scores mostly underflow)
             int above = 0;
-            #pragma unroll
-for (int k = 0; k < STEPS; ++k) {
-    if (k >= steps) break;
+#pragma unroll
+            for (int k = 0; k < STEPS; ++k) {
+                if (k >= steps) break;
                 const int q = quad(k);
                 if (q >= NB4) continue;
                 const uint4 xv = xr[k];
@@ -444,9 +445,9 @@ for (int k = 0; k < STEPS; ++k) {
                     hist[wave][lane + 128] = 0;
                     hist[wave][lane + 192] = 0;
                     __syncthreads();
-                    #pragma unroll
-for (int k = 0; k < STEPS; ++k) {
-    if (k >= steps) break;
+#pragma unroll
+                    for (int k = 0; k < STEPS; ++k) {
+                        if (k >= steps) break;
                         const int q = quad(k);
                         const uint4 xv = xr[k];
                         const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -514,9 +515,9 @@ for (int k = 0; k < STEPS; ++k) {
             }
             jcut = jh;
         }
-        #pragma unroll
-for (int k = 0; k < STEPS; ++k) {
-    if (k >= steps) break;
+#pragma unroll
+        for (int k = 0; k < STEPS; ++k) {
+            if (k >= steps) break;
             const int q = quad(k);
             const uint4 xv = xr[k];
             const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -537,8 +538,59 @@ for (int k = 0; k < STEPS; ++k) {
         __syncthreads();
     };
 
+    // The stopping point is 1 (only the top block forced) exactly when K = 1 or
+    // (K - 1) sigma_(2) < total - sigma_(1): the two largest keys of the row
+    // decide it, and the top is gathered only otherwise.
     int t = 0;
-    {   // fast path: the top min(K, 64), sorted and scanned by wavefront 0
+    bool two_key = false;
+    uint64_t R1 = 0, cut1 = 0;
+    {
+        uint64_t k1 = 0, k2 = 0;   // this thread's largest and second largest keys
+#pragma unroll
+        for (int k = 0; k < STEPS; ++k) {
+            if (k >= steps) break;
+            const int q = quad(k);
+            if (q >= NB4) continue;
+            const uint32_t xs[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * q + e;
+                if (j >= NB) continue;
+                const uint64_t kk = pack_key(xs[e], j);
+                if (kk > k1) {
+                    k2 = k1;
+                    k1 = kk;
+                } else if (kk > k2) {
+                    k2 = kk;
+                }
+            }
+        }
+        const uint64_t w1 = wave_max_u64(k1);
+        const uint64_t w2 = wave_max_u64(k1 == w1 ? k2 : k1);
+        if (lane == 0) {
+            top2_s[0][wave] = w1;
+            top2_s[1][wave] = w2;
+        }
+        __syncthreads();
+        uint64_t m1 = 0, m2 = 0;   // keys are distinct, so the second is the largest one below the first
+#pragma unroll
+        for (int i = 0; i < W; ++i) m1 = top2_s[0][i] > m1 ? top2_s[0][i] : m1;
+#pragma unroll
+        for (int i = 0; i < W; ++i)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const uint64_t c = top2_s[r][i];
+                if (c < m1 && c > m2) m2 = c;
+            }
+        const uint64_t s1 = (m1 >> kKeyIdxBits) + 1, s2 = (m2 >> kKeyIdxBits) + 1;   // NB >= 2 here
+        if (K == 1 || (uint64_t)(K - 1) * s2 < total - s1) {
+            t = 1;
+            two_key = true;
+            R1 = total - s1;
+            cut1 = m1;
+        }
+    }
+    if (t == 0) {   // fast path: the top min(K, 64), sorted and scanned by wavefront 0
         const int T = min(K, kFastTop);
         gather_top(T, kFastTop);
         if (wave == 0) {
@@ -625,7 +677,7 @@ for (int k = 0; k < STEPS; ++k) {
         }
         __syncthreads();
     }
-    const uint64_t R = r_s, cut = cut_s;
+    const uint64_t R = two_key ? R1 : r_s, cut = two_key ? cut1 : cut_s;
     const uint64_t Kt = (uint64_t)(K - t);   // >= 0 since t <= K
 
     // 4. keep decisions (4 bits per quad step), then the compaction in index order

@@ -94,8 +94,13 @@ def test_fine_sampling_bit_exact_on_long_rows(aba, NB, K, peak):
         s[0, 0, 3, ::97] = 1.0                   # a few blocks that all cap
     g = aba.sample(p, s.to(device()), 1234)
     torch.cuda.synchronize()
-    o_idx, o_cnt, o_w, _ = oracle.sample(s.numpy(), K, 1234)
+    o_idx, o_cnt, o_w, theta = oracle.sample(s.numpy(), K, 1234)
     assert compare_lists(*g, o_idx, o_cnt, o_w) == 0
+    if 1 < K < NB:
+        # rows where only the top block is forced (the two-key test) and rows with
+        # a longer capped top (the gathered, sorted top) both occur
+        t = (theta == 2**32).sum(axis=-1)
+        assert (t == 1).any() and (t > 1).any()
     print(f"[long rows NB={NB} K={K}] {NBq} rows bit-exact; mean kept {o_cnt.mean():.1f}")
 
 
