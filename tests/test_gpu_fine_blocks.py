@@ -267,12 +267,13 @@ def test_single_layer_fine_attention_sampled(aba, single_fine):
     assert err <= att_tol(w), f"max abs err {err:.3g}"
 
 
-@pytest.mark.parametrize("key_block,n_tokens,heads", [(4, 4096, 2), (4, 4097, 2), (4, 4100, 2), (128, 131072, 1),
-                                                      (128, 130945, 1)])
+@pytest.mark.parametrize("key_block,n_tokens,heads", [(4, 2048, 2), (4, 2049, 2), (4, 2052, 2), (128, 65536, 1),
+                                                      (128, 65409, 1), (128, 65664, 1), (128, 131072, 1)])
 def test_scores_at_the_one_pass_limit(aba, key_block, n_tokens, heads):
-    """Rows of exactly 1024 key blocks take the one-pass scorer with its largest LDS
-    rows; 1025 or more take the two-pass scorer; both against the oracle, re-scored
-    from the GPU's own centroids, weights and pooled keys."""
+    """Rows of exactly 512 key blocks take the one-pass scorer with its largest LDS
+    rows; 513 or more take the two-pass scorer (up to the largest 128-token row,
+    1024 blocks); both against the oracle, re-scored from the GPU's own centroids,
+    weights and pooled keys."""
     g = torch.Generator().manual_seed(n_tokens + key_block)
     NB = (n_tokens + 127) // 128
     shape = (1, heads, 128 * NB, 128)
