@@ -280,23 +280,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_s_setprio(0);
 
         if (!write) {
-            // lane (l32, half) element r of tile kt: key block j0 + 32kt + 8(r/4) + 4half + r%4, slot l32
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = j0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-                    acc[kt][r] = j < NBk ? acc[kt][r] * scale_log2 : -INFINITY;
-                    mx = fmaxf(mx, acc[kt][r]);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            float sum = 0.f;
-            if (mx > -INFINITY) {
+            // lane (l32, half) element r of tile kt: key block j0 + 32kt + 8(r/4) + 4half + r%4, slot l32.
+            // The maximum is taken on the raw products (the scale is positive and rounding
+            // monotone, so scaling it gives the maximum of the scaled logits) and each
+            // term is 2^(x s - M) in one fma, as in the write pass; blocks past NBk only
+            // occur in the last chunk's wavefronts.
+            float mraw = -INFINITY;
+            if (j0 + 63 < NBk) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(acc[kt][r] - mx);
+                    for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, acc[kt][r]);
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = j0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+                        if (j >= NBk) acc[kt][r] = -INFINITY;
+                        mraw = fmaxf(mraw, acc[kt][r]);
+                    }
+            }
+            mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+            const float mx = mraw * scale_log2;
+            float sum = 0.f;
+            if (mraw > -INFINITY) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[kt][r], scale_log2, -mx));
             }
             sum += __shfl_xor(sum, 32, 64);
             if (half == 0) red[i & 1][wave][l32] = make_float2(mx, sum);
