@@ -122,6 +122,34 @@ def test_fine_attend_matches_oracle_on_oracle_lists(aba, w):
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_fine_attend_empty_lists_give_zeros(aba, w):
+    """4-token lists: a query block with nothing to attend (cnt 0, a negative cnt,
+    or only invalid entries) gets zeros; every other row still matches the oracle."""
+    (q, k, v), (qd, kd, vd) = inputs(w, 208)
+    p = make_fine_plan(aba, w)
+    NB, NBk = w.n_blocks, p.n_key_blocks
+    scores = synth.random_scores(w.batch, w.heads, NB, NBk, seed=10, peak=2.0)
+    idx, cnt, wt, _ = oracle.sample(scores.numpy(), p.budget, 17)
+    idx, cnt, wt = idx.copy(), cnt.copy(), wt.copy()
+    empty = [(0, 0, 0), (w.batch - 1, w.heads - 1, NB - 1), (0, w.heads - 1, NB // 2)]
+    cnt[empty[0]] = 0
+    cnt[empty[1]] = -3
+    idx[empty[2]] = NBk + 7                # every entry past the last key block
+    out = aba.attend(p, qd, kd, vd, *(torch.from_numpy(a).to(device()) for a in (idx, cnt, wt)))
+    torch.cuda.synchronize()
+    clean_cnt = cnt.copy()
+    for e in empty:
+        clean_cnt[e] = 0
+    items = oracle.layer_items(w.batch, w.heads, NB)
+    got = gpu_rows(out, items)
+    is_empty = np.array([it in empty for it in items])
+    assert np.all(got[is_empty] == 0.0)
+    ref = oracle.attend(q, k, v, w.seq_len, idx, clean_cnt, wt, items=[it for it in items if it not in empty],
+                        scale=p.softmax_scale, kblk=FINE)
+    assert np.abs(got[~is_empty] - ref).max() <= att_tol(w)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
 def test_fine_every_block_kept_is_dense(aba, w):
     """A budget of every block caps them all (weight 1): the layer is dense attention."""
     (q, k, v), (qd, kd, vd) = inputs(w, 204)
