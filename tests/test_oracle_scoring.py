@@ -76,6 +76,38 @@ def test_identical_queries_collapse_to_meanpool(oracle_mod):
     assert torch.allclose(torch.from_numpy(s), _meanpool_scores(q, k, N, scale), rtol=0, atol=1e-13)
 
 
+def test_key_block_seen_by_one_cluster_scores_its_share(oracle_mod):
+    """Two well-separated query groups, and key blocks that only one group attends
+    to: with the logits saturated, each centroid's softmax is one-hot on its own
+    block, so that block's score is the group's share of the block's queries
+    (IBCS paragraph: the weight of a centroid is its cluster's share).  Group B
+    is exactly the 8 strided seed rows (share 8/128), so a scorer that weighted
+    the centroids uniformly would give 1/8 and 7/8 instead of 120/128 and 8/128."""
+    D = 16
+    N = 3 * BLK
+    u = torch.zeros(D)
+    u[0] = 1.0
+    v = torch.zeros(D)
+    v[1] = 1.0
+    alpha, beta = 40.0, 40.0                 # s * alpha * beta = 400: every softmax saturates
+    q = torch.zeros(1, 1, N, D)
+    k = torch.zeros(1, 1, N, D)
+    q[0, 0, :] = alpha * u                   # group A everywhere ...
+    for qb in range(3):
+        q[0, 0, qb * BLK + 16 * torch.arange(8)] = alpha * v   # ... but the seed rows m * 128 / 8 are group B
+    k[0, 0, 0:BLK] = beta * u                # key block 0: attended by group A only
+    k[0, 0, BLK:2 * BLK] = beta * v          # key block 1: attended by group B only
+    # key block 2 stays zero: logit 0 for every centroid, far below the saturated ones
+    scale = 1.0 / np.sqrt(D)
+    cent, w, _ = oracle_mod.kmeans(q, N, C=8, T=10)
+    assert np.allclose(np.sort(w[0, 0], axis=-1)[..., ::-1][..., :2], [120 / 128, 8 / 128], rtol=0, atol=0)
+    s = oracle_mod.score(cent, w, oracle_mod.pool(k, N), scale)
+    for qb in range(3):
+        assert abs(s[0, 0, qb, 0] - 120 / 128) < 1e-12
+        assert abs(s[0, 0, qb, 1] - 8 / 128) < 1e-12
+        assert s[0, 0, qb, 2] < 1e-12
+
+
 def test_kmeans_invariants_and_monotone_objective(oracle_mod):
     rng = np.random.default_rng(5)
     for trial in range(6):
