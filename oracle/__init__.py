@@ -63,7 +63,7 @@ def _load():
     lib.oracle_philox4x32_10.restype = None
     lib.oracle_draw.argtypes = [u64, i32, i32, i32, i32]
     lib.oracle_draw.restype = ctypes.c_uint32
-    lib.oracle_sample.argtypes = [P, i32, i32, i32, i32, i32, u64, i32, P, P, P, P]
+    lib.oracle_sample.argtypes = [P, i32, i32, i32, i32, i32, u64, i32, i32, i32, P, P, P, P]
     lib.oracle_sample.restype = None
     lib.oracle_attend.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, f64, P, P, P, i32, P, i32, P, P, P, P]
     lib.oracle_attend.restype = None
@@ -188,8 +188,10 @@ def draw(seed: int, b: int, h: int, qb: int, j: int) -> int:
     return int(_load().oracle_draw(seed, b, h, qb, j))
 
 
-def sample(scores, K: int, seed: int, cap: int | None = None):
-    """SIP sampling plan (SIP paragraph): idx/w [B,H,NBq,cap], cnt [B,H,NBq], theta [B,H,NBq,NBk]."""
+def sample(scores, K: int, seed: int, cap: int | None = None, head_offset: int = 0, batch_offset: int = 0):
+    """SIP sampling plan (SIP paragraph): idx/w [B,H,NBq,cap], cnt [B,H,NBq], theta [B,H,NBq,NBk].
+    The scores may be heads head_offset.. and batch entries batch_offset.. of a larger
+    layer; draws are addressed by those global indices."""
     s = np.ascontiguousarray(np.asarray(scores, np.float32))
     B, H, NBq, NBk = s.shape
     cap = NBk if cap is None else cap
@@ -197,7 +199,8 @@ def sample(scores, K: int, seed: int, cap: int | None = None):
     cnt = np.zeros((B, H, NBq), np.int32)
     w = np.zeros((B, H, NBq, cap), np.float32)
     theta = np.zeros((B, H, NBq, NBk), np.uint64)
-    _load().oracle_sample(_ptr(s), B, H, NBq, NBk, K, seed, cap, _ptr(idx), _ptr(cnt), _ptr(w), _ptr(theta))
+    _load().oracle_sample(_ptr(s), B, H, NBq, NBk, K, seed, cap, head_offset, batch_offset, _ptr(idx), _ptr(cnt),
+                          _ptr(w), _ptr(theta))
     return idx, cnt, w, theta
 
 

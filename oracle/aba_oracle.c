@@ -370,8 +370,11 @@ uint32_t oracle_draw(uint64_t seed, int b, int h, int qb, int j)
 /* (SIP paragraph: a block with probability 25% counts as four).            */
 /* scores [B,H,NBq,NBk] fp32; idx/w [B,H,NBq,cap]; cnt [B,H,NBq].           */
 /* theta_out (nullable) [B,H,NBq,NBk].                                      */
-void oracle_sample(const float *scores, int B, int H, int NBq, int NBk, int K, uint64_t seed, int cap,
-                   int32_t *idx, int32_t *cnt, float *w, uint64_t *theta_out)
+/* READING: the scores may be a slice of a larger layer, heads h0 .. h0+H-1  */
+/* of batch entries b0 .. b0+B-1; the draws are addressed by those global    */
+/* indices, so a slice draws exactly what the whole layer draws for it.     */
+void oracle_sample(const float *scores, int B, int H, int NBq, int NBk, int K, uint64_t seed, int cap, int h0,
+                   int b0, int32_t *idx, int32_t *cnt, float *w, uint64_t *theta_out)
 {
     long total = (long)B * H * NBq;
 #pragma omp parallel for schedule(dynamic)
@@ -383,7 +386,7 @@ void oracle_sample(const float *scores, int B, int H, int NBq, int NBk, int K, u
         oracle_thresholds(scores + it * (long)NBk, NBk, K, theta);
         int n = 0;
         for (int j = 0; j < NBk; ++j) {
-            uint32_t r = oracle_draw(seed, b, h, qb, j);
+            uint32_t r = oracle_draw(seed, b0 + b, h0 + h, qb, j);
             if ((uint64_t)r < theta[j]) {
                 if (n < cap) {
                     idx[it * (long)cap + n] = j;
