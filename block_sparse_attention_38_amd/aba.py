@@ -73,7 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     PP = ctypes.POINTER(PlanStruct)
     lib.aba_plan.argtypes = [PP, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32]
     lib.aba_score.argtypes = [PP, P, P, P, P, P, P, P, P]
-    lib.aba_sample.argtypes = [PP, P, u64, P, P, P, P]
+    lib.aba_sample.argtypes = [PP, P, u64, i32, i32, P, P, P, P]
     lib.aba_attend.argtypes = [PP, P, P, P, P, P, P, P, P, P]
     lib.aba_attend_full.argtypes = [PP, P, P, P, P, P, P]
     lib.aba_block_mass.argtypes = [PP, P, P, P, ctypes.c_int32, P, P]
@@ -177,8 +177,10 @@ def score(p: Plan, q: torch.Tensor, k: torch.Tensor, *, return_parts: bool = Fal
     return (out, cent, wgt, kbar) if return_parts else out
 
 
-def sample(p: Plan, scores: torch.Tensor, seed: int, *, out=None):
-    """aba_sample: (idx [B,H,NB,cap] int32, cnt [B,H,NB] int32, w [B,H,NB,cap] float32)."""
+def sample(p: Plan, scores: torch.Tensor, seed: int, *, out=None, head_offset: int = 0, batch_offset: int = 0):
+    """aba_sample: (idx [B,H,NB,cap] int32, cnt [B,H,NB] int32, w [B,H,NB,cap] float32).
+    head_offset / batch_offset: global indices of this call's head 0 and batch entry 0
+    when it covers a slice of a larger layer (the draws are addressed by them)."""
     dev = scores.device
     B, H, NB, cap = p.batch, p.heads, p.n_blocks, p.list_cap
     _need(scores, "scores", (B, H, NB, p.n_key_blocks), torch.float32, dev)
@@ -190,8 +192,8 @@ def sample(p: Plan, scores: torch.Tensor, seed: int, *, out=None):
     _need(idx, "idx", (B, H, NB, cap), torch.int32, dev)
     _need(cnt, "cnt", (B, H, NB), torch.int32, dev)
     _need(w, "w", (B, H, NB, cap), torch.float32, dev)
-    _check(load_library().aba_sample(ctypes.byref(p.raw), _ptr(scores), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(idx),
-                                     _ptr(cnt), _ptr(w), _stream()))
+    _check(load_library().aba_sample(ctypes.byref(p.raw), _ptr(scores), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                     int(head_offset), int(batch_offset), _ptr(idx), _ptr(cnt), _ptr(w), _stream()))
     return idx, cnt, w
 
 

@@ -25,8 +25,9 @@ hipError_t launch_kmeans(const void *q, const void *k, int dtype, int B, int H, 
                          int T, int kb, int NBk, float *cent, float *weight, float *kbar, bool *pooled, hipStream_t s);
 hipError_t launch_pool(const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB, float *kbar,
                        hipStream_t s);
-hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int cap,
-                         int32_t *idx, int32_t *cnt, float *w, hipStream_t s);
+// Draws use the global indices h0 + h and b0 + b (the call may cover a slice of a layer).
+hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int h0, int b0,
+                         int cap, int32_t *idx, int32_t *cnt, float *w, hipStream_t s);
 // Dynamic LDS the sampler needs for rows of NB key blocks and budget K.
 size_t sample_lds_bytes(int NB, int K);
 // 4-token key pooling, and the two-pass MFMA scoring of either key block size

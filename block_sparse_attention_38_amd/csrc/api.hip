@@ -2,6 +2,7 @@
 // validation, workspace layout and kernel launches.  Host code only; every
 // computation runs in the kernels of kmeans.hip, pool_score.hip, sample.hip and
 // attend.hip.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -183,15 +184,19 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
                       "score launch");
 }
 
-aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, int32_t *idx, int32_t *cnt, float *w,
-                      hipStream_t stream)
+aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, int32_t head_offset,
+                      int32_t batch_offset, int32_t *idx, int32_t *cnt, float *w, hipStream_t stream)
 {
     g_last_error.clear();
     aba_status st = check_plan(p);
     if (st != ABA_OK) return st;
     if (!scores || !idx || !cnt || !w) return fail(ABA_E_INVALID, "scores, idx, cnt and w must be non-NULL");
+    if (head_offset < 0 || batch_offset < 0 || (int64_t)head_offset + p->heads > INT32_MAX ||
+        (int64_t)batch_offset + p->batch > INT32_MAX)
+        return fail(ABA_E_INVALID, "head_offset (%d) and batch_offset (%d) must be >= 0 and keep the global indices "
+                    "below 2^31", head_offset, batch_offset);
     return hip_status(aba::launch_sample(scores, p->batch, p->heads, p->n_blocks, p->n_key_blocks, p->budget, seed,
-                                         p->list_cap, idx, cnt, w, stream),
+                                         head_offset, batch_offset, p->list_cap, idx, cnt, w, stream),
                       "sample launch");
 }
 

@@ -12,7 +12,9 @@
 //   sigma_j = clamp(floor(S_j * 2^32), 1, 2^32)     (uint64, exact)
 //   water-filling over the order (sigma desc, j asc); thresholds by exact
 //   128-bit comparisons; draws from Philox4x32-10 addressed by (seed, b, h,
-//   qb, j); kept blocks compacted in ascending order.
+//   qb, j), with b and h the global batch and head indices (a call may cover
+//   a slice of heads of a larger layer); kept blocks compacted in ascending
+//   order.
 #include "aba_internal.h"
 
 #include <array>
@@ -181,7 +183,7 @@ template <typename T> __device__ __forceinline__ T wave_incl_scan(T x, int lane)
 
 template <int W, int STEPS>   // wavefronts per workgroup, quad steps per thread: rows of up to 256 W STEPS blocks
 __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__restrict__ scores, int H, int NBq, int NB,
-                                                          int K, uint64_t seed, int cap, int P,
+                                                          int K, uint64_t seed, uint32_t h0, uint32_t b0, int cap, int P,
                                                           int32_t *__restrict__ idx, int32_t *__restrict__ cnt,
                                                           float *__restrict__ w)
 {
@@ -688,7 +690,7 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
     for (int k = 0; k < STEPS; ++k) {
         const int q = quad(k);
         if (k < steps && q < NB4) {
-            const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)qb, (uint32_t)h, (uint32_t)b), k0, k1);
+            const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)qb, h0 + (uint32_t)h, b0 + (uint32_t)b), k0, k1);
             const uint32_t draw[4] = {r.x, r.y, r.z, r.w};
             const uint32_t xs[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
             uint32_t nib = 0;
@@ -774,7 +776,8 @@ constexpr int kWaveRowMax = 256;   // longer rows: a whole-row sort per wavefron
 
 template <int QPL>   // quads per lane: rows of up to 256 QPL blocks
 __global__ __launch_bounds__(256) void sample_wave_kernel(const float *__restrict__ scores, int H, int NBq, int NB,
-                                                          int K, uint64_t seed, int cap, int rows,
+                                                          int K, uint64_t seed, uint32_t h0, uint32_t b0, int cap,
+                                                          int rows,
                                                           int32_t *__restrict__ idx, int32_t *__restrict__ cnt,
                                                           float *__restrict__ w)
 {
@@ -919,7 +922,7 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(const float *__restric
         const int q = 64 * k + lane;
         uint32_t nib = 0;
         if (q < NB4) {
-            const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)qb, (uint32_t)h, (uint32_t)b), k0, k1);
+            const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)qb, h0 + (uint32_t)h, b0 + (uint32_t)b), k0, k1);
             const uint32_t draw[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -962,15 +965,16 @@ size_t sample_lds_bytes(int NB, int K)
     return 8 * (size_t)topk_pad(NB, K);
 }
 
-hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int cap,
-                         int32_t *idx, int32_t *cnt, float *w, hipStream_t s)
+hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int h0, int b0,
+                         int cap, int32_t *idx, int32_t *cnt, float *w, hipStream_t s)
 {
     const long rows = (long)B * H * NBq;
     const dim3 grid((unsigned)rows), block(256);
     if (NB > kMaxFineBlocks) return hipErrorInvalidValue;
     if (NB <= kWaveRowMax) {   // one wavefront per row
         const dim3 wgrid((unsigned)((rows + 3) / 4));
-        sample_wave_kernel<1><<<wgrid, block, 0, s>>>(scores, H, NBq, NB, K, seed, cap, (int)rows, idx, cnt, w);
+        sample_wave_kernel<1><<<wgrid, block, 0, s>>>(scores, H, NBq, NB, K, seed, (uint32_t)h0, (uint32_t)b0, cap,
+                                                       (int)rows, idx, cnt, w);
         return hipGetLastError();
     }
     const size_t lds = sample_lds_bytes(NB, K);
@@ -983,7 +987,8 @@ hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        kernel<<<grid, dim3(threads), lds, s>>>(scores, H, NBq, NB, K, seed, cap, P, idx, cnt, w);
+        kernel<<<grid, dim3(threads), lds, s>>>(scores, H, NBq, NB, K, seed, (uint32_t)h0, (uint32_t)b0, cap, P, idx,
+                                                cnt, w);
         return hipGetLastError();
     };
     if (NB <= 256 * 4 * 1) return launch(&sample_topk_kernel<4, 1>, 256);

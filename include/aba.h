@@ -138,18 +138,25 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
  *   capped: theta = 2^32; other blocks theta = clamp(ceil((K-t) sigma 2^32 / R),
  *   1, 2^32) (1 when K - t <= 0), so P(kept) = theta / 2^32 sums to K;
  *   the draw for key block j is word (j & 3) of Philox4x32-10 (Salmon et al.,
- *   SC'11) with key (seed_lo, seed_hi) and counter (j >> 2, query block, h, b);
+ *   SC'11) with key (seed_lo, seed_hi) and counter (j >> 2, query block,
+ *   head_offset + h, batch_offset + b);
  *   block j is kept iff draw < theta_j, with weight w = float(2^32 / theta_j)
  *   (an fp64 division), the Horvitz-Thompson factor 1/pi.
- *   scores : float32 [B,H,NB,NBk]
+ *   scores       : float32 [B,H,NB,NBk]
+ *   head_offset  : global index of head 0 of this call (>= 0): a call over
+ *                  heads h0 .. h0+H-1 of a larger layer passes h0
+ *   batch_offset : global index of batch entry 0 of this call (>= 0)
  *   idx    : out, int32 [B,H,NB,list_cap], kept key blocks in ascending order
  *   cnt    : out, int32 [B,H,NB], number kept (>= 1)
  *   w      : out, float32 [B,H,NB,list_cap], weights of the listed blocks
  * Entries at or past cnt are left unspecified.  The lists depend only on
- * (scores, budget, seed): every draw is addressable by (seed, b, h, query
- * block, key block), whatever the launch shape. */
-aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, int32_t *idx, int32_t *cnt,
-                      float *w, hipStream_t stream);
+ * (scores, budget, seed) and the global (batch, head) indices: every draw is
+ * addressable by (seed, b, h, query block, key block), so a call over a slice
+ * of heads draws exactly what a call over the whole layer draws for them.
+ * Offsets with head_offset + H or batch_offset + B above 2^31 - 1 ->
+ * ABA_E_INVALID. */
+aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, int32_t head_offset,
+                      int32_t batch_offset, int32_t *idx, int32_t *cnt, float *w, hipStream_t stream);
 
 /* Block-sparse attention over a sampling plan (SIP and kernel paragraphs).  For
  * each valid query i of query block b, with the kept list (j, w_j) of key

@@ -103,11 +103,22 @@ def test_entry_points_reject_null_pointers_before_launch(aba):
     pp = ctypes.byref(p.raw)
     nul = None
     assert lib.aba_score(pp, nul, nul, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
-    assert lib.aba_sample(pp, nul, 1, nul, nul, nul, nul) == aba.ABA_E_INVALID
+    assert lib.aba_sample(pp, nul, 1, 0, 0, nul, nul, nul, nul) == aba.ABA_E_INVALID
     assert lib.aba_attend(pp, nul, nul, nul, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
     assert lib.aba_attend_full(pp, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
     assert b"NULL" in lib.aba_last_error()
     assert lib.aba_attend_full(None, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
+
+
+@pytest.mark.parametrize("h0,b0", [(-1, 0), (0, -1), (2**31 - 2, 0), (0, 2**31 - 1)])
+def test_sample_rejects_offsets_outside_the_counter_range(aba, h0, b0):
+    """The draws are addressed by the global (batch, head) indices b0 + b and h0 + h;
+    offsets that are negative or push them past 2^31 - 1 are refused before launch."""
+    lib = aba.load_library()
+    p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 2)
+    fake = ctypes.c_void_p(1)
+    assert lib.aba_sample(ctypes.byref(p.raw), fake, 1, h0, b0, fake, fake, fake, None) == aba.ABA_E_INVALID
+    assert b"offset" in lib.aba_last_error()
 
 
 def test_block_mass_checks_dtype_and_pointers(aba):
