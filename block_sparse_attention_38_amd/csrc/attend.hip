@@ -372,6 +372,16 @@ template <bool full> __device__ __forceinline__ Entry window_entry(const Window 
 
 __device__ __forceinline__ float max2(float a, float b) { return __builtin_fmaxf(a, b); }
 
+// l += p[e - 1] + p[e] for the bf16 probabilities of one pair (e odd): one
+// v_dot2 against (1, 1), so the softmax normaliser sums exactly the rounded
+// values the PV product multiplies.
+__device__ __forceinline__ void row_sum_pair(const bf16x8 &p, int e, float &l)
+{
+    const bf16x2 pair = {p[e - 1], p[e]};
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l, false);
+}
+
 // Maximum of x over the lane pair (l, l ^ 32), in every lane.
 __device__ __forceinline__ float half_pair_max(float x)
 {
@@ -531,15 +541,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
-        // P^T in bf16 straight from the accumulators; the row sum adds the fp32
-        // probabilities with plain adds (two chains), which overlap the MFMAs
-        // (v_dot2 would run on the matrix pipe and serialise with them)
+        // P^T in bf16 straight from the accumulators; the row sum adds the same
+        // bf16-rounded probabilities the PV product uses (numerator and
+        // normaliser agree), a pair per dot2 in two chains
         const float bias = lw - m_run;
         bf16x8 pb[KT][2];
         auto prob = [&](int kt, int r) __attribute__((always_inline)) {
             const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, bias));
-            if (r & 1) l_run1 += pr; else l_run0 += pr;
             pb[kt][r >> 3][r & 7] = (__bf16)pr;
+            if (r & 1) row_sum_pair(pb[kt][r >> 3], r & 7, (r & 2) ? l_run1 : l_run0);
         };
 #pragma unroll
         for (int r = 0; r < 16; ++r) prob(0, r);
@@ -894,8 +904,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         bf16x8 pb[KT][2];
         auto prob = [&](int kt, int r) __attribute__((always_inline)) {
             const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][r], scale_log2, bias[kt][r >> 2]));
-            if (r & 1) l_run1 += pr; else l_run0 += pr;
             pb[kt][r >> 3][r & 7] = (__bf16)pr;
+            if (r & 1) row_sum_pair(pb[kt][r >> 3], r & 7, (r & 2) ? l_run1 : l_run0);
         };
 #pragma unroll
         for (int r = 0; r < 16; ++r) prob(0, r);

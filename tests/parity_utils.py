@@ -13,6 +13,11 @@ from block_sparse_attention_38_amd.workloads import CLUSTERS, KMEANS_ITERS, Work
 SCORE_RTOL = 1e-4          # scores, relative per element
 ATT_ATOL_BF16 = 2e-2       # attention outputs, bf16 inputs, fp32 accumulation
 ATT_ATOL_F32 = 1e-4        # attention outputs, fp32 inputs
+# ... and the same bar relative to the output scale: the largest |reference|
+# output over the compared rows.  With nearly flat attention the outputs are
+# O(1e-2), where the absolute bar alone would pass an all-zero output.
+ATT_RTOL_BF16 = 2e-2
+ATT_RTOL_F32 = 1e-4
 CENT_RTOL = 1e-5           # centroids, relative to the block's largest |centroid|
 POOL_RTOL = 1e-5           # pooled keys, relative to the layer's largest |kbar|
 NEAR_TIE = 1e-4            # k-means blocks whose two best distances are closer are not compared
@@ -42,6 +47,91 @@ def make_fine_plan(aba, w: Workload, density: float | None = None, budget: int |
 
 def att_tol(w: Workload) -> float:
     return ATT_ATOL_BF16 if w.dtype == "bf16" else ATT_ATOL_F32
+
+
+def check_attention(got, ref, dtype: str, what: str = "") -> float:
+    """Attention outputs against the oracle over the compared rows: every value
+    finite, max |got - ref| within the absolute bar and within the same factor
+    of the largest |ref| (the output scale).  Returns the max abs error."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} against {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    atol, rtol = (ATT_ATOL_BF16, ATT_RTOL_BF16) if dtype == "bf16" else (ATT_ATOL_F32, ATT_RTOL_F32)
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    print(f"[{what}] max abs err {err:.3g}, output scale {scale:.3g} (err/scale {err / max(scale, 1e-300):.3g})")
+    assert err <= atol, f"{what}: max abs err {err:.3g} > {atol:g}"
+    assert err <= rtol * scale, f"{what}: max abs err {err:.3g} > {rtol:g} x output scale {scale:.3g}"
+    return err
+
+
+# The peaked variant: the softmax scale 1 instead of 1/sqrt(D), i.e. logits
+# x sqrt(D) on the same inputs.  A row's logits then span ~100 log2 units, so
+# outputs are O(1) and the running maximum keeps moving across sub-tiles.
+PEAKED_SCALE = 1.0
+
+
+def peaked_lists(B, H, NBq, NBk, per_row: int, seed: int, lo=(0.0, 4.0), hi=(16.0, 20.0)):
+    """Random ascending lists of per_row distinct key blocks per query block, the
+    first half weighted 2^U(lo), the second half 2^U(hi) (weights >= 2^16), so
+    that the shifted logits jump upward part-way through every list."""
+    rng = np.random.default_rng(seed)
+    idx = np.zeros((B, H, NBq, NBk), np.int32)
+    cnt = np.zeros((B, H, NBq), np.int32)
+    wt = np.zeros((B, H, NBq, NBk), np.float32)
+    c = min(per_row, NBk)
+    for r in np.ndindex(B, H, NBq):
+        sel = np.sort(rng.choice(NBk, size=c, replace=False))
+        e = np.arange(c)
+        lw = np.where(e < c // 2, rng.uniform(*lo, size=c), rng.uniform(*hi, size=c))
+        idx[r][:c] = sel
+        wt[r][:c] = np.exp2(lw).astype(np.float32)
+        cnt[r] = c
+    return idx, cnt, wt
+
+
+def rescales_after_first_subtile(q, k, n_valid: int, items, idx, cnt, wt, scale: float, kblk: int,
+                                 slack: float = 8.0) -> int:
+    """How often the kernels' lazy rescale runs after the first sub-tile of a list,
+    emulated on the inputs (test-side arithmetic, fp64): each wavefront holds 32
+    query rows (rows past N have q = 0) and a running maximum per row; a sub-tile
+    of 64 keys (half a 128-token block, or 16 entries of 4-token blocks) has the
+    maximum m_t = log2 e * s * max q.k + (the largest log2 w of the sub-tile),
+    and the wavefront rescales when some row has m_t > m_run + slack, every row
+    then taking max(m_run, m_t).  Returns the number of (wavefront, sub-tile
+    u >= 1) rescales over the listed query blocks."""
+    log2e = 1.4426950408889634
+    q, k = (x.float().numpy() if isinstance(x, torch.Tensor) else np.asarray(x) for x in (q, k))
+    total = 0
+    for b, h, qb in items:
+        nq = max(0, min(128, n_valid - 128 * qb))
+        qx = np.zeros((128, q.shape[-1]))
+        qx[:nq] = np.asarray(q[b, h, 128 * qb:128 * qb + nq], np.float64)
+        c = int(cnt[b, h, qb])
+        ents = [(int(idx[b, h, qb, e]), float(wt[b, h, qb, e])) for e in range(c)]
+        subs = []                                   # (keys of the sub-tile, its largest log2 w)
+        if kblk == 128:
+            for j, x in ents:
+                for half in (0, 1):
+                    lo_k, hi_k = 128 * j + 64 * half, min(128 * j + 64 * half + 64, n_valid)
+                    if lo_k < hi_k:
+                        subs.append((np.arange(lo_k, hi_k), np.log2(x)))
+        else:
+            for s0 in range(0, c, 16):
+                chunk = ents[s0:s0 + 16]
+                keys = np.concatenate([np.arange(4 * j, min(4 * j + 4, n_valid)) for j, _ in chunk])
+                subs.append((keys, max(np.log2(x) for _, x in chunk)))
+        m = np.full(128, -np.inf)
+        for u, (keys, lwm) in enumerate(subs):
+            kx = np.asarray(k[b, h, keys], np.float64)
+            mt = log2e * scale * (qx @ kx.T).max(axis=1) + lwm
+            for wv in range(4):
+                rows = slice(32 * wv, 32 * wv + 32)
+                if np.any(mt[rows] > m[rows] + slack):
+                    total += int(u > 0)
+                    m[rows] = np.maximum(m[rows], mt[rows])
+    return total
 
 
 def gpu_rows(out: torch.Tensor, items, blk: int = 128) -> np.ndarray:
