@@ -11,6 +11,7 @@ Steps (AB-Attention page, section "Три приёма AB-Attention"):
     sample(plan, scores, seed)     SIP sampling plan (idx, cnt, w) -> aba_sample
     attend(plan, q, k, v, ...)     HT-weighted block-sparse attn   -> aba_attend
     attend_full(plan, q, k, v)     dense attention                 -> aba_attend_full
+    attend_noalloc(plan, ...)      aba_attend without a workspace  -> aba_attend_noalloc
     block_mass(plan, q, k, items)  attention mass per key block    -> aba_block_mass (diagnostic)
 """
 from __future__ import annotations
@@ -54,8 +55,10 @@ class PlanStruct(ctypes.Structure):
     ]
 
 
-EXPORTS = ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full", "aba_block_mass", "aba_last_error",
-           "aba_version")
+EXPORTS = ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full", "aba_attend_noalloc",
+           "aba_block_mass", "aba_last_error", "aba_version")
+# Query blocks (B * H * NB) the static scratch of aba_attend_noalloc holds.
+NOALLOC_MAX_QUERY_BLOCKS = (1 << 20) // 4
 
 _lib = None
 
@@ -76,8 +79,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.aba_sample.argtypes = [PP, P, u64, i32, i32, P, P, P, P]
     lib.aba_attend.argtypes = [PP, P, P, P, P, P, P, P, P, P]
     lib.aba_attend_full.argtypes = [PP, P, P, P, P, P, P]
+    lib.aba_attend_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P]
     lib.aba_block_mass.argtypes = [PP, P, P, P, ctypes.c_int32, P, P]
-    for name in ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full", "aba_block_mass"):
+    for name in ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full", "aba_attend_noalloc",
+                 "aba_block_mass"):
         getattr(lib, name).restype = ctypes.c_int
     lib.aba_last_error.argtypes = []
     lib.aba_last_error.restype = ctypes.c_char_p
@@ -213,6 +218,22 @@ def attend(p: Plan, q, k, v, idx, cnt, w, *, out=None, ws=None) -> torch.Tensor:
     ws = _ws(p, ws, dev)
     _check(load_library().aba_attend(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(cnt), _ptr(w),
                                      _ptr(out), _ptr(ws), _stream()))
+    return out
+
+
+def attend_noalloc(p: Plan, q, k, v, idx, cnt, w, *, out: torch.Tensor) -> torch.Tensor:
+    """aba_attend_noalloc: aba_attend with the library's static scratch instead of a
+    workspace; the caller passes the output, and nothing is allocated."""
+    dev = q.device
+    shp = _qkv_shape(p)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, shp, p.torch_dtype, dev)
+    B, H, NB, cap = p.batch, p.heads, p.n_blocks, p.list_cap
+    _need(idx, "idx", (B, H, NB, cap), torch.int32, dev)
+    _need(cnt, "cnt", (B, H, NB), torch.int32, dev)
+    _need(w, "w", (B, H, NB, cap), torch.float32, dev)
+    _check(load_library().aba_attend_noalloc(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(cnt),
+                                             _ptr(w), _ptr(out), _stream()))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/aba.h"
@@ -79,6 +80,38 @@ aba_status check_plan(const aba_plan_t *p)
     if (ref.n_blocks != p->n_blocks || ref.seq_pad != p->seq_pad || ref.list_cap != p->list_cap ||
         ref.block != p->block || ref.n_key_blocks != p->n_key_blocks || ref.workspace_bytes != p->workspace_bytes)
         return fail(ABA_E_INVALID, "plan fields are inconsistent; fill the plan with aba_plan");
+    return ABA_OK;
+}
+
+// Scratch of aba_attend_noalloc: the attention work order (one int32 per query
+// block) of calls whose caller cannot allocate a workspace.  Each GPU the
+// library runs on holds its own copy until the process ends; every call on a
+// GPU reuses it, so calls that overlap in time on one GPU race.
+constexpr size_t kStaticScratchBytes = size_t(1) << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch (the current device's), resolved once
+// per device with that device current.  The array's name is only a host-side
+// stand-in; kernels get this address.
+aba_status static_scratch(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ABA_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ABA_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ABA_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
     return ABA_OK;
 }
 
@@ -234,6 +267,37 @@ aba_status aba_attend_full(const aba_plan_t *p, const void *q, const void *k, co
                                          p->n_blocks, p->softmax_scale, nullptr, nullptr, nullptr, p->list_cap, true,
                                          workspace, out, stream),
                       "attend_full launch");
+}
+
+aba_status aba_attend_noalloc(const aba_plan_t *p, const void *q, const void *k, const void *v, const int32_t *idx,
+                              const int32_t *cnt, const float *w, void *out, hipStream_t stream)
+{
+    g_last_error.clear();
+    aba_status st = check_plan(p);
+    if (st != ABA_OK) return st;
+    if (!q || !k || !v || !idx || !cnt || !w || !out)
+        return fail(ABA_E_INVALID, "q, k, v, idx, cnt, w and out must be non-NULL");
+    if (p->dtype == ABA_BF16 && p->head_dim != 128)
+        return fail(ABA_E_UNSUPPORTED, "aba_attend_noalloc: bf16 at head_dim %d stages a transposed copy of v; use "
+                    "aba_attend with a workspace", p->head_dim);
+    const size_t need = workspace_layout(*p).attend_total;
+    if (need > kStaticScratchBytes)
+        return fail(ABA_E_UNSUPPORTED, "aba_attend_noalloc: the work order of %lld query blocks needs %zu bytes, more "
+                    "than the %zu of its static scratch (at most %zu query blocks); use aba_attend with a workspace",
+                    (long long)p->batch * p->heads * p->n_blocks, need, kStaticScratchBytes,
+                    kStaticScratchBytes / sizeof(int32_t));
+    void *ws = nullptr;
+    st = static_scratch(&ws);
+    if (st != ABA_OK) return st;
+    if (p->key_block == ABA_FINE_BLOCK)
+        return hip_status(aba::launch_attend_fine(q, k, v, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad,
+                                                  p->head_dim, p->n_blocks, p->n_key_blocks, p->softmax_scale, idx, cnt,
+                                                  w, p->list_cap, ws, out, stream),
+                          "attend launch");
+    return hip_status(aba::launch_attend(q, k, v, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad, p->head_dim,
+                                         p->n_blocks, p->softmax_scale, idx, cnt, w, p->list_cap, false, ws, out,
+                                         stream),
+                      "attend launch");
 }
 
 aba_status aba_block_mass(const aba_plan_t *p, const void *q, const void *k, const int32_t *items, int32_t n_items,

@@ -182,6 +182,19 @@ aba_status aba_attend(const aba_plan_t *p, const void *q, const void *k, const v
 aba_status aba_attend_full(const aba_plan_t *p, const void *q, const void *k, const void *v, void *out,
                            void *workspace, hipStream_t stream);
 
+/* aba_attend without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments (minus workspace), kernels and
+ * results as aba_attend.  The work order lives in a static device array of the
+ * library (1 MiB, i.e. at most 262144 = B * H * NB query blocks), one per GPU,
+ * held until the process ends; it needs no clearing between calls.  Every call
+ * on a GPU shares that GPU's array: calls that overlap in time on one GPU race
+ * and must be ordered by the caller (one stream, or events).  Allocates
+ * nothing.  Returns ABA_E_UNSUPPORTED for more query blocks than the array
+ * holds, and for bf16 at head_dim 64 (which stages a transposed copy of v). */
+aba_status aba_attend_noalloc(const aba_plan_t *p, const void *q, const void *k, const void *v, const int32_t *idx,
+                              const int32_t *cnt, const float *w, void *out, hipStream_t stream);
+
 /* Dense attention mass per key block (of the plan's key_block tokens), for
  * judging a block selection (IBCS paragraph and the opening of "Три приёма
  * AB-Attention": the share of the attention a selection keeps).  For each
