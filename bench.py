@@ -44,6 +44,7 @@ from block_sparse_attention_38_amd.workloads import ALL, CLUSTERS, KMEANS_ITERS 
 METRIC = "ms/call and effective TFLOP/s of sparse attention, 32K-token video layer"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (vector)
 ATTEND_SRC = os.path.join(ROOT, "block_sparse_attention_38_amd", "csrc", "attend.hip")
 TRAFFIC_FILES = {128: os.path.join(ROOT, "profiles", "attend_single_layer_traffic.json"),
                  4: os.path.join(ROOT, "profiles", "attend_single_layer_4token_traffic.json")}
@@ -146,14 +147,20 @@ def cpu_baseline(w, p, q, k, v, seed: int, target_s: float):
     }
 
 
-def selection_diagnostics(w, p, qkv, lists, ws, n_blocks: int):
+def selection_diagnostics(w, p, qkv, ws, n_blocks: int, seed: int, softmax_scale: float = 0.0):
     """How much dense attention mass the selections keep, on sampled query blocks
     (dense mass per key block from aba_block_mass), and the attention error of the
-    sampled lists against hard top-K lists of the same scores (outputs of
-    aba_attend against aba_attend_full).  Untimed."""
+    sampled lists and of hard top-K lists of the same scores against dense
+    attention (outputs of aba_attend against aba_attend_full), as an RMS over the
+    sampled rows divided by the RMS of v.  Untimed.  softmax_scale > 0 runs the
+    whole layer (scores, lists, attention) at that scale instead of the plan's:
+    1.0 is the peaked variant (logits x sqrt(D) at D = 128)."""
     qd, kd, vd = qkv
-    (scores, (idx, cnt, wt)) = lists
     B, H, NB, K = p.batch, p.heads, p.n_blocks, p.budget
+    if softmax_scale > 0:
+        p = aba.plan(B, H, w.seq_len, w.head_dim, w.dtype, p.n_clusters, p.kmeans_iters, K, softmax_scale=softmax_scale)
+    scores = aba.score(p, qd, kd, ws=ws)
+    idx, cnt, wt = aba.sample(p, scores, seed)
     rng = np.random.default_rng(5)
     items = sorted({(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(NB))) for _ in range(4 * n_blocks)})
     items = items[:max(n_blocks, 32)]
@@ -166,7 +173,8 @@ def selection_diagnostics(w, p, qkv, lists, ws, n_blocks: int):
         return np.take_along_axis(mass, top, axis=1).sum(axis=1)
 
     ibcs = top_k_mass(scores.double().cpu().numpy())
-    p1 = aba.plan(B, H, w.seq_len, w.head_dim, w.dtype, 1, p.kmeans_iters, K)      # one cluster: mean-pool scorer
+    p1 = aba.plan(B, H, w.seq_len, w.head_dim, w.dtype, 1, p.kmeans_iters, K,
+                  softmax_scale=p.softmax_scale)                                    # one cluster: mean-pool scorer
     meanpool = top_k_mass(aba.score(p1, qd, kd, ws=aba.workspace(p1, qd.device)).double().cpu().numpy())
     idx_h, cnt_h, wt_h = (x.cpu().numpy() for x in (idx, cnt, wt))
     kept, ht = [], []
@@ -185,16 +193,9 @@ def selection_diagnostics(w, p, qkv, lists, ws, n_blocks: int):
     o_sip = aba.attend(p, qd, kd, vd, idx, cnt, wt, ws=ws)
     o_top = aba.attend(p, qd, kd, vd, idx_t, cnt_t, wt_t, ws=ws)
     torch.cuda.synchronize()
-
-    def rel_err(o):
-        e = []
-        for b, h, qb in items:
-            n = min(128, w.seq_len - 128 * qb)
-            ref = dense[b, h, 128 * qb:128 * qb + n].float()
-            e.append(((o[b, h, 128 * qb:128 * qb + n].float() - ref).norm() / ref.norm()).item())
-        return float(np.mean(e))
-
+    errs = attention_errors(w, items, vd, dense, {"sip": o_sip, "hard_topk": o_top})
     return {
+        "softmax_scale": float(p.softmax_scale),
         "query_blocks": len(items),
         "ideal_topk_mass": float(ideal.mean()),
         "ibcs_topk_mass": float(ibcs.mean()),
@@ -202,8 +203,29 @@ def selection_diagnostics(w, p, qkv, lists, ws, n_blocks: int):
         "recall_gap": {"ibcs": float((ideal - ibcs).mean()), "meanpool": float((ideal - meanpool).mean())},
         "sip_kept_mass": float(np.mean(kept)),
         "sip_ht_weighted_mass": float(np.mean(ht)),
-        "attention_rel_err_vs_dense": {"sip": rel_err(o_sip), "hard_topk": rel_err(o_top)},
+        "mean_kept_blocks": float(cnt_h.mean()),
+        "attention_rms_err_over_rms_v": errs,
+        "dense_output_rms_over_rms_v": errs.pop("dense_scale"),
     }
+
+
+def attention_errors(w, items, vd, dense, outs):
+    """RMS of (out - dense) over the sampled query blocks' valid rows, divided by
+    the RMS of v over the same heads (the scale of an output that attends to one
+    key); also the dense output's own RMS on that scale."""
+    rows = {name: [] for name in outs}
+    ref, vs = [], []
+    for b, h, qb in items:
+        n = min(128, w.seq_len - 128 * qb)
+        d = dense[b, h, 128 * qb:128 * qb + n].float()
+        ref.append(d)
+        vs.append(vd[b, h, :w.seq_len].float().pow(2).mean())
+        for name, o in outs.items():
+            rows[name].append(o[b, h, 128 * qb:128 * qb + n].float() - d)
+    rms_v = float(torch.stack(vs).mean().sqrt())
+    res = {name: float(torch.cat(r).pow(2).mean().sqrt()) / rms_v for name, r in rows.items()}
+    res["dense_scale"] = float(torch.cat(ref).pow(2).mean().sqrt()) / rms_v
+    return res
 
 
 def fine_leg(args, w, sets, density, coarse_plan, coarse_lists, dense_ms, n_diag: int, diagnostics: bool):
@@ -302,21 +324,15 @@ def fine_leg(args, w, sets, density, coarse_plan, coarse_lists, dense_ms, n_diag
     o_f = aba.attend(p, qd, kd, vd, *set_lists[0][1], ws=ws)
     o_c = aba.attend(coarse_plan, qd, kd, vd, *coarse_lists[1], ws=aba.workspace(coarse_plan, dev))
     torch.cuda.synchronize()
-
-    def rel_err(o):
-        e = []
-        for b, h, qb in items:
-            nq = min(128, w.seq_len - 128 * qb)
-            ref = dense[b, h, 128 * qb:128 * qb + nq].float()
-            e.append(((o[b, h, 128 * qb:128 * qb + nq].float() - ref).norm() / ref.norm()).item())
-        return float(np.mean(e))
+    errs = attention_errors(w, items, vd, dense, {"128_token": o_c, "4_token": o_f})
 
     res["diagnostics"] = {
         "query_blocks": len(items),
         "ideal_topk_mass": {"128_token": float(ideal_c.mean()), "4_token": float(ideal_f.mean())},
         "ibcs_topk_mass": {"128_token": float(ibcs_c.mean()), "4_token": float(ibcs_f.mean())},
         "sip_kept_mass": {"128_token": sip_mass(mass_c, coarse_lists[1]), "4_token": sip_mass(mass_f, set_lists[0][1])},
-        "attention_rel_err_vs_dense": {"128_token": rel_err(o_c), "4_token": rel_err(o_f)},
+        "attention_rms_err_over_rms_v": {"128_token": errs["128_token"], "4_token": errs["4_token"]},
+        "dense_output_rms_over_rms_v": errs["dense_scale"],
     }
     log(f"[bench] 4-token diagnostics: {json.dumps(res['diagnostics'])}")
     return res
@@ -429,6 +445,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--input-sets", type=int, default=3, help="input sets the steps cycle through")
+    ap.add_argument("--windows", type=int, default=5,
+                    help="windows of K steps timed in all (the first gives value; the rest its spread)")
     ap.add_argument("--plan-every", type=int, default=4, help="sweep: steps between plan refreshes (the page: 4)")
     ap.add_argument("--dense-frac", type=float, default=0.2,
                     help="sweep: share of the first steps run dense (the page: 10 of 50)")
@@ -476,7 +494,7 @@ def main():
     out = torch.empty_like(sets[0][0])
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i, ev=None, att=None):
         qd, kd, vd = sets[i % len(sets)]
         seed = args.seed + i % len(sets)
         if ev is not None:
@@ -487,28 +505,72 @@ def main():
         aba.sample(p, scores, seed, out=lists)
         if ev is not None:
             ev[2].record(stream)
+        if att is not None:
+            att[0].record(stream)
         aba.attend(p, qd, kd, vd, *lists, out=out, ws=ws)
+        if att is not None:
+            att[1].record(stream)
         if ev is not None:
             ev[3].record(stream)
+
+    # the dense path first: its own measurement, and it leaves the GPU at its
+    # loaded clock, so that the timed steps do not include the ramp from idle
+    dense_ms = None
+    if not args.no_dense:
+        qd, kd, vd = sets[0]
+        aba.attend_full(p, qd, kd, vd, out=out, ws=ws)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.dense_reps):
+            aba.attend_full(p, qd, kd, vd, out=out, ws=ws)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / args.dense_reps
+        log(f"[bench] dense attention: {dense_ms:.3f} ms")
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # the timed region: K steps, events only around each aba_attend call (the
+    # dominant call, for the roofline)
+    att_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, att=att_ev[i])
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
+    attend_each = np.array([a.elapsed_time(b) for a, b in att_ev])
+    attend_timed_ms = float(attend_each.mean())
+    # the same K steps again with events around every call, for the per-stage
+    # times (the events themselves add a little to these)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     score_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     sample_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     attend_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (score {score_ms:.3f}, sample {sample_ms:.3f}, "
-        f"attend {attend_ms:.3f})")
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, aba_attend {attend_timed_ms:.3f} ms; per stage "
+        f"(a second, evented pass) score {score_ms:.3f}, sample {sample_ms:.3f}, attend {attend_ms:.3f}")
+    # stability: the same K steps timed again in further windows (after the
+    # timed region above, which alone gives `value`)
+    window_ms = [ms_per_step]
+    for _ in range(max(0, args.windows - 1)):
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        window_ms.append(w0.elapsed_time(w1) / args.steps)
+    log(f"[bench] {len(window_ms)} windows of {args.steps} steps: median {np.median(window_ms):.3f} ms/step, "
+        f"range {min(window_ms):.3f} .. {max(window_ms):.3f}")
 
     # kept work per call, averaged over the input sets the steps cycle through
     kflops_sets, dens_sets, set_lists = [], [], []
@@ -524,23 +586,13 @@ def main():
     dense_flops = w.dense_flops
     realised_density = float(np.mean(dens_sets))
 
-    dense_ms = None
-    if not args.no_dense:
-        qd, kd, vd = sets[0]
-        aba.attend_full(p, qd, kd, vd, out=out, ws=ws)
-        torch.cuda.synchronize()
-        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
-        for _ in range(args.dense_reps):
-            aba.attend_full(p, qd, kd, vd, out=out, ws=ws)
-        d1.record(stream)
-        torch.cuda.synchronize()
-        dense_ms = d0.elapsed_time(d1) / args.dense_reps
-        log(f"[bench] dense attention: {dense_ms:.3f} ms")
-
     diagnostics = None
     if not args.no_diagnostics and w.dtype == "bf16" and not fine_main:
-        diagnostics = selection_diagnostics(w, p, sets[0], set_lists[0], ws, args.diag_blocks)
+        diagnostics = {
+            "literal": selection_diagnostics(w, p, sets[0], ws, args.diag_blocks, args.seed),
+            # the same inputs with logits x sqrt(D): reported beside the workload, never in place of it
+            "peaked": selection_diagnostics(w, p, sets[0], ws, args.diag_blocks, args.seed, softmax_scale=1.0),
+        }
         log(f"[bench] diagnostics: {json.dumps(diagnostics)}")
 
     if args.copy_calibration:
@@ -555,7 +607,13 @@ def main():
     rows, krows = B * H * NB, B * H * p.n_key_blocks
     score_bytes = (2 * B * H * w.seq_len * D * elem + 2 * 4 * rows * (p.n_clusters * D + p.n_clusters)
                    + 2 * 4 * krows * D + 4 * rows * p.n_key_blocks)
-    attend_tflops = kflops / (attend_ms * 1e-3) / 1e12
+    # scoring-stage fp32 work: T Lloyd rounds per query block (the assignment's
+    # 2 n C D and the update's n D), then the centroid x pooled-key products 2 C NBk D
+    n_valid = np.minimum(128, w.seq_len - 128 * np.arange(NB)).astype(np.float64)
+    C, T = p.n_clusters, p.kmeans_iters
+    kmeans_flops = B * H * float((T * (2.0 * n_valid * C * D + n_valid * D)).sum())
+    score_flops = kmeans_flops + rows * 2.0 * C * p.n_key_blocks * D
+    attend_tflops = kflops / (attend_timed_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC,
         "value": dense_flops / (ms_per_step * 1e-3) / 1e12,
@@ -576,13 +634,26 @@ def main():
             "seed": args.seed, "input_sets": len(sets),
         },
         "stages_ms": {"score": score_ms, "sample": sample_ms, "attend": attend_ms},
+        "attend_ms_timed_region": attend_timed_ms,
         "dense_attention_ms": dense_ms,
-        "speedup_vs_dense": {"layer": dense_ms / ms_per_step, "attention": dense_ms / attend_ms} if dense_ms else None,
+        "speedup_vs_dense": {"layer": dense_ms / ms_per_step, "attention": dense_ms / attend_timed_ms} if dense_ms else None,
         "realised_density": realised_density,
         "kept_tflop_per_call": kflops / 1e12,
         "attend_kept_tflops": attend_tflops,
+        "timing": {
+            "evented_step_ms_median": float(np.median(step_ms)), "evented_step_ms_p10": float(np.percentile(step_ms, 10)),
+            "evented_step_ms_p90": float(np.percentile(step_ms, 90)),
+            "attend_ms_timed_median": float(np.median(attend_each)),
+            "attend_ms_timed_p10": float(np.percentile(attend_each, 10)),
+            "attend_ms_timed_p90": float(np.percentile(attend_each, 90)),
+            "windows_ms_per_step": window_ms, "windows_median": float(np.median(window_ms)),
+        },
         "score_stage_gbs": score_bytes / (score_ms * 1e-3) / 1e9,
         "score_stage_hbm_frac": score_bytes / (score_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        # the stage is bound by its fp32 arithmetic (k-means dominates), not by HBM
+        "score_stage_fp32_tflops": score_flops / (score_ms * 1e-3) / 1e12,
+        "score_stage_fp32_frac": score_flops / (score_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+        "score_stage_algorithmic_gflop": score_flops / 1e9,
         "roofline": {
             # the whole aba_attend call: the work order is part of it
             "kernel": (("aba_attend: order_kernel + attend_fine_kernel<128>" if fine_main else

@@ -372,6 +372,35 @@ template <bool full> __device__ __forceinline__ Entry window_entry(const Window 
 
 __device__ __forceinline__ float max2(float a, float b) { return __builtin_fmaxf(a, b); }
 
+// Raw v_max3_f32 / v_max_f32 on values that are never NaN (products of finite
+// bf16 operands, or -inf where masked): without the operand canonicalisation
+// the compiler adds around fmaxf.
+__device__ __forceinline__ float vmax3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float vmax(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// Maximum of the 32 values of two S^T accumulator tiles of one lane: two
+// independent v_max3 chains of 16 values each.
+__device__ __forceinline__ float tile_max(const floatx16 &a, const floatx16 &b)
+{
+    float x = vmax3(a[0], a[1], a[2]), y = vmax3(b[0], b[1], b[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) {
+        x = vmax3(x, a[r], a[r + 1]);
+        y = vmax3(y, b[r], b[r + 1]);
+    }
+    return vmax3(vmax(x, a[15]), y, b[15]);
+}
+
 // l += p[e - 1] + p[e] for the bf16 probabilities of one pair (e odd): one
 // v_dot2 against (1, 1), so the softmax normaliser sums exactly the rounded
 // values the PV product multiplies.
@@ -386,7 +415,7 @@ __device__ __forceinline__ void row_sum_pair(const bf16x8 &p, int e, float &l)
 __device__ __forceinline__ float half_pair_max(float x)
 {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 template <int D, bool full>
@@ -519,14 +548,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 for (int r = 0; r < 16; ++r)
                     if (key0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= N) s[kt][r] = -INFINITY;
         }
-        float mx = s[0][0];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (kt | r) mx = max2(mx, s[kt][r]);
+        static_assert(KT == 2, "two 32-key tiles per sub-tile");
         // block weight enters as a logit shift
-        const float m_tile = fmaf(half_pair_max(mx), scale_log2, lw);
+        const float m_tile = fmaf(half_pair_max(tile_max(s[0], s[1])), scale_log2, lw);
         // lazy rescale: the running max moves only when the tile's max
         // exceeds it by more than the slack (always on the first tile)
         if (__ballot(m_tile > m_run + kRescaleSlack) != 0) {
@@ -877,13 +901,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         if (key0 + c >= N) s[kt][4 * i + c] = -INFINITY;
                 }
         }
-        float mx = s[0][0];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (kt | r) mx = max2(mx, s[kt][r]);
-        const float m_tile = fmaf(half_pair_max(mx), scale_log2, lwm);
+        const float m_tile = fmaf(half_pair_max(tile_max(s[0], s[1])), scale_log2, lwm);
         if (__ballot(m_tile > m_run + kRescaleSlack) != 0) {
             asm volatile("s_nop 0");
             const float m_new = max2(m_run, m_tile);

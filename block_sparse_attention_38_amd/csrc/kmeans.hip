@@ -168,12 +168,13 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T *__restrict__ q, in
 //               clusters for its query and adds them locally; the argmin needs
 //               one exchange between the two lane halves.
 //   update      sums = onehot^T X with X^T staged once per block in LDS; new
-//               centroids are sums / counts.  The one-hot operand comes from
-//               the assignment bytes with a few bit operations per four
-//               queries, and the same flags give the counts (popcounts), so
-//               no separate counting pass runs per round; the lanes that form
-//               a centroid element also write its three bf16 parts and its
-//               share of |c|^2, so a round has two barriers.
+//               centroids are sums / counts.  The assignment writes, once per
+//               round, a membership flag byte per (cluster, query) and each
+//               wavefront's cluster counts (ballots) to LDS; the update turns
+//               eight flags into its one-hot operand with two shifts and four
+//               byte permutes; the lanes that form a centroid element also
+//               write its three bf16 parts and its share of |c|^2, so a round
+//               has two barriers.
 // A round whose assignment equals the previous round's leaves every later
 // round unchanged bit for bit (same rows, same sums), so the loop stops there:
 // the result is exactly that of all T rounds.
@@ -190,16 +191,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Bit 7 of byte i set iff byte i of x equals byte i of pat, all other bits clear:
-// t = x ^ pat is zero exactly in the matching bytes; (t & 0x7f) + 0x7f carries
-// into bit 7 iff the low seven bits are not all zero, and no byte carries into
-// the next.
-__device__ __forceinline__ uint32_t match_bytes(uint32_t x, uint32_t pat)
-{
-    const uint32_t t = x ^ pat;
-    return ~(((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t) & 0x80808080u;
-}
-
 // Eight bf16 values from the flags of eight bytes (f0: elements 0..3, f1: 4..7):
 // 4.0 (0x4080: low byte 0x80, high byte 0x40) for a set flag, else 0.  Byte
 // permutes interleave each flag byte (0x80 / 0) with itself shifted right by one
@@ -212,13 +203,13 @@ __device__ __forceinline__ uint4 onehot4(uint32_t f0, uint32_t f1)
                       __builtin_amdgcn_perm(g1, f1, 0x05010400u), __builtin_amdgcn_perm(g1, f1, 0x07030602u));
 }
 
-// The same workgroup then pools the keys of its 128 tokens (IBCS paragraph:
+// The same workgroup also pools the keys of its 128 tokens (IBCS paragraph:
 // a key block is represented by its averaged keys): one 128-token key block
-// (kb = 128) or 32 4-token ones (kb = 4), into kbar [B, H, NBk, D].  The key
-// reads overlap the rounds of the other workgroups on the CU, and the separate
-// pooling pass over k disappears.
+// (kb = 128) or 32 4-token ones (kb = 4), into kbar [B, H, NBk, D].  It does so
+// first: the key loads are issued ahead of the query loads, so their latency
+// overlaps the query staging, and the separate pooling pass over k disappears.
 template <int D>
-__global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__restrict__ q, int N, int N_pad, int NB,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void kmeans_mfma_kernel(const uint16_t *__restrict__ q, int N, int N_pad, int NB,
                                                           int C, int T_iters, float *__restrict__ cent_out,
                                                           float *__restrict__ w_out, const uint16_t *__restrict__ k,
                                                           int kb, int NBk, float *__restrict__ kbar)
@@ -235,8 +226,14 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
     // no separate fp32 copy is kept (that keeps the block under 40 KB of LDS:
     // four workgroups per CU)
     __shared__ uint4 cs_s[24 * DCH];
-    __shared__ __align__(16) uint8_t asg[kBlock];
     __shared__ float cn_part[4][kMaxClusters];   // per-wavefront shares of |c_m|^2
+    // membership flags written by the assignment: byte q of row m is 0x80 when
+    // query q is in cluster m, else 0 (rows padded to 136 bytes: the eight rows
+    // an update operand read touches start on different banks); and the
+    // per-wavefront cluster counts of the last assignment
+    constexpr int kFlagPitch = kBlock + 8;
+    __shared__ __align__(16) uint8_t flag_s[kMaxClusters * kFlagPitch];
+    __shared__ int cnt_s[4][kMaxClusters];
 
     const int row = blockIdx.x;                           // (b*H + h) * NB + query block
     const int qb = row % NB;
@@ -245,6 +242,38 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, half = lane >> 5;
     const uint16_t *src = q + (bh * N_pad + (long)qb * kBlock) * D;
+
+    // ---- key pooling of this block's 128 tokens (n valid), first: the key
+    // loads are issued before the query loads, so their latency overlaps the
+    // query staging below instead of trailing the rounds
+    const uint16_t *ksrc = k + (bh * N_pad + (long)qb * kBlock) * D;
+    constexpr int G = 256 / DCH;           // 128-token key block: thread (group g, chunk c)
+    constexpr int RPT = kBlock / G;        // sums rows g, g + G, .. (loads issued before the sums)
+    constexpr int kFine = kBlock / kFineBlock;
+    constexpr int IPT = kFine * DCH / 256; // 4-token key blocks: (block, chunk) items per thread
+    static_assert(kFine * DCH % 256 == 0, "whole items per thread");
+    static_assert(RPT == IPT * kFineBlock, "the same number of row loads in both cases");
+    uint4 kraw[RPT];
+    if (kb == kBlock) {
+        const int c = tid % DCH, g = tid / DCH;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = g + G * i;
+            kraw[i] = r < n ? *reinterpret_cast<const uint4 *>(ksrc + (long)r * D + 8 * c) : make_uint4(0, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int i = tid + 256 * it, g = i / DCH, c = i % DCH;
+            const int j = qb * kFine + g;
+#pragma unroll
+            for (int r = 0; r < kFineBlock; ++r)
+                kraw[it * kFineBlock + r] =
+                    (j < NBk && kFineBlock * j + r < N)
+                        ? *reinterpret_cast<const uint4 *>(ksrc + (long)(kFineBlock * g + r) * D + 8 * c)
+                        : make_uint4(0, 0, 0, 0);
+        }
+    }
 
     // this wavefront's 32 queries as B fragments of the assignment product
     const int my_q = wave * 32 + l32;
@@ -255,6 +284,62 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
         uint4 raw = make_uint4(0, 0, 0, 0);
         if (qv) raw = *reinterpret_cast<const uint4 *>(src + (long)my_q * D + 16 * ks + 8 * half);
         xf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+
+    // sum the keys (the query loads above stay in flight)
+    if (kb == kBlock) {
+        const int c = tid % DCH, g = tid / DCH;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            if (g + G * i >= n) break;
+            const uint32_t w4[4] = {kraw[i].x, kraw[i].y, kraw[i].z, kraw[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += bf16_lo(w4[e]);
+                acc[2 * e + 1] += bf16_hi(w4[e]);
+            }
+        }
+        // the groups g of one wavefront (lanes c + DCH j) add up by shuffles, the
+        // four wavefronts' sums through LDS (the X^T space, written only below)
+#pragma unroll
+        for (int o = DCH; o < 64; o <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+        float *part = reinterpret_cast<float *>(xt_s);
+        if (lane < DCH) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[wave * D + 8 * lane + e] = acc[e];
+        }
+        __syncthreads();
+        if (tid < D)
+            kbar[((long)bh * NBk + qb) * D + tid] =
+                (((part[tid] + part[D + tid]) + part[2 * D + tid]) + part[3 * D + tid]) / (float)n;
+        __syncthreads();   // the X^T writes below reuse the space
+    } else {
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int i = tid + 256 * it, g = i / DCH, c = i % DCH;
+            const int j = qb * kFine + g;
+            if (j >= NBk) continue;
+            const int nr = min(kFineBlock, N - kFineBlock * j);
+            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < kFineBlock; ++r) {
+                if (r >= nr) break;
+                const uint4 x = kraw[it * kFineBlock + r];
+                const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += bf16_lo(w4[e]);
+                    acc[2 * e + 1] += bf16_hi(w4[e]);
+                }
+            }
+            const float fn = (float)nr;
+            float4 *dst = reinterpret_cast<float4 *>(kbar + ((long)bh * NBk + j) * D + 8 * c);
+            dst[0] = make_float4(acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn);
+            dst[1] = make_float4(acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn);
+        }
     }
 
     // X^T into LDS: thread (c, quad) moves queries 4quad..4quad+3 of dims 8c..8c+7
@@ -360,7 +445,17 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
             bd = od;
             bm = om;
         }
-        if (half == 0) asg[my_q] = qv ? (uint8_t)bm : (uint8_t)0xFF;
+        // lane half h writes the flags of its query in rows 4h .. 4h+3
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = 4 * half + j;
+            flag_s[m * kFlagPitch + my_q] = (qv && bm == m) ? (uint8_t)0x80 : (uint8_t)0;
+        }
+#pragma unroll
+        for (int m = 0; m < kMaxClusters; ++m) {
+            const int c = __popcll(__ballot(half == 0 && qv && bm == m));
+            if (lane == 0) cnt_s[wave][m] = c;
+        }
         const int changed = (half == 0 && qv && bm != prev) ? 1 : 0;
         prev = bm;
         const int any_changed = __syncthreads_or(changed);
@@ -373,29 +468,30 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
             for (int r = 0; r < 16; ++r) sum[r] = 0.f;
             const int d = wave * 32 + l32;
             // A operand row l32 is cluster l32 % 8 (rows >= 8 only feed accumulator
-            // rows that are never read); its entries are 4.0 (bf16 0x4080) where the
-            // query's assignment byte equals the cluster, so the sums are 4x the
-            // cluster sums, exactly
-            const uint32_t pat = 0x01010101u * (uint32_t)(l32 & 7);
-            int cnt = 0;
+            // rows that are never read); its entries are 4.0 (bf16 0x4080) for the
+            // cluster's queries, so the sums are 4x the cluster sums, exactly
+            const uint8_t *flag_row = flag_s + (l32 & 7) * kFlagPitch + 8 * half;
 #pragma unroll
             for (int ks = 0; ks < kBlock / 16; ++ks) {
-                const uint2 ab = *reinterpret_cast<const uint2 *>(&asg[16 * ks + 8 * half]);
-                const uint32_t f0 = match_bytes(ab.x, pat), f1 = match_bytes(ab.y, pat);
-                cnt += __popc(f0) + __popc(f1);
-                const uint4 oh = onehot4(f0, f1);
+                const uint2 f = *reinterpret_cast<const uint2 *>(flag_row + 16 * ks);
+                const uint4 oh = onehot4(f.x, f.y);
                 const uint4 b = xt_s[d * 16 + ((2 * ks + half) ^ xt_swz(d))];
                 sum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, oh),
                                                               __builtin_bit_cast(bf16x8, b), sum, 0, 0, 0);
             }
-            // lane m < 8 (either half) counted cluster m over its half of the queries
-            cnt += __shfl_xor(cnt, 32, 64);
+            // counts of clusters 4half .. 4half+3: the four wavefronts' shares
+            const int4 c0 = *reinterpret_cast<const int4 *>(&cnt_s[0][4 * half]);
+            const int4 c1 = *reinterpret_cast<const int4 *>(&cnt_s[1][4 * half]);
+            const int4 c2 = *reinterpret_cast<const int4 *>(&cnt_s[2][4 * half]);
+            const int4 c3 = *reinterpret_cast<const int4 *>(&cnt_s[3][4 * half]);
+            const int cnts[4] = {c0.x + c1.x + c2.x + c3.x, c0.y + c1.y + c2.y + c3.y, c0.z + c1.z + c2.z + c3.z,
+                                 c0.w + c1.w + c2.w + c3.w};
             // lane holds the sums of clusters 4half .. 4half+3 for dim d
             float sq[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = 4 * half + r;
-                const int cn = __shfl(cnt, m, 64);
+                const int cn = cnts[r];
                 float cv;
                 if (m < C && cn > 0) {
                     // (4 sum) x approximate 1 / (4 n): within 2 ulp of the mean
@@ -429,89 +525,8 @@ __global__ __launch_bounds__(256) void kmeans_mfma_kernel(const uint16_t *__rest
     float *co = cent_out + (long)row * C * D;
     for (int i = tid; i < C * D; i += 256) co[i] = centroid(i / D, i % D);
     if (tid < C) {   // weights from the last assignment
-        const uint32_t pat = 0x01010101u * (uint32_t)tid;
-        const uint32_t *a4 = reinterpret_cast<const uint32_t *>(asg);
-        int cn = 0;
-#pragma unroll 8
-        for (int i = 0; i < kBlock / 4; ++i) cn += __popc(match_bytes(a4[i], pat));
+        const int cn = cnt_s[0][tid] + cnt_s[1][tid] + cnt_s[2][tid] + cnt_s[3][tid];
         w_out[(long)row * C + tid] = (float)((double)cn / (double)n);
-    }
-
-    // ---- key pooling of this block's 128 tokens (n valid)
-    const uint16_t *ksrc = k + (bh * N_pad + (long)qb * kBlock) * D;
-    if (kb == kBlock) {
-        // thread (group g, chunk c) sums rows g, g + G, ..; the G partial rows are
-        // then added in order through LDS (the X^T space, free after the rounds)
-        constexpr int G = 256 / DCH;
-        constexpr int PP = D + 4;   // partial row pitch: the G rows start on different banks
-        float *part = reinterpret_cast<float *>(xt_s);
-        static_assert(G * PP * sizeof(float) <= sizeof(xt_s), "partial rows fit in the X^T space");
-        const int c = tid % DCH, g = tid / DCH;
-        constexpr int RPT = kBlock / G;   // rows per thread; all loads issued before the sums
-        uint4 raw[RPT];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = g + G * i;
-            raw[i] = r < n ? *reinterpret_cast<const uint4 *>(ksrc + (long)r * D + 8 * c) : make_uint4(0, 0, 0, 0);
-        }
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            if (g + G * i >= n) break;
-            const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += bf16_lo(w4[e]);
-                acc[2 * e + 1] += bf16_hi(w4[e]);
-            }
-        }
-        __syncthreads();   // every wavefront is past its last X^T read
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part[g * PP + 8 * c + e] = acc[e];
-        __syncthreads();
-        if (tid < D) {
-            float sum = 0.f;
-            for (int gg = 0; gg < G; ++gg) sum += part[gg * PP + tid];
-            kbar[((long)bh * NBk + qb) * D + tid] = sum / (float)n;
-        }
-    } else {
-        // 4-token blocks 32 qb .. 32 qb + 31: thread (block, chunk)
-        constexpr int kFine = kBlock / kFineBlock;
-        constexpr int IPT = kFine * DCH / 256;   // (block, chunk) items per thread
-        static_assert(kFine * DCH % 256 == 0, "whole items per thread");
-        uint4 raw[IPT][kFineBlock];               // all loads issued before the sums
-#pragma unroll
-        for (int it = 0; it < IPT; ++it) {
-            const int i = tid + 256 * it, g = i / DCH, c = i % DCH;
-            const int j = qb * kFine + g;
-#pragma unroll
-            for (int r = 0; r < kFineBlock; ++r)
-                raw[it][r] = (j < NBk && kFineBlock * j + r < N)
-                                 ? *reinterpret_cast<const uint4 *>(ksrc + (long)(kFineBlock * g + r) * D + 8 * c)
-                                 : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int it = 0; it < IPT; ++it) {
-            const int i = tid + 256 * it, g = i / DCH, c = i % DCH;
-            const int j = qb * kFine + g;
-            if (j >= NBk) continue;
-            const int nr = min(kFineBlock, N - kFineBlock * j);
-            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-            for (int r = 0; r < kFineBlock; ++r) {
-                if (r >= nr) break;
-                const uint32_t w4[4] = {raw[it][r].x, raw[it][r].y, raw[it][r].z, raw[it][r].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[2 * e] += bf16_lo(w4[e]);
-                    acc[2 * e + 1] += bf16_hi(w4[e]);
-                }
-            }
-            const float fn = (float)nr;
-            float4 *dst = reinterpret_cast<float4 *>(kbar + ((long)bh * NBk + j) * D + 8 * c);
-            dst[0] = make_float4(acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn);
-            dst[1] = make_float4(acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn);
-        }
     }
 }
 

@@ -140,3 +140,42 @@ def test_wide_fine_scores_are_run_to_run_identical(aba):
         again = aba.score(p, qd, kd, ws=ws)
         torch.cuda.synchronize()
         assert torch.equal(again, first)
+
+
+def test_high_res_fine_scores_lists_and_attention(aba, highres):
+    """4-token key blocks at the 118,800-token layer (29,700 key blocks, the last of
+    the 16-token tail block ending the layer, budget 2368): pooled keys over the
+    whole layer, scores of sampled rows re-scored by the oracle from the GPU's
+    parts, every list bit for bit, attention on sampled query blocks (the ragged
+    last one included)."""
+    from block_sparse_attention_38_amd.workloads import FINE_BLOCK
+
+    w = HIGHRES
+    q, k, v = highres["cpu"]
+    qd, kd, vd = highres["gpu"]
+    p = aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, 8, 10, w.fine_budget(), key_block=FINE_BLOCK)
+    assert (p.n_key_blocks, p.budget) == (29700, 2368)
+    ws = aba.workspace(p, qd.device)
+    s, cent, wgt, kbar = aba.score(p, qd, kd, return_parts=True, ws=ws)
+    idx, cnt, wt = aba.sample(p, s, 7)
+    out = aba.attend(p, qd, kd, vd, idx, cnt, wt, ws=ws)
+    torch.cuda.synchronize()
+    ref_kbar = oracle.pool(k, w.seq_len, blk=FINE_BLOCK)
+    got_kbar = kbar.cpu().double().numpy()
+    assert np.abs(got_kbar - ref_kbar).max() <= POOL_RTOL * np.abs(ref_kbar).max()
+    items = sample_items(w, 10, seed=14)
+    c_np, w_np, got = cent.cpu().double().numpy(), wgt.cpu().double().numpy(), s.cpu().double().numpy()
+    worst = 0.0
+    for b, h, qb in items:
+        ref = oracle.score(c_np[b:b + 1, h:h + 1, qb:qb + 1], w_np[b:b + 1, h:h + 1, qb:qb + 1],
+                           got_kbar[b:b + 1, h:h + 1], p.softmax_scale)[0, 0, 0]
+        worst = max(worst, float((np.abs(got[b, h, qb] - ref) / ref).max()))
+    print(f"[high_res fine] pooled keys ok; scores of {len(items)} rows of 29700: max rel err {worst:.3g}")
+    assert worst <= SCORE_RTOL
+    del got, c_np, w_np
+    o_idx, o_cnt, o_w, _ = oracle.sample(s.cpu().numpy(), p.budget, 7)
+    assert compare_lists(idx, cnt, wt, o_idx, o_cnt, o_w) == 0
+    print(f"[high_res fine] lists bit-exact over {o_cnt.size} rows; mean kept {o_cnt.mean():.1f} of 29700")
+    a_items = sample_items(w, 10, seed=15)
+    ref = oracle.attend(q, k, v, w.seq_len, o_idx, o_cnt, o_w, items=a_items, scale=p.softmax_scale, kblk=FINE_BLOCK)
+    check_attention(gpu_rows(out, a_items), ref, w.dtype, "high_res fine attention sampled")
