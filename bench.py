@@ -160,7 +160,7 @@ def selection_diagnostics(w, p, qkv, ws, n_blocks: int, seed: int, softmax_scale
     if softmax_scale > 0:
         p = aba.plan(B, H, w.seq_len, w.head_dim, w.dtype, p.n_clusters, p.kmeans_iters, K, softmax_scale=softmax_scale)
     scores = aba.score(p, qd, kd, ws=ws)
-    idx, cnt, wt = aba.sample(p, scores, seed)
+    idx, cnt, wt = aba.sample(p, scores, seed, ws=ws)
     rng = np.random.default_rng(5)
     items = sorted({(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(NB))) for _ in range(4 * n_blocks)})
     items = items[:max(n_blocks, 32)]
@@ -253,7 +253,7 @@ def fine_leg(args, w, sets, density, coarse_plan, coarse_lists, dense_ms, n_diag
         aba.score(p, qd, kd, out=scores, ws=ws)
         if ev is not None:
             ev[1].record(stream)
-        aba.sample(p, scores, args.seed + i % len(sets), out=lists)
+        aba.sample(p, scores, args.seed + i % len(sets), out=lists, ws=ws)
         if ev is not None:
             ev[2].record(stream)
         aba.attend(p, qd, kd, vd, *lists, out=out, ws=ws)
@@ -279,7 +279,7 @@ def fine_leg(args, w, sets, density, coarse_plan, coarse_lists, dense_ms, n_diag
     for i in range(len(sets)):
         qd, kd, vd = sets[i]
         s_i = aba.score(p, qd, kd, ws=ws)
-        l_i = aba.sample(p, s_i, args.seed + i)
+        l_i = aba.sample(p, s_i, args.seed + i, ws=ws)
         idx, cnt, _ = (x.cpu().numpy() for x in l_i)
         kfl.append(kept_flops(p, cnt, idx))
         kept.append(float(cnt.mean()))
@@ -374,7 +374,7 @@ def run_sweep(args, w):
                 if (s - dense_steps) % plan_every == 0:
                     aba.score(p, qd, kd, out=scores, ws=ws)
                     e[1].record(stream)
-                    aba.sample(p, scores, args.seed + s, out=lists)
+                    aba.sample(p, scores, args.seed + s, out=lists, ws=ws)
                 else:
                     e[1].record(stream)
                 e[2].record(stream)
@@ -502,7 +502,7 @@ def main():
         aba.score(p, qd, kd, out=scores, ws=ws)
         if ev is not None:
             ev[1].record(stream)
-        aba.sample(p, scores, seed, out=lists)
+        aba.sample(p, scores, seed, out=lists, ws=ws)
         if ev is not None:
             ev[2].record(stream)
         if att is not None:
@@ -577,7 +577,7 @@ def main():
     for i in range(len(sets)):
         qd, kd, vd = sets[i]
         s_i = aba.score(p, qd, kd, ws=ws)
-        l_i = aba.sample(p, s_i, args.seed + i)
+        l_i = aba.sample(p, s_i, args.seed + i, ws=ws)
         idx, cnt, wt = (x.cpu().numpy() for x in l_i)
         kflops_sets.append(kept_flops(p, cnt, idx))
         dens_sets.append(float(cnt.mean() / p.n_key_blocks))

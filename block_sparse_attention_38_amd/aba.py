@@ -76,7 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     PP = ctypes.POINTER(PlanStruct)
     lib.aba_plan.argtypes = [PP, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32]
     lib.aba_score.argtypes = [PP, P, P, P, P, P, P, P, P]
-    lib.aba_sample.argtypes = [PP, P, u64, i32, i32, P, P, P, P]
+    lib.aba_sample.argtypes = [PP, P, u64, i32, i32, P, P, P, P, P]
     lib.aba_attend.argtypes = [PP, P, P, P, P, P, P, P, P, P]
     lib.aba_attend_full.argtypes = [PP, P, P, P, P, P, P]
     lib.aba_attend_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P]
@@ -182,7 +182,8 @@ def score(p: Plan, q: torch.Tensor, k: torch.Tensor, *, return_parts: bool = Fal
     return (out, cent, wgt, kbar) if return_parts else out
 
 
-def sample(p: Plan, scores: torch.Tensor, seed: int, *, out=None, head_offset: int = 0, batch_offset: int = 0):
+def sample(p: Plan, scores: torch.Tensor, seed: int, *, out=None, head_offset: int = 0, batch_offset: int = 0,
+           ws: torch.Tensor | None = None):
     """aba_sample: (idx [B,H,NB,cap] int32, cnt [B,H,NB] int32, w [B,H,NB,cap] float32).
     head_offset / batch_offset: global indices of this call's head 0 and batch entry 0
     when it covers a slice of a larger layer (the draws are addressed by them)."""
@@ -197,8 +198,10 @@ def sample(p: Plan, scores: torch.Tensor, seed: int, *, out=None, head_offset: i
     _need(idx, "idx", (B, H, NB, cap), torch.int32, dev)
     _need(cnt, "cnt", (B, H, NB), torch.int32, dev)
     _need(w, "w", (B, H, NB, cap), torch.float32, dev)
+    ws = _ws(p, ws, dev)
     _check(load_library().aba_sample(ctypes.byref(p.raw), _ptr(scores), int(seed) & 0xFFFFFFFFFFFFFFFF,
-                                     int(head_offset), int(batch_offset), _ptr(idx), _ptr(cnt), _ptr(w), _stream()))
+                                     int(head_offset), int(batch_offset), _ptr(idx), _ptr(cnt), _ptr(w), _ptr(ws),
+                                     _stream()))
     return idx, cnt, w
 
 
@@ -270,7 +273,7 @@ def layer(p: Plan, q, k, v, seed: int, *, ws=None):
     """One pass of the whole hot path: score -> sample -> attend."""
     ws = _ws(p, ws, q.device)
     s = score(p, q, k, ws=ws)
-    idx, cnt, w = sample(p, s, seed)
+    idx, cnt, w = sample(p, s, seed, ws=ws)
     return attend(p, q, k, v, idx, cnt, w, ws=ws), (s, idx, cnt, w)
 
 

@@ -26,10 +26,13 @@ hipError_t launch_kmeans(const void *q, const void *k, int dtype, int B, int H, 
 hipError_t launch_pool(const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB, float *kbar,
                        hipStream_t s);
 // Draws use the global indices h0 + h and b0 + b (the call may cover a slice of a layer).
+// ws: sample_workspace_bytes of device memory (rows of more than 8192 key blocks; else unused).
 hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int h0, int b0,
-                         int cap, int32_t *idx, int32_t *cnt, float *w, hipStream_t s);
+                         int cap, int32_t *idx, int32_t *cnt, float *w, void *ws, hipStream_t s);
 // Dynamic LDS the sampler needs for rows of NB key blocks and budget K.
 size_t sample_lds_bytes(int NB, int K);
+// Device bytes launch_sample needs at ws (0 unless rows hold more than 8192 key blocks).
+size_t sample_workspace_bytes(int B, int H, int NBq, int NB, int K);
 // 4-token key pooling, and the two-pass MFMA scoring of either key block size
 // (workspace: per-chunk partial statistics, per-centroid coefficients and the
 // split centroid tiles).

@@ -41,9 +41,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // the duration of the call: aba_score keeps centroids, weights and pooled keys
 // there when the caller does not ask for them (and, for 4-token key blocks, the
 // per-chunk softmax statistics of its two-pass scoring), aba_attend and
-// aba_attend_full the work order (and at head_dim 64 a V^T staging copy of v).
+// aba_attend_full the work order (and at head_dim 64 a V^T staging copy of v),
+// aba_sample the per-chunk totals, tops and counts of rows of more than 8192
+// key blocks.
 struct Workspace {
-    size_t cent, weight, kbar, fine, score_total, attend_total, total;
+    size_t cent, weight, kbar, fine, score_total, attend_total, sample_total, total;
 };
 
 Workspace workspace_layout(const aba_plan_t &p)
@@ -57,7 +59,9 @@ Workspace workspace_layout(const aba_plan_t &p)
     w.fine = w.kbar + align256(krows * p.head_dim * sizeof(float));
     w.score_total = w.fine + align256(aba::fine_score_workspace_bytes(p.batch, p.heads, p.n_blocks, p.n_key_blocks));
     w.attend_total = align256(aba::attend_workspace_bytes(p.dtype, p.batch, p.heads, p.seq_pad, p.head_dim));
+    w.sample_total = align256(aba::sample_workspace_bytes(p.batch, p.heads, p.n_blocks, p.n_key_blocks, p.budget));
     w.total = w.score_total > w.attend_total ? w.score_total : w.attend_total;
+    w.total = w.total > w.sample_total ? w.total : w.sample_total;
     return w;
 }
 
@@ -218,18 +222,22 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
 }
 
 aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, int32_t head_offset,
-                      int32_t batch_offset, int32_t *idx, int32_t *cnt, float *w, hipStream_t stream)
+                      int32_t batch_offset, int32_t *idx, int32_t *cnt, float *w, void *workspace,
+                      hipStream_t stream)
 {
     g_last_error.clear();
     aba_status st = check_plan(p);
     if (st != ABA_OK) return st;
     if (!scores || !idx || !cnt || !w) return fail(ABA_E_INVALID, "scores, idx, cnt and w must be non-NULL");
+    if (!workspace && workspace_layout(*p).sample_total > 0)
+        return fail(ABA_E_INVALID, "workspace of %llu bytes is required to sample rows of %d key blocks",
+                    (unsigned long long)p->workspace_bytes, p->n_key_blocks);
     if (head_offset < 0 || batch_offset < 0 || (int64_t)head_offset + p->heads > INT32_MAX ||
         (int64_t)batch_offset + p->batch > INT32_MAX)
         return fail(ABA_E_INVALID, "head_offset (%d) and batch_offset (%d) must be >= 0 and keep the global indices "
                     "below 2^31", head_offset, batch_offset);
     return hip_status(aba::launch_sample(scores, p->batch, p->heads, p->n_blocks, p->n_key_blocks, p->budget, seed,
-                                         head_offset, batch_offset, p->list_cap, idx, cnt, w, stream),
+                                         head_offset, batch_offset, p->list_cap, idx, cnt, w, workspace, stream),
                       "sample launch");
 }
 

@@ -126,12 +126,30 @@ __device__ __forceinline__ uint64_t ceil_ratio_shift32(uint64_t x, uint64_t r, d
 }
 
 // Whether block j (sigma - 1 = x) is kept: capped blocks always, any other iff
-// its draw is below theta = ceil((K - t) sigma 2^32 / R), i.e. draw R < x 2^32
-// with x = (K - t) sigma (exact 128-bit), or draw == 0 when K - t = 0.
-__device__ __forceinline__ bool keep_block(int j, uint32_t x, uint32_t draw, uint64_t cut, uint64_t Kt, uint64_t R)
+// its draw is below theta = ceil((K - t) sigma 2^32 / R), i.e. (the draw being
+// an integer) draw < y = (K - t) sigma 2^32 / R, or draw == 0 when K - t = 0.
+// The test runs in fp32 first: c = fl((K - t) 2^32 / R) once per row, y ~
+// fl(fl(x) c + c), whose relative error is below 3 x 2^-24 (about 1546 units
+// where y <= 2^33; beyond, the draw is below y anyway), and fl(draw) is within
+// 256 of the draw.  Outside a guard band of 4096 around y the fp32 comparison
+// decides; inside it the exact 128-bit test draw R < (K - t) sigma 2^32 does,
+// so the decision is exactly the integer one.
+constexpr float kKeepGuard = 4096.f;
+
+// c of keep_block for a row (0 when K - t = 0, which keep_block handles apart).
+__device__ __forceinline__ float keep_scale(uint64_t Kt, uint64_t R)
+{
+    return (Kt == 0 || R == 0) ? 0.f : (float)((double)Kt * 4294967296.0 / (double)R);
+}
+
+__device__ __forceinline__ bool keep_block(int j, uint32_t x, uint32_t draw, uint64_t cut, uint64_t Kt, uint64_t R,
+                                           float c)
 {
     if (pack_key(x, j) >= cut) return true;
     if (Kt == 0) return draw == 0;
+    const float d = (float)draw - fmaf((float)x, c, c);
+    if (d <= -kKeepGuard) return true;
+    if (d >= kKeepGuard) return false;
     return cmp_mul_shift32(draw, R, Kt * ((uint64_t)x + 1)) < 0;
 }
 
@@ -181,12 +199,24 @@ template <typename T> __device__ __forceinline__ T wave_incl_scan(T x, int lane)
     return x;
 }
 
+// Per-row result of the chunked path for rows of more than kChunkBlocks blocks
+// (below): the stopping point t, R and the cut key, or a request that the
+// whole-row kernel take the row.
+struct ChunkRowState {
+    uint64_t R, cut;
+    int32_t t, fallback;
+    int32_t pad[2];
+};
+
 template <int W, int STEPS>   // wavefronts per workgroup, quad steps per thread: rows of up to 256 W STEPS blocks
 __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__restrict__ scores, int H, int NBq, int NB,
                                                           int K, uint64_t seed, uint32_t h0, uint32_t b0, int cap, int P,
                                                           int32_t *__restrict__ idx, int32_t *__restrict__ cnt,
-                                                          float *__restrict__ w)
+                                                          float *__restrict__ w,
+                                                          const ChunkRowState *__restrict__ only)
 {
+    // with `only`, this kernel takes just the rows the chunked path handed over
+    if (only && !only[blockIdx.x].fallback) return;
     constexpr int NT = 64 * W;
     extern __shared__ __align__(16) char dyn[];
     uint64_t *top = reinterpret_cast<uint64_t *>(dyn);                          // P keys
@@ -681,6 +711,7 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
     }
     const uint64_t R = two_key ? R1 : r_s, cut = two_key ? cut1 : cut_s;
     const uint64_t Kt = (uint64_t)(K - t);   // >= 0 since t <= K
+    const float keep_c = keep_scale(Kt, R);
 
     // 4. keep decisions (4 bits per quad step), then the compaction in index order
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
@@ -697,7 +728,7 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 4 * q + e;
-                if (j < NB) nib |= (uint32_t)keep_block(j, xs[e], draw[e], cut, Kt, R) << e;
+                if (j < NB) nib |= (uint32_t)keep_block(j, xs[e], draw[e], cut, Kt, R, keep_c) << e;
             }
             bits[k >> 3] |= nib << (4 * (k & 7));
             mine += __popc(nib);
@@ -760,6 +791,377 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
         }
     }
     if (tid == 0) cnt[row] = kept_total < cap ? kept_total : cap;
+}
+
+// ---------------------------------------------------------------------------
+// Rows of more than kChunkBlocks blocks (4-token key blocks beyond 32K tokens:
+// 29,700 at the 118,800-token layer) are split into chunks of kChunkBlocks
+// consecutive blocks, one workgroup each, so that sigma always fits in
+// registers and the row is spread over several CUs.  The integer decisions are
+// exactly those of the whole-row kernel above:
+//   A  per chunk: sigma - 1 of its blocks, their total, and the chunk's top 64
+//      packed keys (the blocks at or above the 64th largest of the threads'
+//      maxima, ranked among themselves);
+//   B  per row: the total, the row's top 64 (a bitonic sort of the chunks'
+//      tops), and the stopping point t scanned over it (positions 1 .. 63):
+//      R and the cut key.  A row whose stopping point lies past the top 64
+//      (64 or more blocks capped), or a chunk with more than kCandMax blocks at
+//      or above its bound (many ties), is handed to the whole-row kernel;
+//   C  per chunk: the draws and keep decisions, the kept blocks compacted in
+//      index order into the row's list at the chunk's own offset c * kChunkBlocks
+//      (the list holds NB entries, so every chunk has room), with their weights;
+//   D  per row: the chunks' lists moved down to close the gaps, and the count.
+// Chunk c holds blocks [c kChunkBlocks, min(NB, (c + 1) kChunkBlocks)); thread
+// (wavefront w, lane l) of its workgroup (8 wavefronts) holds the quads
+// 256 w + 64 k + l, k = 0 .. 3, as the whole-row kernel lays them out.
+// ---------------------------------------------------------------------------
+constexpr int kChunkBlocks = 8192;
+constexpr int kChunkWaves = 8;                            // wavefronts per chunk workgroup
+constexpr int kChunkThreads = 64 * kChunkWaves;
+constexpr int kChunkSteps = kChunkBlocks / 4 / kChunkThreads;   // quad steps per thread
+constexpr int kMaxChunks = kMaxFineBlocks / kChunkBlocks;
+constexpr int kChunkTop = 64;
+
+__device__ __forceinline__ int chunk_quad(int wave, int k, int lane)
+{
+    return (kChunkBlocks / 4 / kChunkWaves) * wave + 64 * k + lane;
+}
+
+// sigma - 1 of this thread's blocks of chunk c (0 past the row), and the thread's
+// total, minimum and maximum over its valid blocks.
+__device__ __forceinline__ void load_chunk(const float *__restrict__ srow, int NB, int c, int wave, int lane,
+                                           uint4 xr[kChunkSteps], uint64_t &part, uint32_t &vmax)
+{
+    const int jb = c * kChunkBlocks;
+    float sv[kChunkSteps][4];
+    if ((NB & 3) == 0) {   // rows of whole quads start 16-byte aligned: one load per quad
+#pragma unroll
+        for (int k = 0; k < kChunkSteps; ++k) {
+            const int j0 = jb + 4 * chunk_quad(wave, k, lane);
+            const float4 v = j0 < NB ? *reinterpret_cast<const float4 *>(srow + j0) : make_float4(0, 0, 0, 0);
+            sv[k][0] = v.x;
+            sv[k][1] = v.y;
+            sv[k][2] = v.z;
+            sv[k][3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kChunkSteps; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = jb + 4 * chunk_quad(wave, k, lane) + e;
+                sv[k][e] = j < NB ? srow[j] : 0.f;
+            }
+    }
+    part = 0;
+    vmax = 0;
+#pragma unroll
+    for (int k = 0; k < kChunkSteps; ++k) {
+        uint32_t x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = jb + 4 * chunk_quad(wave, k, lane) + e;
+            x[e] = 0;
+            if (j < NB) {
+                const uint64_t sg = fixed_point(sv[k][e]);
+                part += sg;
+                x[e] = (uint32_t)(sg - 1);
+                vmax = max(vmax, x[e]);
+            }
+        }
+        xr[k] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+}
+
+// A: chunk totals and tops.  ctot [rows][nc], ctop [rows][nc][64] (descending,
+// 0-padded), cflag [rows][nc] (1: too many candidates for the direct ranking).
+__global__ __launch_bounds__(kChunkThreads) void sample_chunk_top_kernel(const float *__restrict__ scores, int NB, int nc,
+                                                               uint64_t *__restrict__ ctot, uint64_t *__restrict__ ctop,
+                                                               int32_t *__restrict__ cflag)
+{
+    __shared__ uint32_t lmax_s[kChunkThreads];
+    __shared__ uint64_t cand[kCandMax];
+    __shared__ uint64_t ured[kChunkWaves];
+    __shared__ uint32_t lo_s;
+    __shared__ int cand_n;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = blockIdx.x % nc;
+    const long row = blockIdx.x / nc;
+    const long item = row * nc + c;
+    const int jb = c * kChunkBlocks;
+    uint4 xr[kChunkSteps];
+    uint64_t part;
+    uint32_t vmax;
+    load_chunk(scores + row * NB, NB, c, wave, lane, xr, part, vmax);
+    part = wave_sum_t<uint64_t>(part);
+    if (lane == 0) ured[wave] = part;
+    lmax_s[tid] = vmax;
+    if (tid == 0) cand_n = 0;
+    __syncthreads();
+    // the 64th largest of the threads' maxima bounds the chunk's 64th largest
+    // value from below (threads without blocks report 0, which only lowers it)
+    if (wave == 0) {
+        uint32_t a[kChunkWaves], mn = 0xFFFFFFFFu, mx = 0;
+#pragma unroll
+        for (int i = 0; i < kChunkWaves; ++i) {
+            a[i] = lmax_s[lane + 64 * i];
+            mn = min(mn, a[i]);
+            mx = max(mx, a[i]);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+        }
+        // the answer lies in [mn, mx]: only the bits below their common prefix are searched
+        const uint32_t diff = mn ^ mx;
+        const int top = diff ? 31 - __clz(diff) : -1;
+        uint32_t v = top >= 0 ? (mx & ~((2u << top) - 1u)) : mx;
+        if (top == 31) v = 0;
+        for (int bit = top; bit >= 0; --bit) {
+            const uint32_t cnd = v | (1u << bit);
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < kChunkWaves; ++i) n += __popcll(__ballot(a[i] >= cnd));
+            if (n >= kChunkTop) v = cnd;
+        }
+        if (lane == 0) lo_s = v;
+    }
+    __syncthreads();
+    const uint32_t lo = lo_s;
+#pragma unroll
+    for (int k = 0; k < kChunkSteps; ++k) {
+        const int q = chunk_quad(wave, k, lane);
+        const uint32_t xs[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = jb + 4 * q + e;
+            const bool sel = j < NB && xs[e] >= lo;
+            const uint64_t bal = __ballot(sel);
+            if (bal) {
+                int base = 0;
+                if (lane == __builtin_ctzll(bal)) base = atomicAdd(&cand_n, __popcll(bal));
+                base = __shfl(base, __builtin_ctzll(bal), 64);
+                const int at = base + __popcll(bal & ((1ull << lane) - 1));
+                if (sel && at < kCandMax) cand[at] = pack_key(xs[e], j);
+            }
+        }
+    }
+    __syncthreads();
+    const int C = cand_n;
+    if (tid == 0) {
+        uint64_t t = 0;
+#pragma unroll
+        for (int i = 0; i < kChunkWaves; ++i) t += ured[i];
+        ctot[item] = t;
+        cflag[item] = C > kCandMax ? 1 : 0;
+    }
+    if (C > kCandMax) return;
+    uint64_t *out = ctop + item * kChunkTop;
+    for (int i = tid; i < C; i += kChunkThreads) {   // keys are distinct: each rank is taken once
+        const uint64_t key = cand[i];
+        int rank = 0;
+        for (int m = 0; m < C; ++m) rank += cand[m] > key;
+        if (rank < kChunkTop) out[rank] = key;
+    }
+    for (int i = C + tid; i < kChunkTop; i += kChunkThreads) out[i] = 0;
+}
+
+// B: one wavefront per row.
+__global__ __launch_bounds__(64) void sample_chunk_merge_kernel(const uint64_t *__restrict__ ctot,
+                                                                const uint64_t *__restrict__ ctop,
+                                                                const int32_t *__restrict__ cflag, int nc, int K,
+                                                                ChunkRowState *__restrict__ state)
+{
+    constexpr int kKeys = kMaxChunks * kChunkTop;
+    __shared__ uint64_t keys[kKeys];
+    const int lane = threadIdx.x;
+    const long row = blockIdx.x;
+    uint64_t total = 0;
+    int overflow = 0;
+    for (int c = 0; c < nc; ++c) {
+        total += ctot[row * nc + c];
+        overflow |= cflag[row * nc + c];
+    }
+    ChunkRowState st = {0, 0, 0, 1, {0, 0}};
+    if (overflow) {
+        if (lane == 0) state[row] = st;
+        return;
+    }
+    for (int i = lane; i < kKeys; i += 64) keys[i] = i < nc * kChunkTop ? ctop[row * nc * kChunkTop + i] : 0;
+    __syncthreads();
+    // bitonic sort, descending: each step compares kKeys / 2 pairs, two per lane
+    for (int size = 2; size <= kKeys; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = lane; i < kKeys / 2; i += 64) {
+                const int a = 2 * i - (i & (stride - 1)), b = a + stride;
+                const bool desc = (a & size) == 0;
+                const uint64_t x = keys[a], y = keys[b];
+                if ((x < y) == desc) {
+                    keys[a] = y;
+                    keys[b] = x;
+                }
+            }
+            __syncthreads();
+        }
+    // the stopping point: the first position p in 1 .. T-1 where (K - p) sigma_p
+    // < total - (sigma_0 + .. + sigma_{p-1}); none and T = K: t = K
+    const int T = min(K, kChunkTop);
+    const uint64_t key = keys[lane];
+    const uint64_t sg = lane < T ? (key >> kKeyIdxBits) + 1 : 0;
+    const uint64_t incl = wave_incl_scan<uint64_t>(sg, lane);
+    const bool fail = lane >= 1 && lane < T && (uint64_t)(K - lane) * sg < total - (incl - sg);
+    const uint64_t fb = __ballot(fail);
+    const int tt = fb ? __builtin_ctzll(fb) : T;
+    const uint64_t r_inc = __shfl(incl, tt - 1, 64);
+    const uint64_t cut = __shfl(key, tt - 1, 64);
+    if (lane == 0) {
+        if (tt < T || T == K) {
+            st.R = total - r_inc;
+            st.cut = cut;
+            st.t = tt;
+            st.fallback = 0;
+        }
+        state[row] = st;
+    }
+}
+
+// C: draws, keep decisions and the chunk's list at offset c * kChunkBlocks.
+__global__ __launch_bounds__(kChunkThreads) void sample_chunk_draw_kernel(const float *__restrict__ scores, int H, int NBq, int NB,
+                                                                int nc, int K, uint64_t seed, uint32_t h0, uint32_t b0,
+                                                                int cap, const ChunkRowState *__restrict__ state,
+                                                                int32_t *__restrict__ ccnt, int32_t *__restrict__ idx,
+                                                                float *__restrict__ w)
+{
+    // the first kChunkStage kept blocks (index and sigma - 1), whose weights all
+    // threads then form over consecutive positions: a weight takes an fp64
+    // division, and formed where each block is found it would run, divergent,
+    // for almost every block slot of almost every wavefront
+    constexpr int kChunkStage = 2048;
+    __shared__ int32_t stage_j[kChunkStage];
+    __shared__ uint32_t stage_x[kChunkStage];
+    __shared__ int wtot[kChunkWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = blockIdx.x % nc;
+    const long row = blockIdx.x / nc;
+    const ChunkRowState st = state[row];
+    if (st.fallback) return;   // uniform over the workgroup
+    const int qb = (int)(row % NBq), h = (int)((row / NBq) % H), b = (int)(row / ((long)NBq * H));
+    const int jb = c * kChunkBlocks;
+    uint4 xr[kChunkSteps];
+    uint64_t part;
+    uint32_t vmax;
+    load_chunk(scores + row * NB, NB, c, wave, lane, xr, part, vmax);
+    const uint64_t R = st.R, cut = st.cut, Kt = (uint64_t)(K - st.t);
+    const float keep_c = keep_scale(Kt, R);
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    uint32_t bits = 0;   // 4 bits per quad step
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < kChunkSteps; ++k) {
+        const int q = jb / 4 + chunk_quad(wave, k, lane);   // the row's quad index
+        if (4 * q < NB) {
+            const uint4 r = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)qb, h0 + (uint32_t)h, b0 + (uint32_t)b),
+                                          k0, k1);
+            const uint32_t draw[4] = {r.x, r.y, r.z, r.w};
+            const uint32_t xs[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+            uint32_t nib = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * q + e;
+                if (j < NB) nib |= (uint32_t)keep_block(j, xs[e], draw[e], cut, Kt, R, keep_c) << e;
+            }
+            bits |= nib << (4 * k);
+            mine += __popc(nib);
+        }
+    }
+    mine = wave_sum_t<int>(mine);
+    if (lane == 0) wtot[wave] = mine;
+    __syncthreads();
+    int running = 0, kept = 0;
+#pragma unroll
+    for (int i = 0; i < kChunkWaves; ++i) {
+        if (i < wave) running += wtot[i];
+        kept += wtot[i];
+    }
+    const double inv_r = R > 0 ? 1.0 / (double)R : 0.0;
+    int32_t *irow = idx + row * cap + jb;
+    float *wrow = w + row * cap + jb;
+#pragma unroll
+    for (int k = 0; k < kChunkSteps; ++k) {
+        const uint32_t nib = (bits >> (4 * k)) & 15u;
+        const int cn = __popc(nib);
+        const int incl = wave_incl_scan<int>(cn, lane);
+        int pos = running + incl - cn;
+        running += __shfl(incl, 63, 64);
+        const int q = jb / 4 + chunk_quad(wave, k, lane);
+        const uint32_t xs[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if ((nib >> e) & 1u) {
+                const int j = 4 * q + e;
+                if (pos < kChunkStage) {
+                    stage_j[pos] = j;
+                    stage_x[pos] = xs[e];
+                } else {   // a chunk keeping more than the stage holds: formed here
+                    irow[pos] = j;
+                    wrow[pos] = kept_weight(j, xs[e], cut, Kt, R, inv_r);
+                }
+                ++pos;
+            }
+        }
+    }
+    __syncthreads();
+    const int staged = kept < kChunkStage ? kept : kChunkStage;
+    for (int p = tid; p < staged; p += kChunkThreads) {
+        const int j = stage_j[p];
+        irow[p] = j;
+        wrow[p] = kept_weight(j, stage_x[p], cut, Kt, R, inv_r);
+    }
+    if (tid == 0) ccnt[row * nc + c] = kept;
+}
+
+// D: close the gaps between the chunks' lists (each moves down, in order, a
+// tile at a time: a tile's destination never reaches a later tile's source).
+__global__ __launch_bounds__(256) void sample_chunk_compact_kernel(const ChunkRowState *__restrict__ state,
+                                                                   const int32_t *__restrict__ ccnt, int nc, int cap,
+                                                                   int32_t *__restrict__ idx, int32_t *__restrict__ cnt,
+                                                                   float *__restrict__ w)
+{
+    constexpr int kPer = 4;
+    const int tid = threadIdx.x;
+    const long row = blockIdx.x;
+    if (state[row].fallback) return;
+    int32_t *irow = idx + row * cap;
+    float *wrow = w + row * cap;
+    int off = ccnt[row * nc];
+    for (int c = 1; c < nc; ++c) {
+        const int n = ccnt[row * nc + c], src = c * kChunkBlocks;
+        if (off != src) {
+            for (int i0 = 0; i0 < n; i0 += 256 * kPer) {
+                int32_t jv[kPer];
+                float wv[kPer];
+#pragma unroll
+                for (int r = 0; r < kPer; ++r) {
+                    const int i = i0 + r * 256 + tid;
+                    jv[r] = i < n ? irow[src + i] : 0;
+                    wv[r] = i < n ? wrow[src + i] : 0.f;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < kPer; ++r) {
+                    const int i = i0 + r * 256 + tid;
+                    if (i < n) {
+                        irow[off + i] = jv[r];
+                        wrow[off + i] = wv[r];
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        off += n;
+    }
+    if (tid == 0) cnt[row] = off < cap ? off : cap;
 }
 
 // ---------------------------------------------------------------------------
@@ -912,6 +1314,7 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(const float *__restric
     }
     const uint64_t R = total - pre_t;
     const uint64_t Kt = (uint64_t)(K - t);
+    const float keep_c = keep_scale(Kt, R);
     const double inv_r = R > 0 ? 1.0 / (double)R : 0.0;
 
     // draws, keep decisions and the compaction in index order
@@ -927,7 +1330,7 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(const float *__restric
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 4 * q + e;
-                if (j < NB) nib |= (uint32_t)keep_block(j, x[k][e], draw[e], cut, Kt, R) << e;
+                if (j < NB) nib |= (uint32_t)keep_block(j, x[k][e], draw[e], cut, Kt, R, keep_c) << e;
             }
         }
         const int c = __popc(nib);
@@ -965,8 +1368,37 @@ size_t sample_lds_bytes(int NB, int K)
     return 8 * (size_t)topk_pad(NB, K);
 }
 
+// Workspace of the chunked path (rows of more than kChunkBlocks blocks with a
+// budget below the row length): chunk totals, tops, flags and counts, and the
+// per-row state.
+struct ChunkWs {
+    size_t tot, top, flag, cnt, state, total;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static ChunkWs chunk_ws_layout(long rows, int NB)
+{
+    const size_t nc = (size_t)((NB + kChunkBlocks - 1) / kChunkBlocks), items = (size_t)rows * nc;
+    ChunkWs l;
+    l.tot = 0;
+    l.top = l.tot + align256(items * sizeof(uint64_t));
+    l.flag = l.top + align256(items * kChunkTop * sizeof(uint64_t));
+    l.cnt = l.flag + align256(items * sizeof(int32_t));
+    l.state = l.cnt + align256(items * sizeof(int32_t));
+    l.total = l.state + align256((size_t)rows * sizeof(ChunkRowState));
+    return l;
+}
+
+static bool chunked_rows(int NB, int K, int cap) { return NB > kChunkBlocks && K < NB && cap >= NB; }
+
+size_t sample_workspace_bytes(int B, int H, int NBq, int NB, int K)
+{
+    return chunked_rows(NB, K, NB) ? chunk_ws_layout((long)B * H * NBq, NB).total : 0;
+}
+
 hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int K, uint64_t seed, int h0, int b0,
-                         int cap, int32_t *idx, int32_t *cnt, float *w, hipStream_t s)
+                         int cap, int32_t *idx, int32_t *cnt, float *w, void *ws, hipStream_t s)
 {
     const long rows = (long)B * H * NBq;
     const dim3 grid((unsigned)rows), block(256);
@@ -980,6 +1412,23 @@ hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int
     const size_t lds = sample_lds_bytes(NB, K);
     if (lds > kSampleLdsLimit) return hipErrorInvalidValue;
     const int P = topk_pad(NB, K);
+    // rows of more than kChunkBlocks blocks: the chunked path, the whole-row
+    // kernel only for the rows it hands over
+    const bool chunked = chunked_rows(NB, K, cap) && ws != nullptr;
+    const ChunkRowState *only = nullptr;
+    if (chunked) {
+        const int nc = (NB + kChunkBlocks - 1) / kChunkBlocks;
+        const ChunkWs l = chunk_ws_layout(rows, NB);
+        char *base = static_cast<char *>(ws);
+        uint64_t *ctot = reinterpret_cast<uint64_t *>(base + l.tot);
+        uint64_t *ctop = reinterpret_cast<uint64_t *>(base + l.top);
+        int32_t *cflag = reinterpret_cast<int32_t *>(base + l.flag);
+        ChunkRowState *state = reinterpret_cast<ChunkRowState *>(base + l.state);
+        sample_chunk_top_kernel<<<dim3((unsigned)(rows * nc)), dim3(kChunkThreads), 0, s>>>(scores, NB, nc, ctot, ctop,
+                                                                                         cflag);
+        sample_chunk_merge_kernel<<<grid, dim3(64), 0, s>>>(ctot, ctop, cflag, nc, K, state);
+        only = state;
+    }
     // as few quad steps per thread as the row needs: 1 to 8 on 4 wavefronts, 8 or 16 on 8
     auto launch = [&](auto kernel, int threads) {
         // allow more than the default dynamic LDS (a host-side attribute of the current device);
@@ -988,7 +1437,16 @@ hipError_t launch_sample(const float *scores, int B, int H, int NBq, int NB, int
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         kernel<<<grid, dim3(threads), lds, s>>>(scores, H, NBq, NB, K, seed, (uint32_t)h0, (uint32_t)b0, cap, P, idx,
-                                                cnt, w);
+                                                cnt, w, only);
+        hipError_t r = hipGetLastError();
+        if (r != hipSuccess || !chunked) return r;
+        const int nc = (NB + kChunkBlocks - 1) / kChunkBlocks;
+        const ChunkWs l = chunk_ws_layout(rows, NB);
+        char *base = static_cast<char *>(ws);
+        int32_t *ccnt = reinterpret_cast<int32_t *>(base + l.cnt);
+        sample_chunk_draw_kernel<<<dim3((unsigned)(rows * nc)), dim3(kChunkThreads), 0, s>>>(
+            scores, H, NBq, NB, nc, K, seed, (uint32_t)h0, (uint32_t)b0, cap, only, ccnt, idx, w);
+        sample_chunk_compact_kernel<<<grid, dim3(256), 0, s>>>(only, ccnt, nc, cap, idx, cnt, w);
         return hipGetLastError();
     };
     if (NB <= 256 * 4 * 1) return launch(&sample_topk_kernel<4, 1>, 256);

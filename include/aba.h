@@ -90,8 +90,8 @@ typedef struct aba_plan {
     int32_t key_block;      /* tokens per key block: ABA_BLOCK or ABA_FINE_BLOCK */
     int32_t n_key_blocks;   /* NBk = ceil(N / key_block) */
     int32_t reserved;
-    uint64_t workspace_bytes; /* device scratch for aba_score, aba_attend and
-                                 aba_attend_full;
+    uint64_t workspace_bytes; /* device scratch for aba_score, aba_sample, aba_attend
+                                 and aba_attend_full;
                                  every call uses it from offset 0 and only while it
                                  runs, so one buffer serves all calls ordered on a
                                  stream (calls that overlap in time need their own) */
@@ -149,6 +149,11 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
  *   idx    : out, int32 [B,H,NB,list_cap], kept key blocks in ascending order
  *   cnt    : out, int32 [B,H,NB], number kept (>= 1)
  *   w      : out, float32 [B,H,NB,list_cap], weights of the listed blocks
+ *   workspace : at least p->workspace_bytes of device memory; required when
+ *               rows hold more than 8192 key blocks (4-token key blocks beyond
+ *               32768 tokens) and the budget is below the row length: those
+ *               rows are split into chunks whose totals, tops and counts it
+ *               keeps.  May be NULL otherwise.
  * Entries at or past cnt are left unspecified.  The lists depend only on
  * (scores, budget, seed) and the global (batch, head) indices: every draw is
  * addressable by (seed, b, h, query block, key block), so a call over a slice
@@ -156,7 +161,8 @@ aba_status aba_score(const aba_plan_t *p, const void *q, const void *k, float *s
  * Offsets with head_offset + H or batch_offset + B above 2^31 - 1 ->
  * ABA_E_INVALID. */
 aba_status aba_sample(const aba_plan_t *p, const float *scores, uint64_t seed, int32_t head_offset,
-                      int32_t batch_offset, int32_t *idx, int32_t *cnt, float *w, hipStream_t stream);
+                      int32_t batch_offset, int32_t *idx, int32_t *cnt, float *w, void *workspace,
+                      hipStream_t stream);
 
 /* Block-sparse attention over a sampling plan (SIP and kernel paragraphs).  For
  * each valid query i of query block b, with the kept list (j, w_j) of key

@@ -103,7 +103,7 @@ def test_entry_points_reject_null_pointers_before_launch(aba):
     pp = ctypes.byref(p.raw)
     nul = None
     assert lib.aba_score(pp, nul, nul, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
-    assert lib.aba_sample(pp, nul, 1, 0, 0, nul, nul, nul, nul) == aba.ABA_E_INVALID
+    assert lib.aba_sample(pp, nul, 1, 0, 0, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
     assert lib.aba_attend(pp, nul, nul, nul, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
     assert lib.aba_attend_full(pp, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
     assert b"NULL" in lib.aba_last_error()
@@ -117,7 +117,7 @@ def test_sample_rejects_offsets_outside_the_counter_range(aba, h0, b0):
     lib = aba.load_library()
     p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 2)
     fake = ctypes.c_void_p(1)
-    assert lib.aba_sample(ctypes.byref(p.raw), fake, 1, h0, b0, fake, fake, fake, None) == aba.ABA_E_INVALID
+    assert lib.aba_sample(ctypes.byref(p.raw), fake, 1, h0, b0, fake, fake, fake, None, None) == aba.ABA_E_INVALID
     assert b"offset" in lib.aba_last_error()
 
 
@@ -155,6 +155,18 @@ def test_tampered_plan_is_rejected(aba):
     p = aba.plan(1, 2, 1024, 64, "f32", 8, 10, 64, key_block=4)
     p.raw.key_block = 128       # fields of the other key block size
     assert lib.aba_attend_full(ctypes.byref(p.raw), fake, fake, fake, fake, None, None) == aba.ABA_E_INVALID
+
+
+def test_long_rows_sample_needs_a_workspace(aba):
+    """Rows of more than 8192 4-token key blocks are sampled in chunks whose state
+    lives in the workspace; shorter rows need none."""
+    lib = aba.load_library()
+    fake = ctypes.c_void_p(1)
+    p = aba.plan(1, 2, 118800, 128, "bf16", 8, 10, 2368, key_block=4)
+    assert lib.aba_sample(ctypes.byref(p.raw), fake, 1, 0, 0, fake, fake, fake, None, None) == aba.ABA_E_INVALID
+    assert b"workspace" in lib.aba_last_error()
+    short = aba.plan(1, 2, 32760, 128, "bf16", 8, 10, 832, key_block=4)   # 8190 blocks: one workgroup per row
+    assert short.workspace_bytes < p.workspace_bytes
 
 
 @pytest.mark.parametrize("key_block", [128, 4])
