@@ -89,6 +89,77 @@ def traffic_entry(key_block: int = 128):
     return rec.get("bytes_per_launch")
 
 
+def summarize_traffic(fetch_dir: str, write_dir: str, key_block: int, commands: list):
+    """Turn two rocprofv3 counter runs of ``bench.py --copy-calibration`` (one with
+    FETCH_SIZE, one with WRITE_SIZE, KiB per dispatch) into the per-kernel HBM
+    bytes of the 32K-token layer: each counter is scaled by what it reads for the
+    run's plain 1 GiB device copy.  Writes profiles/hbm_traffic_single_layer*.md
+    and the aba_attend record that traffic_entry() reads (tied to the hash of
+    attend.hip)."""
+    import csv
+    import glob
+    import re
+
+    def load(d, counter):
+        per, grid = {}, {}
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = re.sub(r"\(.*", "", r["Kernel_Name"].replace("aba::(anonymous namespace)::", "aba::"))
+                per.setdefault(name, []).append(float(r["Counter_Value"]))
+                grid[name] = r.get("Grid_Size", "")
+        return per, grid
+
+    fetch, grid = load(fetch_dir, "FETCH_SIZE")
+    write, _ = load(write_dir, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+
+    def copy_kib(per):   # the calibration copy: the largest copy dispatch of the run
+        vals = [v for n, vs in per.items() if "copyBuffer" in n for v in vs]
+        return max(vals) if vals else 0.0
+
+    f_copy, w_copy = copy_kib(fetch), copy_kib(write)
+    if f_copy < gib_kib / 4 or w_copy < gib_kib / 4:
+        raise SystemExit("no 1 GiB calibration copy in the counter runs (run bench.py with --copy-calibration)")
+    fs, ws = gib_kib / f_copy, gib_kib / w_copy
+    sfx = "" if key_block == 128 else "_4token"
+    rows = []
+    kernels = {}
+    attend_kernels = ("aba::order_kernel",
+                      "void aba::attend_bf16_kernel<128, false>" if key_block == 128 else "void aba::attend_fine_kernel<128>")
+    for name in sorted(fetch, key=lambda n: -sum(fetch[n]) / len(fetch[n])):
+        if "copyBuffer" in name:
+            continue
+        fk = sum(fetch[name]) / len(fetch[name])
+        wk = sum(write.get(name, [0.0])) / max(1, len(write.get(name, [])))
+        rows.append(f"| `{name}` | {grid.get(name, '')} | {fk:.0f} | {wk:.0f} | {fk * 1024 * fs / 1e6:.1f} | "
+                    f"{wk * 1024 * ws / 1e6:.1f} |")
+        if name in attend_kernels:
+            kernels[name] = {"read_bytes": fk * 1024 * fs, "write_bytes": wk * 1024 * ws}
+    if len(kernels) != 2:
+        raise SystemExit(f"the counter runs lack the aba_attend kernels {attend_kernels}")
+    md = [f"# HBM traffic per launch, single 32K layer, {key_block}-token key blocks", "",
+          "Counter passes (each its own run, from /tmp with TMPDIR=/tmp; R = repository root), then the summary:", "",
+          "```", *commands, "```", "",
+          f"Scale factors from the plain 1 GiB device copy in the same runs (`--copy-calibration`): FETCH_SIZE reads "
+          f"{f_copy:.0f} KiB for 1 GiB read (x{fs:.4f}), WRITE_SIZE reads {w_copy:.0f} KiB for 1 GiB written "
+          f"(x{ws:.4f}).", "",
+          "| kernel | grid | FETCH_SIZE KiB (raw) | WRITE_SIZE KiB (raw) | read MB (scaled) | written MB (scaled) |",
+          "|---|---|---|---|---|---|", *rows]
+    md_path = os.path.join(ROOT, "profiles", f"hbm_traffic_single_layer{sfx}.md")
+    open(md_path, "w").write("\n".join(md) + "\n")
+    rd = sum(k["read_bytes"] for k in kernels.values())
+    wr = sum(k["write_bytes"] for k in kernels.values())
+    rec = {"call": "aba_attend", "key_block": key_block, "kernels": kernels, "workload": "single_layer",
+           "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr, "fetch_scale": fs, "write_scale": ws,
+           "attend_src_sha256_16": source_digest(ATTEND_SRC),
+           "source": os.path.relpath(md_path, ROOT)}
+    json.dump(rec, open(TRAFFIC_FILES[key_block], "w"), indent=1)
+    print(f"wrote {os.path.relpath(md_path, ROOT)} and {os.path.relpath(TRAFFIC_FILES[key_block], ROOT)}: "
+          f"aba_attend reads {rd / 1e9:.3f} GB, writes {wr / 1e9:.3f} GB per call")
+
+
 def cpu_baseline(w, p, q, k, v, seed: int, target_s: float):
     """The oracle (as it stands) on a bounded sample: whole heads when it is fast
     enough, else evenly spaced query blocks of head 0."""
@@ -458,7 +529,15 @@ def main():
                     help="key block size of the timed layer (4: the page's fine-grained selection)")
     ap.add_argument("--no-fine", action="store_true",
                     help="skip the 4-token key block measurement that follows the 128-token one")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
+                         "with --copy-calibration into profiles/ for --key-block")
+    ap.add_argument("--command", action="append", default=[],
+                    help="with --summarize-traffic: a command line that produced the counters (recorded verbatim)")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.key_block, args.command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer shards over heads with no exchange, and no multi-GPU "
