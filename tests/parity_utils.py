@@ -20,7 +20,7 @@ ATT_RTOL_BF16 = 2e-2
 ATT_RTOL_F32 = 1e-4
 CENT_RTOL = 1e-5           # centroids, relative to the block's largest |centroid|
 POOL_RTOL = 1e-5           # pooled keys, relative to the layer's largest |kbar|
-NEAR_TIE = 1e-4            # k-means blocks whose two best distances are closer are not compared
+NEAR_TIE = 1e-5            # k-means blocks whose two best distances are closer (relative gap) are not compared
 
 
 def device():
