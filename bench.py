@@ -73,11 +73,11 @@ def source_digest(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_entry(key_block: int = 128):
+def traffic_entry(key_block: int = 128, path: str = None):
     """HBM traffic per attend call (bytes) of the 32K bf16 layer from the committed
     rocprofv3 counter runs for that key block size, if the kernel source has not
     changed since they were taken."""
-    path = TRAFFIC_FILES.get(key_block)
+    path = path or TRAFFIC_FILES.get(key_block)
     if path is None or not os.path.exists(path):
         return None
     try:
@@ -89,7 +89,7 @@ def traffic_entry(key_block: int = 128):
     return rec.get("bytes_per_launch")
 
 
-def summarize_traffic(fetch_dir: str, write_dir: str, key_block: int, commands: list):
+def summarize_traffic(fetch_dir: str, write_dir: str, key_block: int, commands: list, out_dir: str = None):
     """Turn two rocprofv3 counter runs of ``bench.py --copy-calibration`` (one with
     FETCH_SIZE, one with WRITE_SIZE, KiB per dispatch) into the per-kernel HBM
     bytes of the 32K-token layer: each counter is scaled by what it reads for the
@@ -147,17 +147,19 @@ def summarize_traffic(fetch_dir: str, write_dir: str, key_block: int, commands: 
           f"(x{ws:.4f}).", "",
           "| kernel | grid | FETCH_SIZE KiB (raw) | WRITE_SIZE KiB (raw) | read MB (scaled) | written MB (scaled) |",
           "|---|---|---|---|---|---|", *rows]
-    md_path = os.path.join(ROOT, "profiles", f"hbm_traffic_single_layer{sfx}.md")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    md_path = os.path.join(out_dir, f"hbm_traffic_single_layer{sfx}.md")
+    json_path = os.path.join(out_dir, os.path.basename(TRAFFIC_FILES[key_block]))
     open(md_path, "w").write("\n".join(md) + "\n")
     rd = sum(k["read_bytes"] for k in kernels.values())
     wr = sum(k["write_bytes"] for k in kernels.values())
     rec = {"call": "aba_attend", "key_block": key_block, "kernels": kernels, "workload": "single_layer",
            "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr, "fetch_scale": fs, "write_scale": ws,
            "attend_src_sha256_16": source_digest(ATTEND_SRC),
-           "source": os.path.relpath(md_path, ROOT)}
-    json.dump(rec, open(TRAFFIC_FILES[key_block], "w"), indent=1)
-    print(f"wrote {os.path.relpath(md_path, ROOT)} and {os.path.relpath(TRAFFIC_FILES[key_block], ROOT)}: "
-          f"aba_attend reads {rd / 1e9:.3f} GB, writes {wr / 1e9:.3f} GB per call")
+           "source": "profiles/" + os.path.basename(md_path)}
+    json.dump(rec, open(json_path, "w"), indent=1)
+    print(f"wrote {md_path} and {json_path}: aba_attend reads {rd / 1e9:.3f} GB, writes {wr / 1e9:.3f} GB per call")
+    return rec
 
 
 def cpu_baseline(w, p, q, k, v, seed: int, target_s: float):
