@@ -24,6 +24,7 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -531,6 +532,10 @@ def main():
                     help="key block size of the timed layer (4: the page's fine-grained selection)")
     ap.add_argument("--no-fine", action="store_true",
                     help="skip the 4-token key block measurement that follows the 128-token one")
+    ap.add_argument("--head-shard", default=None, metavar="I/N",
+                    help="time one GPU's share of the layer sharded by heads over N GPUs: heads "
+                         "[I*H/N, (I+1)*H/N), drawn with their global head offset (no 4-token leg, diagnostics "
+                         "or CPU baseline)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
                          "with --copy-calibration into profiles/ for --key-block")
@@ -556,10 +561,24 @@ def main():
     density = w.densities[0] if args.density is None else args.density
     dev = torch.device("cuda:0")
     log(f"[bench] workload {w.name}: {w.description}; density {density}")
+    # One GPU's share of a layer sharded by heads: the inputs are the layer's own
+    # (generated whole, then sliced), and the draws use the global head index.
+    h0, shard = 0, None
+    if args.head_shard:
+        si, sn = (int(x) for x in args.head_shard.split("/"))
+        if not (sn >= 1 and 0 <= si < sn and w.heads >= sn):
+            raise SystemExit(f"--head-shard {args.head_shard}: need 0 <= I < N <= heads ({w.heads})")
+        h0, h1 = si * w.heads // sn, (si + 1) * w.heads // sn
+        shard = {"shard": f"{si}/{sn}", "layer_heads": w.heads, "head_offset": h0}
+        args.no_fine = args.no_diagnostics = args.no_cpu_baseline = True
+        log(f"[bench] head shard {si}/{sn}: heads {h0}..{h1 - 1} of {w.heads}")
     # Several input sets, used in turn: one set's q and k (201 MB at the single
     # layer) would otherwise stay in the 256 MB MALL from one step to the next.
     t0 = time.perf_counter()
     host_sets = [synth.make_inputs(w, seed=1001 + 10 * i) for i in range(args.input_sets)]
+    if shard:
+        host_sets = [tuple(x[:, h0:h1].contiguous() for x in hs) for hs in host_sets]
+        w = dataclasses.replace(w, heads=h1 - h0)
     sets = [tuple(x.to(dev) for x in hs) for hs in host_sets]
     log(f"[bench] {len(sets)} input sets ready in {time.perf_counter() - t0:.1f} s")
 
@@ -583,7 +602,7 @@ def main():
         aba.score(p, qd, kd, out=scores, ws=ws)
         if ev is not None:
             ev[1].record(stream)
-        aba.sample(p, scores, seed, out=lists, ws=ws)
+        aba.sample(p, scores, seed, out=lists, ws=ws, head_offset=h0)
         if ev is not None:
             ev[2].record(stream)
         if att is not None:
@@ -658,7 +677,7 @@ def main():
     for i in range(len(sets)):
         qd, kd, vd = sets[i]
         s_i = aba.score(p, qd, kd, ws=ws)
-        l_i = aba.sample(p, s_i, args.seed + i, ws=ws)
+        l_i = aba.sample(p, s_i, args.seed + i, ws=ws, head_offset=h0)
         idx, cnt, wt = (x.cpu().numpy() for x in l_i)
         kflops_sets.append(kept_flops(p, cnt, idx))
         dens_sets.append(float(cnt.mean() / p.n_key_blocks))
@@ -712,7 +731,7 @@ def main():
             "workload": w.name, "batch": B, "heads": H, "seq_len": w.seq_len, "seq_pad": p.seq_pad,
             "head_dim": D, "grid": list(w.grid), "density": density, "budget_blocks": p.budget,
             "clusters": p.n_clusters, "kmeans_iters": p.kmeans_iters, "block": 128, "key_block": p.key_block,
-            "seed": args.seed, "input_sets": len(sets),
+            "seed": args.seed, "input_sets": len(sets), **(shard or {}),
         },
         "stages_ms": {"score": score_ms, "sample": sample_ms, "attend": attend_ms},
         "attend_ms_timed_region": attend_timed_ms,
@@ -745,7 +764,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attend_tflops / PEAK_BF16_TFLOPS,
-            "traffic": traffic_entry(p.key_block) if w.name == "single_layer" and w.dtype == "bf16" else None,
+            "traffic": traffic_entry(p.key_block) if w.name == "single_layer" and w.dtype == "bf16" and not shard else None,
         },
         "diagnostics": diagnostics,
         "fine_key_blocks": None,
