@@ -232,7 +232,8 @@ def selection_diagnostics(w, p, qkv, ws, n_blocks: int, seed: int, softmax_scale
     qd, kd, vd = qkv
     B, H, NB, K = p.batch, p.heads, p.n_blocks, p.budget
     if softmax_scale > 0:
-        p = aba.plan(B, H, w.seq_len, w.head_dim, w.dtype, p.n_clusters, p.kmeans_iters, K, softmax_scale=softmax_scale)
+        p = aba.plan(B, H, w.seq_len, w.head_dim, w.dtype, p.n_clusters, p.kmeans_iters, K, softmax_scale=softmax_scale,
+                     key_block=p.key_block)
     scores = aba.score(p, qd, kd, ws=ws)
     idx, cnt, wt = aba.sample(p, scores, seed, ws=ws)
     rng = np.random.default_rng(5)
@@ -247,8 +248,8 @@ def selection_diagnostics(w, p, qkv, ws, n_blocks: int, seed: int, softmax_scale
         return np.take_along_axis(mass, top, axis=1).sum(axis=1)
 
     ibcs = top_k_mass(scores.double().cpu().numpy())
-    p1 = aba.plan(B, H, w.seq_len, w.head_dim, w.dtype, 1, p.kmeans_iters, K,
-                  softmax_scale=p.softmax_scale)                                    # one cluster: mean-pool scorer
+    p1 = aba.plan(B, H, w.seq_len, w.head_dim, w.dtype, 1, p.kmeans_iters, K, softmax_scale=p.softmax_scale,
+                  key_block=p.key_block)                                          # one cluster: mean-pool scorer
     meanpool = top_k_mass(aba.score(p1, qd, kd, ws=aba.workspace(p1, qd.device)).double().cpu().numpy())
     idx_h, cnt_h, wt_h = (x.cpu().numpy() for x in (idx, cnt, wt))
     kept, ht = [], []
@@ -407,6 +408,9 @@ def fine_leg(args, w, sets, density, coarse_plan, coarse_lists, dense_ms, n_diag
         "sip_kept_mass": {"128_token": sip_mass(mass_c, coarse_lists[1]), "4_token": sip_mass(mass_f, set_lists[0][1])},
         "attention_rms_err_over_rms_v": {"128_token": errs["128_token"], "4_token": errs["4_token"]},
         "dense_output_rms_over_rms_v": errs["dense_scale"],
+        # the peaked variant (softmax scale 1) at 4-token granularity: ideal, IBCS, mean-pool and sampled
+        # selections, and sampled against hard top-K lists, as the 128-token diagnostics report them
+        "peaked": selection_diagnostics(w, p, sets[0], ws, n_diag, args.seed, softmax_scale=1.0),
     }
     log(f"[bench] 4-token diagnostics: {json.dumps(res['diagnostics'])}")
     return res
