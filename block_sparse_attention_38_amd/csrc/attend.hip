@@ -277,8 +277,8 @@ __device__ __forceinline__ Entry list_entry(const int32_t *lrow, const float *wr
 // works through one contiguous range of slots (its L2 then sees neighbouring
 // query blocks of one head); otherwise slots go round-robin over the XCDs, so
 // that all of them work on the same few heads at once.  The second keeps the
-// K and V in use inside the MALL when eight heads' worth (one per XCD) would not
-// fit there (see attend_xcd_ranges).
+// K and V in use inside the MALL when the layer's K and V do not fit there as a
+// whole (see attend_xcd_ranges).
 __device__ __forceinline__ int mapped_slot(bool xcd_ranges)
 {
     return xcd_ranges ? xcd_contiguous_id(blockIdx.x, gridDim.x) : (int)blockIdx.x;
@@ -1196,14 +1196,17 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(const float *__restrict
 
 }  // namespace
 
-// XCD-contiguous ranges of the order while the K and V of eight heads (one per
-// XCD) fit in the 256 MB MALL, round-robin slots otherwise (measured: 32K-token
-// heads run ~10% faster with the ranges, 119K-token heads ~10% faster without).
-static bool attend_xcd_ranges(int N_pad, int D)
+// XCD-contiguous ranges of the order while the layer's K and V fit in the
+// 256 MB MALL as a whole, round-robin slots otherwise.  Measured with the same
+// lists: 12 heads of 32K tokens (201 MB of K and V) run 9% faster with the
+// ranges; 40 such heads (672 MB) 12% faster round-robin, and 24 heads of 119K
+// tokens (1.5 GB) ~10% faster round-robin: once the layer does not fit, eight
+// XCDs on eight different heads lose the MALL, all XCDs on the same heads keep it.
+static bool attend_xcd_ranges(int B, int H, int N_pad, int D)
 {
     constexpr double kMallBytes = 256.0 * 1024 * 1024;
-    const double kv_per_head = 2.0 * N_pad * D * sizeof(uint16_t);
-    return 8.0 * kv_per_head <= kMallBytes;
+    const double kv_bytes = 2.0 * B * H * N_pad * D * sizeof(uint16_t);
+    return kv_bytes <= kMallBytes;
 }
 
 // Workspace of the bf16 attention calls: the V^T copy (head_dim 64 only; at 128
@@ -1232,13 +1235,13 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
         if (D == 128) {
             attend_bf16_kernel<128, full><<<grid, dim3(kThreads), 0, s>>>(
                 (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, cnt, w, order, (uint16_t *)out, N,
-                N_pad, NB, cap, sl2, attend_xcd_ranges(N_pad, D));
+                N_pad, NB, cap, sl2, attend_xcd_ranges(B, H, N_pad, D));
         } else {
             vt_kernel<64><<<dim3((unsigned)((long)B * H * (N_pad / kSub))), block, 0, s>>>((const uint16_t *)v, N, N_pad,
                                                                                         vt);
             attend_bf16_kernel<64, full><<<grid, dim3(kThreads), 0, s>>>(
                 (const uint16_t *)q, (const uint16_t *)k, vt, idx, cnt, w, order, (uint16_t *)out, N, N_pad, NB, cap, sl2,
-                attend_xcd_ranges(N_pad, D));
+                attend_xcd_ranges(B, H, N_pad, D));
         }
     } else if (dtype == kF32 && D == 64) {
         attend_f32_kernel<64, full><<<grid, block, 0, s>>>((const float *)q, (const float *)k, (const float *)v, idx,
@@ -1261,7 +1264,7 @@ hipError_t launch_attend_fine(const void *q, const void *k, const void *v, int d
         order_kernel<<<dim3(8), dim3(kOrderThreads), 0, s>>>(cnt, G, cap, kFineSub, order);
         attend_fine_kernel<128><<<dim3((unsigned)G), dim3(kThreads), 0, s>>>(
             (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, cnt, w, order, (uint16_t *)out, N,
-            N_pad, NBq, NBk, cap, sl2, attend_xcd_ranges(N_pad, D));
+            N_pad, NBq, NBk, cap, sl2, attend_xcd_ranges(B, H, N_pad, D));
     } else if (dtype == kF32 && D == 64) {
         attend_f32_fine_kernel<64><<<dim3((unsigned)G), dim3(256), 0, s>>>((const float *)q, (const float *)k,
                                                                           (const float *)v, idx, cnt, w, (float *)out,
