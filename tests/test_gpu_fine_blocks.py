@@ -27,7 +27,10 @@ RAGGED = Workload("ragged_bf16", 1, 3, 128, "bf16", (3, 10, 43), 16, (0.25,),
                   description="1290 tokens: 11 query blocks, 323 key blocks, the last with 2 valid tokens")
 ONE_TAIL = Workload("one_token_tail", 1, 2, 128, "bf16", (1, 1, 257), 4, (0.5,),
                     description="257 tokens: the last key block holds a single token")
-SMALL = [TINY, RAGGED, ONE_TAIL]
+BATCH2 = Workload("batch2_bf16", 2, 2, 128, "bf16", (2, 9, 37), 16, (0.3,),
+                  description="batch 2, 666 tokens: 6 query blocks (the last with 26 valid), 167 key blocks "
+                              "(the last with 2 valid tokens)")
+SMALL = [TINY, RAGGED, ONE_TAIL, BATCH2]
 
 
 @pytest.fixture(scope="module")

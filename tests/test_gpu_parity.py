@@ -26,7 +26,9 @@ RAGGED64 = Workload("ragged_bf16_d64", 2, 2, 64, "bf16", (2, 9, 50), 16, (0.3,),
                     description="batch 2, 900 tokens: 8 blocks, the last with 4 valid")
 ONE_TAIL = Workload("one_token_tail", 1, 2, 128, "bf16", (1, 1, 257), 4, (0.5,),
                     description="257 tokens: the last block holds a single token")
-SMALL = [TINY, RAGGED, RAGGED64, ONE_TAIL]
+BATCH2 = Workload("batch2_bf16", 2, 2, 128, "bf16", (2, 9, 37), 16, (0.3,),
+                  description="batch 2, head_dim 128, 666 tokens: 6 blocks, the last with 26 valid")
+SMALL = [TINY, RAGGED, RAGGED64, ONE_TAIL, BATCH2]
 
 
 @pytest.fixture(scope="module")
