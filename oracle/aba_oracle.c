@@ -74,8 +74,19 @@ static const float *row_ptr(const float *base, int H, long n_pad, int D, int b, 
     return base + (((long)b * H + h) * n_pad + t) * (long)D;
 }
 
+static int same_centroid(const double *cent, int D, int m1, int m2)
+{
+    for (int d = 0; d < D; ++d)
+        if (cent[(long)m1 * D + d] != cent[(long)m2 * D + d]) return 0;
+    return 1;
+}
+
 /* Assignment step: a[i] = argmin_m |x_i - c_m|^2, ties to the smallest m.
- * Returns the smallest relative gap (d2 - d1) / d2 over the rows (1 if C == 1). */
+ * Returns the smallest relative gap (d2 - d1) / d2 over the rows, where d2 is
+ * the nearest centroid that differs from the chosen one (1 if there is none).
+ * Copies of the chosen centroid (a block with fewer rows than clusters starts
+ * with repeated rows) tie with it exactly in any precision and so do not make
+ * the assignment fragile; a different centroid at the same distance does. */
 static double assign_rows(const float *x, long ld, int n, int D, int C, const double *cent, int *a)
 {
     double min_gap = 1.0;
@@ -92,12 +103,14 @@ static double assign_rows(const float *x, long ld, int n, int D, int C, const do
                 second = best;
                 best = dist;
                 bm = m;
+            } else if (dist == best && same_centroid(cent, D, m, bm)) {
+                /* a copy of the chosen centroid */
             } else if (dist < second) {
                 second = dist;
             }
         }
         a[i] = bm;
-        if (C > 1) {
+        if (second < INFINITY) {
             double gap = second > 0.0 ? (second - best) / second : 0.0;
             if (gap < min_gap) min_gap = gap;
         }

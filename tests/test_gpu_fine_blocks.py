@@ -30,7 +30,9 @@ ONE_TAIL = Workload("one_token_tail", 1, 2, 128, "bf16", (1, 1, 257), 4, (0.5,),
 BATCH2 = Workload("batch2_bf16", 2, 2, 128, "bf16", (2, 9, 37), 16, (0.3,),
                   description="batch 2, 666 tokens: 6 query blocks (the last with 26 valid), 167 key blocks "
                               "(the last with 2 valid tokens)")
-SMALL = [TINY, RAGGED, ONE_TAIL, BATCH2]
+ONE_TOKEN = Workload("one_token", 1, 2, 128, "bf16", (1, 1, 1), 1, (0.5,), tiles=1,
+                     description="a single token: one query block, one 4-token key block with one valid token")
+SMALL = [TINY, RAGGED, ONE_TAIL, BATCH2, ONE_TOKEN]
 
 
 @pytest.fixture(scope="module")

@@ -130,6 +130,32 @@ def test_kmeans_invariants_and_monotone_objective(oracle_mod):
             assert np.allclose((w[:, None] * cent).sum(0), x.astype(np.float64).mean(0), rtol=0, atol=1e-12)
 
 
+def test_kmeans_with_fewer_rows_than_clusters(oracle_mod):
+    """n < C distinct rows: the strided initial centroids x[floor(m n / C)] repeat
+    rows, every row sits at distance 0 from its own copies and goes to the first
+    of them, m = ceil(r C / n), so each such cluster holds one row (weight 1/n),
+    the others stay empty and keep their copy, and nothing moves in later rounds.
+    Copies tie exactly, so the smallest gap to a different centroid is 1."""
+    rng = np.random.default_rng(8)
+    for n, D in [(1, 128), (2, 64), (3, 16), (4, 128), (5, 64), (7, 32)]:
+        x = rng.normal(size=(n, D)).astype(np.float32)
+        cent, w, a, gap = oracle_mod.kmeans_block(x, C=8, T=10)
+        first = [-(-r * 8 // n) for r in range(n)]                # ceil(r C / n)
+        assert a.tolist() == first
+        ref_w = np.zeros(8)
+        ref_w[first] = 1.0 / n
+        assert np.array_equal(w, ref_w)
+        for m in range(8):
+            assert np.array_equal(cent[m], x[m * n // 8].astype(np.float64))
+        assert gap == 1.0
+    # a row exactly halfway between two different centroids is a true tie: it
+    # goes to the smaller index, and the gap says the assignment is fragile (0)
+    x = np.zeros((3, 4), np.float32)
+    x[0, 0], x[1, 0] = -1.0, 1.0                             # initial centroids rows 0 and 1; row 2 halfway
+    _, w, a, gap = oracle_mod.kmeans_block(x, C=2, T=1)
+    assert a.tolist() == [0, 1, 0] and gap == 0.0 and np.array_equal(w, [2 / 3, 1 / 3])
+
+
 def test_kmeans_recovers_separated_blobs(oracle_mod):
     rng = np.random.default_rng(6)
     D = 32
