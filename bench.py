@@ -16,8 +16,9 @@ step time.  Printed as one JSON line, with the roofline of the dominant call
 (aba_attend, measured with HIP events on the stream it runs on), untimed
 selection diagnostics (dense attention mass kept by the ideal, IBCS, mean-pool
 and sampled selections on sampled query blocks, and the attention error of the
-sampled lists against hard top-K lists), and the CPU oracle timed on a bounded
-sample of the same workload.
+sampled lists against hard top-K lists), the rate the bf16 matrix cores sustain
+on register operands alone (the practical ceiling beside the quoted peak), and
+the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload single_layer]
 """
@@ -53,6 +54,33 @@ TRAFFIC_FILES = {128: os.path.join(ROOT, "profiles", "attend_single_layer_traffi
 
 def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
+
+
+def mfma_rate(iters: int, reps: int = 3) -> dict:
+    """Sustained bf16 matrix-core rate (aba_mfma_rate: MFMAs on register operands
+    only, two wavefronts per SIMD), on random operands and on zeros; the median
+    of the reps after one untimed call each."""
+    dev = torch.device("cuda:0")
+    out = torch.empty(aba.MFMA_RATE_THREADS, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, random in (("random", True), ("zero", False)):
+        aba.mfma_rate(iters, random, out)
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            aba.mfma_rate(iters, random, out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        res[f"{name}_tflops"] = iters * aba.MFMA_RATE_FLOP_PER_ITER / (float(np.median(ms)) * 1e-3) / 1e12
+        res[f"{name}_ms"] = ms
+    res["iters"] = iters
+    res["random_frac_of_peak"] = res["random_tflops"] / PEAK_BF16_TFLOPS
+    log(f"[bench] sustained bf16 MFMA (register operands only): random {res['random_tflops']:.0f} TFLOP/s "
+        f"({res['random_frac_of_peak']:.3f} of peak), zeros {res['zero_tflops']:.0f} TFLOP/s")
+    return res
 
 
 def kept_flops(p, cnt: np.ndarray, idx: np.ndarray) -> float:
@@ -545,7 +573,19 @@ def main():
                          "with --copy-calibration into profiles/ for --key-block")
     ap.add_argument("--command", action="append", default=[],
                     help="with --summarize-traffic: a command line that produced the counters (recorded verbatim)")
+    ap.add_argument("--no-mfma-rate", action="store_true",
+                    help="skip the sustained matrix-core rate measurement (aba_mfma_rate) reported beside the roofline")
+    ap.add_argument("--mfma-rate-iters", type=int, default=10000,
+                    help="rounds of the matrix-core rate loop per timed call (2^30 flop each; 10^4: ~6 ms)")
+    ap.add_argument("--mfma-rate-only", action="store_true",
+                    help="only measure the sustained matrix-core rate and print it (for its counter profile)")
     args = ap.parse_args()
+    if args.mfma_rate_only:
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"mfma_sustained": mfma_rate(args.mfma_rate_iters)}), flush=True)
+        return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.key_block, args.command)
         return
@@ -777,6 +817,11 @@ def main():
     if not fine_main and not args.no_fine and w.dtype == "bf16":
         result["fine_key_blocks"] = fine_leg(args, w, sets, density, p, set_lists[0], dense_ms, args.diag_blocks,
                                              not args.no_diagnostics)
+    if not args.no_mfma_rate and w.dtype == "bf16":
+        rate = mfma_rate(args.mfma_rate_iters)
+        result["mfma_sustained"] = rate
+        result["roofline"]["sustained_peak"] = rate["random_tflops"]
+        result["roofline"]["frac_of_sustained"] = attend_tflops / rate["random_tflops"]
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         q, k, v = host_sets[0]

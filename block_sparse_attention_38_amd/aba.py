@@ -13,6 +13,7 @@ Steps (AB-Attention page, section "Три приёма AB-Attention"):
     attend_full(plan, q, k, v)     dense attention                 -> aba_attend_full
     attend_noalloc(plan, ...)      aba_attend without a workspace  -> aba_attend_noalloc
     block_mass(plan, q, k, items)  attention mass per key block    -> aba_block_mass (diagnostic)
+    mfma_rate(iters, random, out)  sustained matrix-core rate     -> aba_mfma_rate (measurement)
 """
 from __future__ import annotations
 
@@ -56,7 +57,11 @@ class PlanStruct(ctypes.Structure):
 
 
 EXPORTS = ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full", "aba_attend_noalloc",
-           "aba_block_mass", "aba_last_error", "aba_version")
+           "aba_block_mass", "aba_mfma_rate", "aba_last_error", "aba_version")
+# aba_mfma_rate: workgroups x threads of its checksum buffer, and floating-point
+# operations per round of its loop (512 x 4 wavefronts x 16 MFMAs x 32*32*16*2)
+MFMA_RATE_THREADS = 512 * 256
+MFMA_RATE_FLOP_PER_ITER = 512 * 4 * 16 * 32 * 32 * 16 * 2
 # Query blocks (B * H * NB) the static scratch of aba_attend_noalloc holds.
 NOALLOC_MAX_QUERY_BLOCKS = (1 << 20) // 4
 
@@ -81,8 +86,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.aba_attend_full.argtypes = [PP, P, P, P, P, P, P]
     lib.aba_attend_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P]
     lib.aba_block_mass.argtypes = [PP, P, P, P, ctypes.c_int32, P, P]
+    lib.aba_mfma_rate.argtypes = [i32, i32, P, P]
     for name in ("aba_plan", "aba_score", "aba_sample", "aba_attend", "aba_attend_full", "aba_attend_noalloc",
-                 "aba_block_mass"):
+                 "aba_block_mass", "aba_mfma_rate"):
         getattr(lib, name).restype = ctypes.c_int
     lib.aba_last_error.argtypes = []
     lib.aba_last_error.restype = ctypes.c_char_p
@@ -267,6 +273,15 @@ def block_mass(p: Plan, q, k, items) -> torch.Tensor:
     _check(load_library().aba_block_mass(ctypes.byref(p.raw), _ptr(q), _ptr(k), _ptr(it), it.shape[0], _ptr(mass),
                                          _stream()))
     return mass
+
+
+def mfma_rate(iters: int, random: bool, out: torch.Tensor) -> None:
+    """aba_mfma_rate: iters x MFMA_RATE_FLOP_PER_ITER bf16 matrix-core operations on
+    register operands (random bits or zeros), on the current stream; out is a
+    float32 cuda tensor of MFMA_RATE_THREADS elements.  Timing is the caller's."""
+    if not (out.is_cuda and out.dtype == torch.float32 and out.numel() >= MFMA_RATE_THREADS):
+        raise ValueError(f"out must be a float32 cuda tensor of {MFMA_RATE_THREADS} elements")
+    _check(load_library().aba_mfma_rate(int(iters), 1 if random else 0, _ptr(out), _stream()))
 
 
 def layer(p: Plan, q, k, v, seed: int, *, ws=None):

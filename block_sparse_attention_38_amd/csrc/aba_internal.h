@@ -54,6 +54,11 @@ hipError_t launch_block_mass(const void *q, const void *k, int dtype, int B, int
                              int kb, float scale, const int32_t *items, int n_items, float *mass, hipStream_t s);
 // Device bytes launch_attend needs at ws (the work order, and at head_dim 64 the V^T copy; 0 for fp32).
 size_t attend_workspace_bytes(int dtype, int B, int H, int N_pad, int D);
+// Sustained bf16 MFMA rate: kMfmaRateBlocks workgroups of 256 threads, each
+// wavefront 16 * iters MFMAs on register operands (random bits or zeros); out
+// holds one float per thread.
+constexpr int kMfmaRateBlocks = 512;
+hipError_t launch_mfma_rate(int iters, int random, float *out, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Device helpers

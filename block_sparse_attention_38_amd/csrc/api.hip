@@ -1,7 +1,7 @@
 // api.hip -- the C ABI of libaba.so (declared in include/aba.h): argument
 // validation, workspace layout and kernel launches.  Host code only; every
-// computation runs in the kernels of kmeans.hip, pool_score.hip, sample.hip and
-// attend.hip.
+// computation runs in the kernels of kmeans.hip, pool_score.hip, fine_score.hip,
+// sample.hip, attend.hip, diag.hip and calib.hip.
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -321,6 +321,13 @@ aba_status aba_block_mass(const aba_plan_t *p, const void *q, const void *k, con
     return hip_status(aba::launch_block_mass(q, k, p->dtype, p->batch, p->heads, p->seq_len, p->seq_pad, p->head_dim,
                                              p->n_blocks, p->key_block, p->softmax_scale, items, n_items, mass, stream),
                       "block_mass launch");
+}
+
+aba_status aba_mfma_rate(int32_t iters, int32_t random, float *out, hipStream_t stream)
+{
+    if (iters < 1 || iters > 1000000) return fail(ABA_E_INVALID, "aba_mfma_rate: iters %d outside 1 .. 10^6", iters);
+    if (!out) return fail(ABA_E_INVALID, "aba_mfma_rate: out is null");
+    return hip_status(aba::launch_mfma_rate(iters, random, out, stream), "aba_mfma_rate launch");
 }
 
 const char *aba_last_error(void) { return g_last_error.c_str(); }

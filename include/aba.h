@@ -217,6 +217,21 @@ aba_status aba_attend_noalloc(const aba_plan_t *p, const void *q, const void *k,
 aba_status aba_block_mass(const aba_plan_t *p, const void *q, const void *k, const int32_t *items, int32_t n_items,
                           float *mass, hipStream_t stream);
 
+/* Measurement support, not a step of the layer: a loop of bf16 matrix-core
+ * products with register operands and no memory traffic, on every compute unit
+ * (512 workgroups of 256 threads: two wavefronts per SIMD, the occupancy of the
+ * attention kernels).  Each wavefront runs iters x 16 v_mfma_f32_32x32x16_bf16,
+ * so one call performs iters x 2^30 floating-point operations (512 x 4 x 16 x
+ * 32768 per round).  Timed by the caller on `stream`, it gives the rate the
+ * matrix cores sustain: with random != 0 on operands with random bits (the
+ * power drawn, hence the shader clock the chip holds, depends on operand
+ * toggling), with random == 0 on zeros.  The bf16 peak of 2.5 PFLOP/s is quoted
+ * at a 2.4 GHz clock; a kernel's measured rate can be set against both.
+ *   iters : 1 .. 10^6 (else ABA_E_INVALID)
+ *   out   : device float32 [512 * 256], a checksum per thread (keeps the
+ *           products from being discarded); contents are not meaningful */
+aba_status aba_mfma_rate(int32_t iters, int32_t random, float *out, hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * pointer stays valid until the thread's next aba_* call. */
 const char *aba_last_error(void);

@@ -110,6 +110,14 @@ def test_entry_points_reject_null_pointers_before_launch(aba):
     assert lib.aba_attend_full(None, nul, nul, nul, nul, nul, nul) == aba.ABA_E_INVALID
 
 
+def test_mfma_rate_rejects_bad_arguments_before_launch(aba):
+    lib = aba.load_library()
+    assert lib.aba_mfma_rate(0, 1, ctypes.c_void_p(16), None) == aba.ABA_E_INVALID
+    assert lib.aba_mfma_rate(1000001, 1, ctypes.c_void_p(16), None) == aba.ABA_E_INVALID
+    assert lib.aba_mfma_rate(10, 1, None, None) == aba.ABA_E_INVALID
+    assert b"null" in lib.aba_last_error()
+
+
 @pytest.mark.parametrize("h0,b0", [(-1, 0), (0, -1), (2**31 - 2, 0), (0, 2**31 - 1)])
 def test_sample_rejects_offsets_outside_the_counter_range(aba, h0, b0):
     """The draws are addressed by the global (batch, head) indices b0 + b and h0 + h;
