@@ -184,6 +184,8 @@ __global__ __launch_bounds__(256) void kmeans_kernel(const T *__restrict__ q, in
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
 {
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
     // sum the keys (the query loads above stay in flight)
     if (kb == kBlock) {
-        const int c = tid % DCH, g = tid / DCH;
+        const int g = tid / DCH;
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
@@ -530,6 +532,333 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 at head_dim 128: the same rounds with the block's query rows kept in LDS
+// row-major, as they arrive.  Direct buffer->LDS loads copy the 128 rows (no
+// registers, no transposing pass, q read once); the assignment's B fragments
+// are plain 16-byte LDS reads of those rows, and the update's X operand comes
+// from transposing LDS reads (ds_read_b64_tr_b16), so the update's one-hot
+// operand takes its queries in the order the transposing reads deliver them.
+// The key rows for the pooling are loaded right after the queries and summed
+// only after the rounds: their latency and bandwidth overlap the rounds, and no
+// barrier inside the rounds waits for them (the barriers are bare s_barriers
+// after an LDS wait; a workgroup fence would drain every load in flight).
+// The arithmetic is that of kmeans_mfma_kernel; only the order in which the
+// update's MFMA adds its (exact) products differs, so sums may differ in the
+// last place.
+// ---------------------------------------------------------------------------
+template <int D, int KB>   // KB: tokens per key block of the pooling (128 or 4)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void kmeans_lds_kernel(
+    const uint16_t *__restrict__ q, int N, int N_pad, int NB, int C, int T_iters, float *__restrict__ cent_out,
+    float *__restrict__ w_out, const uint16_t *__restrict__ k, int NBk, float *__restrict__ kbar)
+{
+    static_assert(KB == kBlock || KB == kFineBlock, "128-token or 4-token key blocks");
+    static_assert(D == 128, "a direct load of 1024 bytes fills 4 query rows of 256 bytes");
+    constexpr int KS = D / 16;          // k-steps over the head dimension
+    constexpr int DCH = D / 8;          // 16-byte chunks per row
+    constexpr int kPitch = D * 2;       // bytes per query row in LDS
+    // X: row r (query) holds its D bf16 values, chunk c stored at c ^ xswz(r) with
+    // xswz(r) = 4 (r % 4) + (r / 4) % 4: the 16 rows of a 16-lane phase of the
+    // assignment's 16-byte reads land on 16 different chunks, and so do the 4
+    // rows x 4 chunks of a 32-lane phase of the update's transposing reads
+    __shared__ __align__(16) char xs[kBlock * kPitch];
+    __shared__ uint4 cs_s[24 * DCH];                  // split centroids, as in kmeans_mfma_kernel
+    __shared__ float cn_part[4][kMaxClusters];
+    constexpr int kFlagPitch = kBlock + 8;
+    __shared__ __align__(16) uint8_t flag_s[kMaxClusters * kFlagPitch];
+    __shared__ int cnt_s[4][kMaxClusters];
+    __shared__ int chg_s[4];
+
+    const int row = blockIdx.x;                           // (b*H + h) * NB + query block
+    const int qb = row % NB;
+    const long bh = row / NB;
+    const int n = min(kBlock, N - qb * kBlock);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, half = lane >> 5;
+    auto xrow = [&](int r) __attribute__((always_inline)) { return xs + r * kPitch; };
+    auto xswz = [](int r) __attribute__((always_inline)) { return 4 * (r & 3) + ((r >> 2) & 3); };
+    auto xchunk = [&](int r, int c) __attribute__((always_inline)) { return 16 * (c ^ xswz(r)); };
+
+    // ---- the block's query rows into LDS: wavefront w copies rows 32w .. 32w+31,
+    // four per load; the row offset rides in the range-checked per-lane offset,
+    // so rows >= N (past the descriptor) arrive as zeros
+    {
+        const int4v rq = head_rsrc(q + bh * N_pad * D, N * D * 2);
+        // load t fills LDS rows 32w + 4t .. +3: lane L row 32w + 4t + L / 16, chunk
+        // position L % 16, which holds logical chunk (L % 16) ^ xswz(row)
+        const int r4 = lane >> 4;
+        const int voff = (qb * kBlock + 32 * wave + r4) * kPitch;
+        char *dst = xrow(32 * wave);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            load_lds16(rq, voff + 4 * t * kPitch + 16 * ((lane & 15) ^ (4 * r4 + (t & 3))), 0, dst + 1024 * t);
+    }
+    // ---- the keys of the block's 128 tokens (one 128-token key block, or 32
+    // 4-token ones), eight 16-byte rows per thread, issued now and summed after
+    // the rounds; rows >= N read as zeros (range-checked buffer loads, always
+    // issued, so the count of loads in flight below is exact)
+    constexpr int G = 256 / DCH;           // 128-token key block: thread (group g, chunk c), rows g + G i
+    constexpr int RPT = kBlock / G;
+    constexpr int kFine = kBlock / kFineBlock;
+    constexpr int IPT = kFine * DCH / 256; // 4-token key blocks: (block, chunk) items per thread
+    static_assert(RPT == 8 && RPT == IPT * kFineBlock, "eight key loads per thread in both cases");
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(k + bh * N_pad * D), (short)0, N * D * 2, 0x00020000);
+    uint4 kraw[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        int r, c;
+        if (KB == kBlock) {
+            c = tid % DCH;
+            r = tid / DCH + G * i;
+        } else {
+            const int it = i / kFineBlock, item = tid + 256 * it;
+            c = item % DCH;
+            r = kFineBlock * (item / DCH) + i % kFineBlock;
+        }
+        kraw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rk, (qb * kBlock + r) * kPitch + 16 * c, 0, 0));
+    }
+    // the query copies are in LDS once at most the eight key loads remain in flight
+    wait_loads_and_sync<RPT>();
+
+    // this wavefront's 32 queries: the B fragments of the assignment product are
+    // read from LDS in every round (holding them would leave too few registers
+    // for the key rows kept across the rounds)
+    const int my_q = wave * 32 + l32;
+    const bool qv = my_q < n;
+
+    // strided initial centroids q[floor(m n / C)] (bf16: the high part is the row
+    // itself, the other two zero) and |c_m|^2, as in kmeans_mfma_kernel
+    if (tid < kMaxClusters * DCH) {
+        const int m = tid / DCH, c = tid % DCH;
+        uint4 hi = make_uint4(0, 0, 0, 0);
+        if (m < C) {
+            const int r = m * n / C;
+            hi = *reinterpret_cast<const uint4 *>(xrow(r) + xchunk(r, c));
+        }
+        const uint32_t *h = reinterpret_cast<const uint32_t *>(&hi);
+        float nrm = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x0 = bf16_lo(h[e]), x1 = bf16_hi(h[e]);
+            nrm = fmaf(x0, x0, nrm);
+            nrm = fmaf(x1, x1, nrm);
+        }
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp) {
+            const int r = 8 * pp + m;
+            cs_s[r * DCH + (c ^ (r & (DCH - 1)))] = pp == 0 ? hi : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int o = 1; o < DCH; o <<= 1) nrm += __shfl_xor(nrm, o, 64);
+        if (c == 0) {
+            cn_part[0][m] = nrm;
+            cn_part[1][m] = cn_part[2][m] = cn_part[3][m] = 0.f;
+        }
+    }
+    wait_loads_lds_and_sync<RPT>();
+    uint16_t *cs16 = reinterpret_cast<uint16_t *>(cs_s);
+    auto part_at = [&](int p, int m, int d) __attribute__((always_inline)) -> uint16_t & {
+        const int rr = 8 * p + m;
+        return cs16[(rr * DCH + ((d >> 3) ^ (rr & (DCH - 1)))) * 8 + (d & 7)];
+    };
+    auto centroid = [&](int m, int d) __attribute__((always_inline)) {
+        return (bf16_bits_to_f32(part_at(0, m, d)) + bf16_bits_to_f32(part_at(1, m, d))) +
+               bf16_bits_to_f32(part_at(2, m, d));
+    };
+
+    // Transposing reads of X for the update (the lane layout of the attention
+    // kernel's V operand): lane (l32, half) of wavefront w receives dimension
+    // 32w + l32 of queries 16ks + 4half + j (first read, rows row0 + 16ks) and
+    // 16ks + 8 + 4half + j (second read, rows row0 + 8 + 16ks), j = 0..3; a
+    // k-step of 16 rows keeps xswz, the 8 rows between the two reads do not.
+    int x_rd0, x_rd1;
+    {
+        const int g = lane >> 4, m = lane & 15, row0 = 4 * (g >> 1) + (m >> 2);
+        const int chunk = 4 * wave + 2 * (g & 1) + ((m & 3) >> 1);
+        x_rd0 = row0 * kPitch + xchunk(row0, chunk) + 8 * (m & 1);
+        x_rd1 = (row0 + 8) * kPitch + xchunk(row0 + 8, chunk) + 8 * (m & 1);
+    }
+
+    const int rounds = T_iters > 0 ? T_iters : 1;
+    int prev = -1;
+    for (int it = 0; it < rounds; ++it) {
+        // ---- assignment: dots^T = C_split X^T for this wavefront's 32 queries
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int ar = l32 < 24 ? l32 : l32 - 8;
+            const uint4 a = cs_s[ar * DCH + ((2 * ks + half) ^ (ar & (DCH - 1)))];
+            const uint4 x = *reinterpret_cast<const uint4 *>(xrow(my_q) + xchunk(my_q, 2 * ks + half));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, x),
+                                                          acc, 0, 0, 0);
+        }
+        float bd = INFINITY;
+        int bm = 4 * half;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = 4 * half + j;
+            const float dot = acc[j] + acc[4 + j] + acc[8 + j];
+            const float cn2 = cn_part[0][m] + cn_part[1][m] + cn_part[2][m] + cn_part[3][m];
+            const float dist = m < C ? fmaf(-2.f, dot, cn2) : INFINITY;
+            if (dist < bd) {
+                bd = dist;
+                bm = m;
+            }
+        }
+        const float od = __shfl_xor(bd, 32, 64);
+        const int om = __shfl_xor(bm, 32, 64);
+        if (od < bd || (od == bd && om < bm)) {
+            bd = od;
+            bm = om;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = 4 * half + j;
+            flag_s[m * kFlagPitch + my_q] = (qv && bm == m) ? (uint8_t)0x80 : (uint8_t)0;
+        }
+#pragma unroll
+        for (int m = 0; m < kMaxClusters; ++m) {
+            const int c = __popcll(__ballot(half == 0 && qv && bm == m));
+            if (lane == 0) cnt_s[wave][m] = c;
+        }
+        const bool changed = __ballot(half == 0 && qv && bm != prev) != 0;
+        prev = bm;
+        if (lane == 0) chg_s[wave] = changed ? 1 : 0;
+        wait_loads_lds_and_sync<RPT>();
+        const bool any_changed = (chg_s[0] | chg_s[1] | chg_s[2] | chg_s[3]) != 0;
+        if (T_iters == 0 || !any_changed) break;   // initial-centroid weights, or converged
+
+        // ---- update: sums = onehot^T X, wavefront w owns dims [32w, 32w + 32)
+        {
+            floatx16 sum;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[r] = 0.f;
+            const int d = wave * 32 + l32;
+            // A operand row l32 is cluster l32 % 8; its k-step entries are the
+            // flags of queries 16ks + 4half + j and 16ks + 8 + 4half + j, the
+            // order in which the transposing reads hand over X
+            const uint8_t *flag_row = flag_s + (l32 & 7) * kFlagPitch + 4 * half;
+#pragma unroll
+            for (int ks = 0; ks < kBlock / 16; ++ks) {
+                const uint32_t f0 = *reinterpret_cast<const uint32_t *>(flag_row + 16 * ks);
+                const uint32_t f1 = *reinterpret_cast<const uint32_t *>(flag_row + 16 * ks + 8);
+                const uint4 oh = onehot4(f0, f1);
+                const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(xs + x_rd0 + 16 * ks * kPitch));
+                const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(xs + x_rd1 + 16 * ks * kPitch));
+                const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                sum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, oh), b, sum, 0, 0, 0);
+                // operands of at most two k-steps in flight: the registers go to
+                // the key rows held across the rounds
+                if (ks & 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            const int4 c0 = *reinterpret_cast<const int4 *>(&cnt_s[0][4 * half]);
+            const int4 c1 = *reinterpret_cast<const int4 *>(&cnt_s[1][4 * half]);
+            const int4 c2 = *reinterpret_cast<const int4 *>(&cnt_s[2][4 * half]);
+            const int4 c3 = *reinterpret_cast<const int4 *>(&cnt_s[3][4 * half]);
+            const int cnts[4] = {c0.x + c1.x + c2.x + c3.x, c0.y + c1.y + c2.y + c3.y, c0.z + c1.z + c2.z + c3.z,
+                                 c0.w + c1.w + c2.w + c3.w};
+            float sq[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * half + r;
+                const int cn = cnts[r];
+                float cv;
+                if (m < C && cn > 0) {
+                    cv = sum[r] * __builtin_amdgcn_rcpf((float)(4 * cn));
+                    const uint16_t hb = f32_to_bf16_bits(cv);
+                    const float r1 = cv - bf16_bits_to_f32(hb);
+                    const uint16_t mb = f32_to_bf16_bits(r1);
+                    const uint16_t lb = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mb));
+                    part_at(0, m, d) = hb;
+                    part_at(1, m, d) = mb;
+                    part_at(2, m, d) = lb;
+                } else {
+                    cv = centroid(m, d);
+                }
+                sq[r] = cv * cv;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) sq[r] += __shfl_xor(sq[r], o, 64);
+            }
+            if (l32 == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) cn_part[wave][4 * half + r] = sq[r];
+            }
+        }
+        wait_loads_lds_and_sync<RPT>();
+    }
+
+    float *co = cent_out + (long)row * C * D;
+    for (int i = tid; i < C * D; i += 256) co[i] = centroid(i / D, i % D);
+    if (tid < C) {   // weights from the last assignment
+        const int cn = cnt_s[0][tid] + cnt_s[1][tid] + cnt_s[2][tid] + cnt_s[3][tid];
+        w_out[(long)row * C + tid] = (float)((double)cn / (double)n);
+    }
+
+    // ---- the pooled keys, from the rows loaded before the rounds (the same
+    // summation order as kmeans_mfma_kernel and the standalone pooling kernels)
+    if (KB == kBlock) {
+        const int g = tid / DCH;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            if (g + G * i >= n) break;
+            const uint32_t w4[4] = {kraw[i].x, kraw[i].y, kraw[i].z, kraw[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += bf16_lo(w4[e]);
+                acc[2 * e + 1] += bf16_hi(w4[e]);
+            }
+        }
+#pragma unroll
+        for (int o = DCH; o < 64; o <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+        // every wavefront's last read of X lies before the loop's last barrier
+        float *part = reinterpret_cast<float *>(xs);
+        if (lane < DCH) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[wave * D + 8 * lane + e] = acc[e];
+        }
+        wait_loads_lds_and_sync<0>();
+        if (tid < D)
+            kbar[((long)bh * NBk + qb) * D + tid] =
+                (((part[tid] + part[D + tid]) + part[2 * D + tid]) + part[3 * D + tid]) / (float)n;
+    } else {
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int i = tid + 256 * it, g = i / DCH, c = i % DCH;
+            const int j = qb * kFine + g;
+            if (j >= NBk) continue;
+            const int nr = min(kFineBlock, N - kFineBlock * j);
+            float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < kFineBlock; ++r) {
+                if (r >= nr) break;
+                const uint4 x = kraw[it * kFineBlock + r];
+                const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += bf16_lo(w4[e]);
+                    acc[2 * e + 1] += bf16_hi(w4[e]);
+                }
+            }
+            const float fn = (float)nr;
+            float4 *dst = reinterpret_cast<float4 *>(kbar + ((long)bh * NBk + j) * D + 8 * c);
+            dst[0] = make_float4(acc[0] / fn, acc[1] / fn, acc[2] / fn, acc[3] / fn);
+            dst[1] = make_float4(acc[4] / fn, acc[5] / fn, acc[6] / fn, acc[7] / fn);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_kmeans(const void *q, const void *k, int dtype, int B, int H, int N, int N_pad, int D, int NB, int C,
@@ -538,8 +867,8 @@ hipError_t launch_kmeans(const void *q, const void *k, int dtype, int B, int H, 
     const dim3 grid((unsigned)((long)B * H * NB)), block(256);
     *pooled = dtype == kBF16;
     if (dtype == kBF16 && D == 128)
-        kmeans_mfma_kernel<128><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight,
-                                                       (const uint16_t *)k, kb, NBk, kbar);
+        (kb == kBlock ? kmeans_lds_kernel<128, kBlock> : kmeans_lds_kernel<128, kFineBlock>)<<<grid, block, 0, s>>>(
+            (const uint16_t *)q, N, N_pad, NB, C, T, cent, weight, (const uint16_t *)k, NBk, kbar);
     else if (dtype == kBF16 && D == 64)
         kmeans_mfma_kernel<64><<<grid, block, 0, s>>>((const uint16_t *)q, N, N_pad, NB, C, T, cent, weight,
                                                       (const uint16_t *)k, kb, NBk, kbar);
