@@ -533,6 +533,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 }
 
 
+// Sum of x over the 32 lanes of each wavefront half, in every lane: butterflies
+// within quads (quad_perm), 8-lane (row_half_mirror) and 16-lane (row_mirror)
+// groups by DPP, then the two rows of the half by v_permlane16_swap; no LDS.
+__device__ __forceinline__ float half_sum32(float x)
+{
+#define ABA_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, true))
+    x += ABA_DPP(x, 0xB1);    // quad_perm(1, 0, 3, 2)
+    x += ABA_DPP(x, 0x4E);    // quad_perm(2, 3, 0, 1)
+    x += ABA_DPP(x, 0x141);   // row_half_mirror
+    x += ABA_DPP(x, 0x140);   // row_mirror
+#undef ABA_DPP
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------------------
 // bf16 at head_dim 128: the same rounds with the block's query rows kept in LDS
 // row-major, as they arrive.  Direct buffer->LDS loads copy the 128 rows (no
@@ -564,7 +579,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     // rows x 4 chunks of a 32-lane phase of the update's transposing reads
     __shared__ __align__(16) char xs[kBlock * kPitch];
     __shared__ uint4 cs_s[24 * DCH];                  // split centroids, as in kmeans_mfma_kernel
-    __shared__ float cn_part[4][kMaxClusters];
+    __shared__ __align__(16) float cn_part[4][kMaxClusters];
     constexpr int kFlagPitch = kBlock + 8;
     __shared__ __align__(16) uint8_t flag_s[kMaxClusters * kFlagPitch];
     __shared__ int cnt_s[4][kMaxClusters];
@@ -698,21 +713,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, x),
                                                           acc, 0, 0, 0);
         }
+        // the four wavefronts' shares of |c_m|^2 for this half's clusters 4half .. 4half+3
+        float4 cnv[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) cnv[w] = *reinterpret_cast<const float4 *>(&cn_part[w][4 * half]);
         float bd = INFINITY;
         int bm = 4 * half;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int m = 4 * half + j;
             const float dot = acc[j] + acc[4 + j] + acc[8 + j];
-            const float cn2 = cn_part[0][m] + cn_part[1][m] + cn_part[2][m] + cn_part[3][m];
+            const float cn2 = cnv[0][j] + cnv[1][j] + cnv[2][j] + cnv[3][j];
             const float dist = m < C ? fmaf(-2.f, dot, cn2) : INFINITY;
             if (dist < bd) {
                 bd = dist;
                 bm = m;
             }
         }
-        const float od = __shfl_xor(bd, 32, 64);
-        const int om = __shfl_xor(bm, 32, 64);
+        // the other half's candidate (lane l ^ 32), by one lane swap each
+        const auto dsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bd), __float_as_uint(bd), false, false);
+        const auto msw = __builtin_amdgcn_permlane32_swap((uint32_t)bm, (uint32_t)bm, false, false);
+        const float od = __uint_as_float(half ? dsw[0] : dsw[1]);
+        const int om = (int)(half ? msw[0] : msw[1]);
         if (od < bd || (od == bd && om < bm)) {
             bd = od;
             bm = om;
@@ -784,10 +806,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 sq[r] = cv * cv;
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) sq[r] += __shfl_xor(sq[r], o, 64);
-            }
+            for (int r = 0; r < 4; ++r) sq[r] = half_sum32(sq[r]);
             if (l32 == 0) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) cn_part[wave][4 * half + r] = sq[r];
@@ -818,10 +837,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 acc[2 * e + 1] += bf16_hi(w4[e]);
             }
         }
+        // the four groups of a wavefront (lanes c + 16 j) add up by lane swaps
+        // between rows and between halves, no LDS
 #pragma unroll
-        for (int o = DCH; o < 64; o <<= 1)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+        for (int e = 0; e < 8; ++e) {
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[e]), __float_as_uint(acc[e]), false, false);
+            acc[e] = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[e]), __float_as_uint(acc[e]), false, false);
+            acc[e] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+        }
         // every wavefront's last read of X lies before the loop's last barrier
         float *part = reinterpret_cast<float *>(xs);
         if (lane < DCH) {
