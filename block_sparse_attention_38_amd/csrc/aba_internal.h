@@ -97,6 +97,91 @@ __device__ __forceinline__ int xcd_contiguous_id(int hw_id, int n)
     return xcd * per + (xcd < extra ? xcd : extra) + k;
 }
 
+// Cross-lane exchanges without LDS: DPP butterflies inside 16-lane rows
+// (quad_perm xor 1, xor 2; row_half_mirror and row_mirror pair the two quads of
+// an 8-lane group and the two halves of a row), then v_permlane16_swap between
+// rows and v_permlane32_swap between the wavefront's halves.
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t swap16_u32(uint32_t v, bool second)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return second ? r[1] : r[0];
+}
+__device__ __forceinline__ uint32_t swap32_u32(uint32_t v, bool second)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return second ? r[1] : r[0];
+}
+
+// op over the 64 lanes of a wavefront, the result in every lane; op must be
+// commutative and associative (sum, min, max).  T is 32 or 64 bits wide.
+template <typename T, typename Op> __device__ __forceinline__ T wave_allreduce(T x, Op op)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+    auto pull = [](T v, auto f) __attribute__((always_inline)) {
+        if constexpr (sizeof(T) == 4) {
+            return __builtin_bit_cast(T, f(__builtin_bit_cast(uint32_t, v)));
+        } else {
+            const uint64_t u = __builtin_bit_cast(uint64_t, v);
+            const uint64_t lo = f((uint32_t)u), hi = f((uint32_t)(u >> 32));
+            return __builtin_bit_cast(T, lo | (hi << 32));
+        }
+    };
+    x = op(x, pull(x, [](uint32_t v) { return dpp_u32<0xB1>(v); }));    // quad_perm(1, 0, 3, 2)
+    x = op(x, pull(x, [](uint32_t v) { return dpp_u32<0x4E>(v); }));    // quad_perm(2, 3, 0, 1)
+    x = op(x, pull(x, [](uint32_t v) { return dpp_u32<0x141>(v); }));   // row_half_mirror
+    x = op(x, pull(x, [](uint32_t v) { return dpp_u32<0x140>(v); }));   // row_mirror
+    x = op(pull(x, [](uint32_t v) { return swap16_u32(v, false); }), pull(x, [](uint32_t v) { return swap16_u32(v, true); }));
+    x = op(pull(x, [](uint32_t v) { return swap32_u32(v, false); }), pull(x, [](uint32_t v) { return swap32_u32(v, true); }));
+    return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (32- or 64-bit integers
+// or floats): Hillis-Steele inside each 16-lane row (row_shr 1, 2, 4, 8; lanes
+// shifted in from outside the row read 0), then the last lane of rows 0 and 2
+// into rows 1 and 3 (row_bcast:15) and the last lane of row 1 into rows 2 and 3
+// (row_bcast:31).
+template <typename T> __device__ __forceinline__ T wave_incl_scan_dpp(T x)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+    auto step = [&](auto f) __attribute__((always_inline)) {
+        if constexpr (sizeof(T) == 4) {
+            x = x + __builtin_bit_cast(T, f(__builtin_bit_cast(uint32_t, x)));
+        } else {
+            const uint64_t u = __builtin_bit_cast(uint64_t, x);
+            const uint64_t lo = f((uint32_t)u), hi = f((uint32_t)(u >> 32));
+            x = x + __builtin_bit_cast(T, lo | (hi << 32));
+        }
+    };
+#define ABA_DPP_STEP(ctrl, rows) \
+    step([](uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, rows, 0xF, true); })
+    ABA_DPP_STEP(0x111, 0xF);   // row_shr:1
+    ABA_DPP_STEP(0x112, 0xF);   // row_shr:2
+    ABA_DPP_STEP(0x114, 0xF);   // row_shr:4
+    ABA_DPP_STEP(0x118, 0xF);   // row_shr:8
+    ABA_DPP_STEP(0x142, 0xA);   // row_bcast:15 into rows 1 and 3
+    ABA_DPP_STEP(0x143, 0xC);   // row_bcast:31 into rows 2 and 3
+#undef ABA_DPP_STEP
+    return x;
+}
+
+// The value of x in lane l (l the same in every lane of the wavefront).
+template <typename T> __device__ __forceinline__ T lane_value(T x, int l)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+        const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+        return __builtin_bit_cast(T, lo | (hi << 32));
+    }
+}
+
 __device__ __forceinline__ float wave_max(float x)
 {
     for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));

@@ -172,31 +172,19 @@ __device__ __forceinline__ float kept_weight(int j, uint32_t x, uint64_t cut, ui
 
 template <typename T> __device__ __forceinline__ T wave_sum_t(T x)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    return wave_allreduce(x, [](T a, T b) { return a + b; });
 }
 
 // Maximum over the 64 lanes of a wavefront.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t y = __shfl_xor(x, o, 64);
-        x = y > x ? y : x;
-    }
-    return x;
+    return wave_allreduce(x, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront.
-template <typename T> __device__ __forceinline__ T wave_incl_scan(T x, int lane)
+template <typename T> __device__ __forceinline__ T wave_incl_scan(T x, int /*lane*/)
 {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const T y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
-    return x;
+    return wave_incl_scan_dpp(x);
 }
 
 // Per-row result of the chunked path for rows of more than kChunkBlocks blocks
@@ -297,11 +285,8 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
     }
     part = wave_sum_t<uint64_t>(part);
     lmax_s[tid] = vmax;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        vmin = min(vmin, (uint32_t)__shfl_xor((int)vmin, o, 64));
-        vmax = max(vmax, (uint32_t)__shfl_xor((int)vmax, o, 64));
-    }
+    vmin = wave_allreduce(vmin, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+    vmax = wave_allreduce(vmax, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
     if (lane == 0) {
         ured[wave] = part;
         mm_s[0][wave] = vmin;
@@ -414,7 +399,7 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
                     if (bal) {
                         int base = 0;
                         if (lane == __builtin_ctzll(bal)) base = atomicAdd(&cand_n, __popcll(bal));
-                        base = __shfl(base, __builtin_ctzll(bal), 64);
+                        base = lane_value(base, __builtin_ctzll(bal));
                         const int at = base + __popcll(bal & ((1ull << lane) - 1));
                         if (sel && at < kCandMax) cand[at] = pack_key(xs[e], j);
                     }
@@ -561,7 +546,7 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
                 if (bal) {
                     int base = 0;
                     if (lane == __builtin_ctzll(bal)) base = atomicAdd(&top_n, __popcll(bal));
-                    base = __shfl(base, __builtin_ctzll(bal), 64);
+                    base = lane_value(base, __builtin_ctzll(bal));
                     if (sel) top[base + __popcll(bal & ((1ull << lane) - 1))] = pack_key(xs[e], j);
                 }
             }
@@ -643,8 +628,8 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
             int tt = fb ? __builtin_ctzll(fb) : T;
             const bool found = tt < T || T == K;
             if (found) {
-                const uint64_t r = total - __shfl(incl, tt - 1, 64);
-                const uint64_t c = __shfl(key, tt - 1, 64);
+                const uint64_t r = total - lane_value(incl, tt - 1);
+                const uint64_t c = lane_value(key, tt - 1);
                 if (lane == 0) {
                     r_s = r;
                     cut_s = c;
@@ -761,7 +746,7 @@ __global__ __launch_bounds__(64 * W) void sample_topk_kernel(const float *__rest
             const int c = __popc(nib);
             const int incl = wave_incl_scan<int>(c, lane);
             int pos = running + incl - c;
-            running += __shfl(incl, 63, 64);
+            running += lane_value(incl, 63);
             const int q = quad(k);
             const uint32_t xs[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
 #pragma unroll
@@ -908,11 +893,8 @@ __global__ __launch_bounds__(kChunkThreads) void sample_chunk_top_kernel(const f
             mn = min(mn, a[i]);
             mx = max(mx, a[i]);
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-        }
+        mn = wave_allreduce(mn, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+        mx = wave_allreduce(mx, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
         // the answer lies in [mn, mx]: only the bits below their common prefix are searched
         const uint32_t diff = mn ^ mx;
         const int top = diff ? 31 - __clz(diff) : -1;
@@ -941,7 +923,7 @@ __global__ __launch_bounds__(kChunkThreads) void sample_chunk_top_kernel(const f
             if (bal) {
                 int base = 0;
                 if (lane == __builtin_ctzll(bal)) base = atomicAdd(&cand_n, __popcll(bal));
-                base = __shfl(base, __builtin_ctzll(bal), 64);
+                base = lane_value(base, __builtin_ctzll(bal));
                 const int at = base + __popcll(bal & ((1ull << lane) - 1));
                 if (sel && at < kCandMax) cand[at] = pack_key(xs[e], j);
             }
@@ -1013,8 +995,8 @@ __global__ __launch_bounds__(64) void sample_chunk_merge_kernel(const uint64_t *
     const bool fail = lane >= 1 && lane < T && (uint64_t)(K - lane) * sg < total - (incl - sg);
     const uint64_t fb = __ballot(fail);
     const int tt = fb ? __builtin_ctzll(fb) : T;
-    const uint64_t r_inc = __shfl(incl, tt - 1, 64);
-    const uint64_t cut = __shfl(key, tt - 1, 64);
+    const uint64_t r_inc = lane_value(incl, tt - 1);
+    const uint64_t cut = lane_value(key, tt - 1);
     if (lane == 0) {
         if (tt < T || T == K) {
             st.R = total - r_inc;
@@ -1093,7 +1075,7 @@ __global__ __launch_bounds__(kChunkThreads) void sample_chunk_draw_kernel(const 
         const int cn = __popc(nib);
         const int incl = wave_incl_scan<int>(cn, lane);
         int pos = running + incl - cn;
-        running += __shfl(incl, 63, 64);
+        running += lane_value(incl, 63);
         const int q = jb / 4 + chunk_quad(wave, k, lane);
         const uint32_t xs[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
 #pragma unroll
@@ -1303,10 +1285,10 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(const float *__restric
             if (fb) {
                 const int tt = __builtin_ctzll(fb);   // >= 1 in the first chunk
                 t = c0 + tt;
-                pre_t = tt > 0 ? __shfl(incl, tt - 1, 64) : before;
+                pre_t = tt > 0 ? lane_value(incl, tt - 1) : before;
                 found = true;
             } else {
-                before = __shfl(incl, 63, 64);
+                before = lane_value(incl, 63);
             }
         }
         if (!found) pre_t = before;
@@ -1336,7 +1318,7 @@ __global__ __launch_bounds__(256) void sample_wave_kernel(const float *__restric
         const int c = __popc(nib);
         const int incl = wave_incl_scan<int>(c, lane);
         int pos = base + incl - c;
-        base += __shfl(incl, 63, 64);
+        base += lane_value(incl, 63);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if (!((nib >> e) & 1u)) continue;
