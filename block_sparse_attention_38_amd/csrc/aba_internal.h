@@ -116,6 +116,32 @@ __device__ __forceinline__ uint32_t swap32_u32(uint32_t v, bool second)
     return second ? r[1] : r[0];
 }
 
+// x[l] + x[l ^ 32] and max(x[l], x[l ^ 32]) in every lane l (one lane swap).
+__device__ __forceinline__ float xor32_sum(float x)
+{
+    return __uint_as_float(swap32_u32(__float_as_uint(x), false)) + __uint_as_float(swap32_u32(__float_as_uint(x), true));
+}
+__device__ __forceinline__ float xor32_max(float x)
+{
+    return fmaxf(__uint_as_float(swap32_u32(__float_as_uint(x), false)),
+                 __uint_as_float(swap32_u32(__float_as_uint(x), true)));
+}
+
+// Sum and maximum over each aligned group of 8 lanes, in every lane of the group
+// (the same pairing, hence the same rounding, as xor butterflies over 1, 2, 4).
+__device__ __forceinline__ float group8_sum(float x)
+{
+    x += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(x)));    // quad_perm(1, 0, 3, 2)
+    x += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(x)));    // quad_perm(2, 3, 0, 1)
+    return x + __uint_as_float(dpp_u32<0x141>(__float_as_uint(x)));   // row_half_mirror
+}
+__device__ __forceinline__ float group8_max(float x)
+{
+    x = fmaxf(x, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(x))));
+    return fmaxf(x, __uint_as_float(dpp_u32<0x141>(__float_as_uint(x))));
+}
+
 // op over the 64 lanes of a wavefront, the result in every lane; op must be
 // commutative and associative (sum, min, max).  T is 32 or 64 bits wide.
 template <typename T, typename Op> __device__ __forceinline__ T wave_allreduce(T x, Op op)

@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         mraw = fmaxf(mraw, acc[kt][r]);
                     }
             }
-            mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+            mraw = xor32_max(mraw);
             const float mx = mraw * scale_log2;
             float sum = 0.f;
             if (mraw > -INFINITY) {
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[kt][r], scale_log2, -mx));
             }
-            sum += __shfl_xor(sum, 32, 64);
+            sum = xor32_sum(sum);
             if (half == 0) red[i & 1][wave][l32] = make_float2(mx, sum);
         } else {
             // lane (l32, half) element r of tile kt: slot 8(r/4) + 4half + r%4 (query block
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         a += sv[e].y * __builtin_amdgcn_exp2f(fmaf(acc[kt][4 * p + e], scale_log2, -sv[e].x));
-                    part[kt][p] = a + __shfl_xor(a, 32, 64);
+                    part[kt][p] = xor32_sum(a);
                 }
             }
 #pragma unroll
@@ -502,15 +502,13 @@ __global__ __launch_bounds__(256) void row_score_kernel(const float *__restrict_
 #pragma unroll
             for (int u = 0; u < 4; ++u) m4[u] = fmaxf(m4[u], row[j + 8 * u]);
         float M = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        M = group8_max(M);
         float z4[4] = {0.f, 0.f, 0.f, 0.f};
         for (int j = sub; j < n32; j += 32)
 #pragma unroll
             for (int u = 0; u < 4; ++u) z4[u] += __builtin_amdgcn_exp2f(row[j + 8 * u] - M);
         float Z = (z4[0] + z4[1]) + (z4[2] + z4[3]);
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) Z += __shfl_xor(Z, o, 64);
+        Z = group8_sum(Z);
         if (sub == 0) {
             const int qb = kTileBlocks * ct + sl / kSlots, m = sl % kSlots;
             float coef = 0.f;
