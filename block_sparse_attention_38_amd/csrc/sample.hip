@@ -865,7 +865,7 @@ __global__ __launch_bounds__(kChunkThreads) void sample_chunk_top_kernel(const f
                                                                int32_t *__restrict__ cflag)
 {
     __shared__ uint32_t lmax_s[kChunkThreads];
-    __shared__ uint64_t cand[kCandMax];
+    __shared__ __align__(16) uint64_t cand[kCandMax + 8];   // + padding read by the ranking's 16-byte reads
     __shared__ uint64_t ured[kChunkWaves];
     __shared__ uint32_t lo_s;
     __shared__ int cand_n;
@@ -940,10 +940,22 @@ __global__ __launch_bounds__(kChunkThreads) void sample_chunk_top_kernel(const f
     }
     if (C > kCandMax) return;
     uint64_t *out = ctop + item * kChunkTop;
-    for (int i = tid; i < C; i += kChunkThreads) {   // keys are distinct: each rank is taken once
+    // rank of each candidate among all of them (keys are distinct: each rank is
+    // taken once); the candidates are read eight at a time in 16-byte pieces,
+    // all lanes at the same address, and the padding past C holds zeros, which
+    // rank below every key
+    if (tid < 8) cand[C + tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < C; i += kChunkThreads) {
         const uint64_t key = cand[i];
         int rank = 0;
-        for (int m = 0; m < C; ++m) rank += cand[m] > key;
+        for (int m = 0; m < C; m += 8) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(cand + m);
+            const uint4 a = p[0], b = p[1], c4 = p[2], d = p[3];
+            auto gt = [&](uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32 | lo) > key ? 1 : 0; };
+            rank += gt(a.x, a.y) + gt(a.z, a.w) + gt(b.x, b.y) + gt(b.z, b.w) + gt(c4.x, c4.y) + gt(c4.z, c4.w) +
+                    gt(d.x, d.y) + gt(d.z, d.w);
+        }
         if (rank < kChunkTop) out[rank] = key;
     }
     for (int i = C + tid; i < kChunkTop; i += kChunkThreads) out[i] = 0;
