@@ -822,6 +822,9 @@ def main():
         result["mfma_sustained"] = rate
         result["roofline"]["sustained_peak"] = rate["random_tflops"]
         result["roofline"]["frac_of_sustained"] = attend_tflops / rate["random_tflops"]
+        if result["fine_key_blocks"]:
+            fk = result["fine_key_blocks"]
+            fk["attend_kept_frac_of_sustained"] = fk["attend_kept_tflops"] / rate["random_tflops"]
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         q, k, v = host_sets[0]
