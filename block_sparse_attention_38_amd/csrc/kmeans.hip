@@ -744,11 +744,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             const int m = 4 * half + j;
             flag_s[m * kFlagPitch + my_q] = (qv && bm == m) ? (uint8_t)0x80 : (uint8_t)0;
         }
+        // this wavefront's cluster counts: lane m keeps count m, lanes 0..7 store
+        int my_cnt = 0;
 #pragma unroll
         for (int m = 0; m < kMaxClusters; ++m) {
             const int c = __popcll(__ballot(half == 0 && qv && bm == m));
-            if (lane == 0) cnt_s[wave][m] = c;
+            my_cnt = lane == m ? c : my_cnt;
         }
+        if (lane < kMaxClusters) cnt_s[wave][lane] = my_cnt;
         const bool changed = __ballot(half == 0 && qv && bm != prev) != 0;
         prev = bm;
         if (lane == 0) chg_s[wave] = changed ? 1 : 0;
