@@ -538,6 +538,109 @@ def run_sweep(args, w):
     print(json.dumps(result), flush=True)
 
 
+def _smi_sample(exe: str):
+    """One amd-smi reading of GPU 0: (socket power W, mean graphics clock MHz over the XCDs), or None."""
+    import subprocess
+    r = subprocess.run(["timeout", "10", exe, "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True, text=True)
+    try:
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clks = [v["clk"]["value"] for name, v in g["clock"].items()
+                if name.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk", {}).get("value"), (int, float))]
+        return float(g["power"]["socket_power"]["value"]), float(np.mean(clks))
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
+
+
+def power_trace(args):
+    """Socket power and graphics clock (amd-smi, sampled from a host thread) while
+    one kind of call runs back to back for a few seconds: the sparse and dense
+    attention of the layer, the matrix-core rate loop on random operands and on
+    zeros, and the score stage; idle first.  For each phase: median power and
+    clock, time per call, and for the attention and the loop their bf16 rate
+    against the quoted peak and against the peak at the clock the phase ran at."""
+    import shutil
+    import threading
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe) or _smi_sample(exe) is None:
+        print("amd-smi is not available or reads no power: no power trace", file=sys.stderr)
+        sys.exit(2)
+    w = ALL[args.workload]
+    density = w.densities[0] if args.density is None else args.density
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in synth.make_inputs(w, seed=1001))
+    p = aba.plan(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, CLUSTERS, KMEANS_ITERS, w.budget(density))
+    ws = aba.workspace(p, dev)
+    sc = aba.score(p, qd, kd, ws=ws)
+    lists = aba.sample(p, sc, args.seed, ws=ws)
+    out = torch.empty_like(qd)
+    kept = int(lists[1].clamp(min=0).sum().item())
+    kept_flop = kept_flops(p, lists[1].cpu().numpy(), lists[0].cpu().numpy())
+    dense_flop = 4.0 * w.batch * w.heads * float(w.seq_len) ** 2 * w.head_dim
+    rate_out = torch.empty(aba.MFMA_RATE_THREADS, dtype=torch.float32, device=dev)
+    rate_iters = 2000
+    rate_flop = float(aba.MFMA_RATE_FLOP_PER_ITER) * rate_iters
+    torch.cuda.synchronize()
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            t0 = time.time()
+            r = _smi_sample(exe)
+            if r is not None:
+                samples.append(((t0 + time.time()) / 2, *r))
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    phases = []
+
+    def run(name, fn, flop):
+        if fn is None:
+            t0 = time.time()
+            time.sleep(args.power_seconds / 2)
+            phases.append((name, t0, time.time(), 0, flop))
+            return
+        fn()
+        torch.cuda.synchronize()
+        t0, n = time.time(), 0
+        while time.time() - t0 < args.power_seconds:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            n += 10
+        phases.append((name, t0, time.time(), n, flop))
+        log(f"[bench] power trace: {name} {n} calls")
+        time.sleep(1.0)
+
+    run("idle", None, 0.0)
+    run("sparse_attend", lambda: aba.attend(p, qd, kd, vd, *lists, out=out, ws=ws), kept_flop)
+    run("dense_attend", lambda: aba.attend_full(p, qd, kd, vd, out=out, ws=ws), dense_flop)
+    run("mfma_rate_random", lambda: aba.mfma_rate(rate_iters, True, rate_out), rate_flop)
+    run("mfma_rate_zeros", lambda: aba.mfma_rate(rate_iters, False, rate_out), rate_flop)
+    run("score", lambda: aba.score(p, qd, kd, out=sc, ws=ws), 0.0)
+    stop.set()
+    th.join(timeout=15)
+    res = {}
+    for name, a, b, n, flop in phases:
+        sel = [x for x in samples if a + 0.5 < x[0] < b - 0.1]   # skip the first half second of a phase
+        pw = np.array([x[1] for x in sel]) if sel else np.array([np.nan])
+        ck = np.array([x[2] for x in sel]) if sel else np.array([np.nan])
+        e = {"samples": len(sel), "socket_power_w_median": float(np.median(pw)), "socket_power_w_max": float(pw.max()),
+             "gfx_clock_mhz_median": float(np.median(ck))}
+        if n:
+            ms = (b - a) / n * 1e3
+            e["ms_per_call"] = ms
+            if flop:
+                tf = flop / (ms * 1e-3) / 1e12
+                e["bf16_tflops"] = tf
+                e["frac_of_peak"] = tf / PEAK_BF16_TFLOPS
+                e["frac_of_peak_at_clock"] = tf / (PEAK_BF16_TFLOPS * np.median(ck) / 2400.0)
+        res[name] = e
+    print(json.dumps({"power_trace": res, "workload": w.name, "kept_blocks": kept,
+                      "seconds_per_phase": args.power_seconds, "sample_period_s":
+                      float(np.mean(np.diff([x[0] for x in samples]))) if len(samples) > 1 else None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -579,7 +682,17 @@ def main():
                     help="rounds of the matrix-core rate loop per timed call (2^30 flop each; 10^4: ~6 ms)")
     ap.add_argument("--mfma-rate-only", action="store_true",
                     help="only measure the sustained matrix-core rate and print it (for its counter profile)")
+    ap.add_argument("--power-only", action="store_true",
+                    help="only sample socket power and graphics clock (amd-smi) while each kind of call runs back to "
+                         "back (sparse and dense attention, the matrix-core rate loop, the score stage)")
+    ap.add_argument("--power-seconds", type=float, default=4.0, help="--power-only: seconds per phase")
     args = ap.parse_args()
+    if args.power_only:
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(2)
+        power_trace(args)
+        return
     if args.mfma_rate_only:
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
