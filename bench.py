@@ -770,8 +770,16 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    # the dense path first: its own measurement, and it leaves the GPU at its
-    # loaded clock, so that the timed steps do not include the ramp from idle
+    t_warm = time.perf_counter()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warm-up steps in {time.perf_counter() - t_warm:.3f} s")
+    # the dense path between the warm-up and the timed steps: its own
+    # measurement, and it leaves the GPU at its loaded clock, so that the
+    # timed steps do not include the ramp from idle (the warm-up's first calls
+    # spend host time in which the chip idles, and a first window after 0.5 s
+    # of idle runs ~13% slower than the windows after it)
     dense_ms = None
     if not args.no_dense:
         qd, kd, vd = sets[0]
@@ -785,10 +793,6 @@ def main():
         torch.cuda.synchronize()
         dense_ms = d0.elapsed_time(d1) / args.dense_reps
         log(f"[bench] dense attention: {dense_ms:.3f} ms")
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
 
     # the timed region: K steps, events only around each aba_attend call (the
     # dominant call, for the roofline)
