@@ -174,19 +174,19 @@ template <int D> __device__ __forceinline__ bf16x8 v_frag_tr(const char *p)
 // rows (so rows >= N read as 0).  Rows of K past N are read as they are (they
 // lie inside the padded sequence) and masked after the product.  A slot is
 // read only after a vmcnt wait and a barrier.
-template <int D> struct Dma {
-    static constexpr int loads = Lds<D>::kBytes / 1024 / kWaves;   // per tensor and wavefront
+template <int D, int W = kWaves> struct Dma {
+    static constexpr int loads = Lds<D>::kBytes / 1024 / W;       // per tensor and wavefront (W wavefronts)
     static constexpr int k_rows = 1024 / Lds<D>::pitch;             // K rows per load
     static constexpr int k_period = 16 / k_rows;                    // loads per K swizzle period
     int k[k_period];
     int v[2];                                                       // V rows: one period; V^T: 2 loads
 };
 
-template <int D>
-__device__ __forceinline__ Dma<D> dma_offsets(int wave, int lane)
+template <int D, int W = kWaves>
+__device__ __forceinline__ Dma<D, W> dma_offsets(int wave, int lane)
 {
     using L = Lds<D>;
-    using O = Dma<D>;
+    using O = Dma<D, W>;
     O off;
     const int k0 = O::loads * O::k_rows * wave, v0 = O::loads * 8 * wave;
 #pragma unroll
@@ -211,11 +211,11 @@ __device__ __forceinline__ Dma<D> dma_offsets(int wave, int lane)
 
 // Issue the direct loads of K rows key0 .. key0+63 into a K slot, or of the
 // matching V rows or V^T tile into a V slot (wavefront w fills its share).
-template <int D>
-__device__ __forceinline__ void issue_k(int4v rk, int key0, char *slot, int wave, const Dma<D> &off)
+template <int D, int W = kWaves>
+__device__ __forceinline__ void issue_k(int4v rk, int key0, char *slot, int wave, const Dma<D, W> &off)
 {
     using L = Lds<D>;
-    using O = Dma<D>;
+    using O = Dma<D, W>;
     const int base = key0 * D * 2;
     char *dst = slot + O::loads * 1024 * wave;
 #pragma unroll
@@ -223,11 +223,11 @@ __device__ __forceinline__ void issue_k(int4v rk, int key0, char *slot, int wave
         load_lds16(rk, off.k[t % O::k_period], base + (t / O::k_period) * 16 * L::pitch, dst + 1024 * t);
 }
 
-template <int D>
-__device__ __forceinline__ void issue_v(int4v rv, int key0, char *slot, int wave, const Dma<D> &off)
+template <int D, int W = kWaves>
+__device__ __forceinline__ void issue_v(int4v rv, int key0, char *slot, int wave, const Dma<D, W> &off)
 {
     using L = Lds<D>;
-    using O = Dma<D>;
+    using O = Dma<D, W>;
     const int base = key0 * D * 2;   // a V^T tile sits where its keys' rows of v do
     char *dst = slot + O::loads * 1024 * wave;
     if (v_rows<D>()) {
@@ -418,8 +418,13 @@ __device__ __forceinline__ float half_pair_max(float x)
     return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int D, bool full>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(
+// QB query blocks per workgroup (4 QB wavefronts).  QB = 2 serves the dense
+// path only: both query blocks take the same full key list, so each K and V
+// sub-tile is copied into LDS once for 256 query rows instead of 128.  Every
+// wavefront runs exactly the instructions it runs with QB = 1, in the same
+// order, so the outputs do not depend on QB.
+template <int D, bool full, int QB = 1>
+__global__ __launch_bounds__(kThreads * QB) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
     const int32_t *__restrict__ order, uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap,
@@ -437,13 +442,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __align__(16) char ks0[L::kBytes], ks1[L::kBytes], ks2[L::kBytes];
     __shared__ __align__(16) char vs0[L::vBytes], vs1[L::vBytes];
 
+    static_assert(QB == 1 || (QB == 2 && full), "two query blocks per workgroup only on the dense path");
+    constexpr int W = kWaves * QB;     // wavefronts of the workgroup (they share the LDS staging)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qwave = wave % kWaves;   // the wavefront's 32 rows within its query block
     const int l32 = lane & 31, half = lane >> 5;
     // (b*H + h) * NB + query block; sparse lists run longest first within each range
     // of the order (see mapped_slot)
     const int slot = mapped_slot(xcd_ranges);
-    const int blk = full ? slot : order[slot];
+    const int blk = full ? slot * QB + wave / kWaves : order[slot];
     const int qb = blk % NB;
     const long bh = blk / NB;
     const uint16_t *qh = q + bh * N_pad * D;
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int4v rv = head_rsrc(vt + bh * N_pad * D, (v_rows<D>() ? N : N_pad) * D * 2);
 
     // this lane's query row (the MFMA column l32 of wavefront's tile); padding rows read as zero
-    const int qrow = qb * kBlock + 32 * wave + l32;
+    const int qrow = qb * kBlock + 32 * qwave + l32;
     const bool qvalid = qrow < N;
     bf16x8 qf[KS];
 #pragma unroll
@@ -512,7 +520,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                   *reinterpret_cast<const uint4 *>(st + v_rd[i / DT] + (i % DT) * 32 * L::vPitch));
     };
 
-    const Dma<D> dma = dma_offsets<D>(wave, lane);
+    const Dma<D, W> dma = dma_offsets<D, W>(wave, lane);
 
     // One 64-key sub-tile held in K slot kst and V slot vst (compile-time
     // offsets, so every LDS read address is a per-lane base plus an
@@ -605,7 +613,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // K(u + 2) loads: K(u + 1) and V(u + 1) are then in LDS.  The entry loop is unrolled three times, so
     // every slot is a compile-time offset.  Branches are uniform over the
     // workgroup; invalid entries and sub-tiles past N load and compute nothing.
-    constexpr int KL = Dma<D>::loads;
+    constexpr int KL = Dma<D, W>::loads;
     auto kptr = [&](int sl) __attribute__((always_inline)) { return sl == 0 ? ks0 : (sl == 1 ? ks1 : ks2); };
     auto vptr = [&](int sl) __attribute__((always_inline)) { return sl == 0 ? vs0 : vs1; };
     const Entry none{-1, 0.f};
@@ -614,10 +622,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     Entry ne = n_list > 1 ? window_entry<full>(win, 1) : none;
     auto hi_valid = [&](const Entry &en) __attribute__((always_inline)) { return en.j >= 0 && en.j * kBlock + kSub < N; };
     if (ce.j >= 0) {
-        issue_k<D>(rk, ce.j * kBlock, kptr(0), wave, dma);
-        issue_v<D>(rv, ce.j * kBlock, vptr(0), wave, dma);
+        issue_k<D, W>(rk, ce.j * kBlock, kptr(0), wave, dma);
+        issue_v<D, W>(rv, ce.j * kBlock, vptr(0), wave, dma);
     }
-    if (hi_valid(ce)) issue_k<D>(rk, ce.j * kBlock + kSub, kptr(1), wave, dma);
+    if (hi_valid(ce)) issue_k<D, W>(rk, ce.j * kBlock + kSub, kptr(1), wave, dma);
     // settle the Q loads here, once, rather than before every tile of the loop
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
@@ -630,13 +638,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const Entry nn = e2 < n_list ? window_entry<full>(win, e2) : none;
         const bool ce_hi = hi_valid(ce), ne_ok = ne.j >= 0, ne_hi = hi_valid(ne);
         // first half: V of the second half, K of the next entry's first half
-        if (ce_hi) issue_v<D>(rv, ce.j * kBlock + kSub, vptr(1), wave, dma);
-        if (ne_ok) issue_k<D>(rk, ne.j * kBlock, kptr((2 * E3 + 2) % 3), wave, dma);
+        if (ce_hi) issue_v<D, W>(rv, ce.j * kBlock + kSub, vptr(1), wave, dma);
+        if (ne_ok) issue_k<D, W>(rk, ne.j * kBlock, kptr((2 * E3 + 2) % 3), wave, dma);
         if (ce.j >= 0) tile(kptr(k0), vptr(0), ce.j * kBlock, ce.lw);
         if (ne_ok) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
         // second half: V of the next entry's first half, K of its second half
-        if (ne_ok) issue_v<D>(rv, ne.j * kBlock, vptr(0), wave, dma);
-        if (ne_hi) issue_k<D>(rk, ne.j * kBlock + kSub, kptr((2 * E3 + 3) % 3), wave, dma);
+        if (ne_ok) issue_v<D, W>(rv, ne.j * kBlock, vptr(0), wave, dma);
+        if (ne_hi) issue_k<D, W>(rk, ne.j * kBlock + kSub, kptr((2 * E3 + 3) % 3), wave, dma);
         if (ce_hi) tile(kptr(k1), vptr(1), ce.j * kBlock + kSub, ce.lw);
         if (ne_hi) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
         ce = ne;
@@ -1232,7 +1240,13 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
             order = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + vt_bytes(B, H, N_pad, D));
             order_kernel<<<dim3(8), dim3(kOrderThreads), 0, s>>>(cnt, G, cap, 1, order);
         }
-        if (D == 128) {
+        if (D == 128 && full && NB % 2 == 0) {
+            // dense, an even number of query blocks per head: two query blocks of
+            // one head per workgroup share the K and V staging
+            attend_bf16_kernel<128, true, 2><<<dim3((unsigned)(G / 2)), dim3(2 * kThreads), 0, s>>>(
+                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, cnt, w, order, (uint16_t *)out, N,
+                N_pad, NB, cap, sl2, attend_xcd_ranges(B, H, N_pad, D));
+        } else if (D == 128) {
             attend_bf16_kernel<128, full><<<grid, dim3(kThreads), 0, s>>>(
                 (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, cnt, w, order, (uint16_t *)out, N,
                 N_pad, NB, cap, sl2, attend_xcd_ranges(B, H, N_pad, D));
