@@ -418,13 +418,13 @@ __device__ __forceinline__ float half_pair_max(float x)
     return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// QB query blocks per workgroup (4 QB wavefronts).  QB = 2 serves the dense
-// path only: both query blocks take the same full key list, so each K and V
-// sub-tile is copied into LDS once for 256 query rows instead of 128.  Every
-// wavefront runs exactly the instructions it runs with QB = 1, in the same
-// order, so the outputs do not depend on QB.
-template <int D, bool full, int QB = 1>
-__global__ __launch_bounds__(kThreads * QB) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(
+// The attention of one workgroup: QB query blocks (4 QB wavefronts).  QB = 2
+// serves the dense path only: both query blocks take the same full key list,
+// so each K and V sub-tile is copied into LDS once for 256 query rows instead
+// of 128.  Every wavefront runs exactly the instructions it runs with QB = 1,
+// in the same order, so the outputs do not depend on QB.
+template <int D, bool full, int QB>
+__device__ __forceinline__ void attend_bf16_body(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
     const int32_t *__restrict__ order, uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap,
@@ -679,6 +679,29 @@ __global__ __launch_bounds__(kThreads * QB) __attribute__((amdgpu_waves_per_eu(2
         }
 }
 
+
+// One query block per workgroup: sparse lists, and dense at an odd number of
+// query blocks per head.
+template <int D, bool full>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ cnt, const float *__restrict__ w,
+    const int32_t *__restrict__ order, uint16_t *__restrict__ out, int N, int N_pad, int NB, int cap,
+    float scale_log2, bool xcd_ranges)
+{
+    attend_bf16_body<D, full, 1>(q, k, vt, idx, cnt, w, order, out, N, N_pad, NB, cap, scale_log2, xcd_ranges);
+}
+
+// Dense, two query blocks of one head per workgroup (an even number of query
+// blocks per head): they share the K and V staging.
+template <int D>
+__global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_dense_pair_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
+    uint16_t *__restrict__ out, int N, int N_pad, int NB, float scale_log2, bool xcd_ranges)
+{
+    attend_bf16_body<D, true, 2>(q, k, vt, nullptr, nullptr, nullptr, nullptr, out, N, N_pad, NB, NB, scale_log2,
+                                 xcd_ranges);
+}
 
 // ---------------------------------------------------------------------------
 // 4-token key blocks (kernel paragraph: the unit of selection is smaller than
@@ -1243,9 +1266,9 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
         if (D == 128 && full && NB % 2 == 0) {
             // dense, an even number of query blocks per head: two query blocks of
             // one head per workgroup share the K and V staging
-            attend_bf16_kernel<128, true, 2><<<dim3((unsigned)(G / 2)), dim3(2 * kThreads), 0, s>>>(
-                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, cnt, w, order, (uint16_t *)out, N,
-                N_pad, NB, cap, sl2, attend_xcd_ranges(B, H, N_pad, D));
+            attend_dense_pair_kernel<128><<<dim3((unsigned)(G / 2)), dim3(2 * kThreads), 0, s>>>(
+                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, N, N_pad, NB, sl2,
+                attend_xcd_ranges(B, H, N_pad, D));
         } else if (D == 128) {
             attend_bf16_kernel<128, full><<<grid, dim3(kThreads), 0, s>>>(
                 (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, idx, cnt, w, order, (uint16_t *)out, N,
