@@ -206,9 +206,11 @@ def test_attend_skips_malformed_list_entries(aba):
     check_attention(gpu_rows(out, items), ref, w.dtype, "attend_skips_malformed_list_entries")
 
 
-def test_every_block_kept_equals_dense(aba):
-    """Budget >= NB: every inclusion probability is 1 and sparse attention is dense attention."""
-    w = RAGGED
+@pytest.mark.parametrize("w", [RAGGED, BATCH2], ids=lambda w: w.name)
+def test_every_block_kept_equals_dense(aba, w):
+    """Budget >= NB: every inclusion probability is 1 and sparse attention is dense attention
+    (an odd number of query blocks per head: one query block per dense workgroup; an even
+    number, batch 2: two per workgroup)."""
     (q, k, v), (qd, kd, vd) = inputs(w, 108)
     p = make_plan(aba, w, budget=w.n_blocks)
     out, (s, idx, cnt, wt) = aba.layer(p, qd, kd, vd, seed=3)
@@ -322,11 +324,12 @@ def test_single_layer_dense_sampled(aba, single):
     print(f"[single] attend_full: {len(items)} query blocks, max abs err {err:.3g}")
 
 
+@pytest.mark.parametrize("w", [RAGGED, BATCH2], ids=lambda w: w.name)
 @pytest.mark.parametrize("key_block", [128, 4])
-def test_padding_rows_are_ignored(aba, key_block):
+def test_padding_rows_are_ignored(aba, key_block, w):
     """Rows >= N of q, k and v may hold anything (NaN, inf, huge values): scores,
-    lists, sparse and dense outputs are bitwise those of zero padding."""
-    w = RAGGED
+    lists, sparse and dense outputs are bitwise those of zero padding (both dense
+    workgroup shapes: an odd and an even number of query blocks per head)."""
     (q, k, v), (qd, kd, vd) = inputs(w, 17)
     N = w.seq_len
     p = aba.plan(w.batch, w.heads, N, w.head_dim, w.dtype, 8, 10, w.budget() if key_block == 128 else 64,
