@@ -448,12 +448,18 @@ __device__ __forceinline__ void attend_bf16_body(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qwave = wave % kWaves;   // the wavefront's 32 rows within its query block
     const int l32 = lane & 31, half = lane >> 5;
-    // (b*H + h) * NB + query block; sparse lists run longest first within each range
-    // of the order (see mapped_slot)
+    // QB = 1: blk = (b*H + h) * NB + query block; sparse lists run longest first
+    // within each range of the order (see mapped_slot).  QB = 2: slot = (b*H + h) *
+    // ceil(NB / 2) + pair p, query blocks 2p and 2p + 1 of that head.  When NB is
+    // odd the head's last pair has no second query block: its wavefronts still
+    // copy their share of K and V and meet every barrier, but compute and store
+    // nothing.
     const int slot = mapped_slot(xcd_ranges);
-    const int blk = full ? slot * QB + wave / kWaves : order[slot];
-    const int qb = blk % NB;
-    const long bh = blk / NB;
+    const int blk = QB == 1 ? (full ? slot : order[slot]) : 0;
+    const int np = (NB + 1) / 2;
+    const long bh = QB == 1 ? blk / NB : slot / np;
+    const int qb = QB == 1 ? blk % NB : 2 * (slot % np) + wave / kWaves;
+    const bool active = QB == 1 || qb < NB;   // uniform over the wavefront
     const uint16_t *qh = q + bh * N_pad * D;
     const int4v rk = head_rsrc(k + bh * N_pad * D, N_pad * D * 2);
     const int4v rv = head_rsrc(vt + bh * N_pad * D, (v_rows<D>() ? N : N_pad) * D * 2);
@@ -640,12 +646,12 @@ __device__ __forceinline__ void attend_bf16_body(
         // first half: V of the second half, K of the next entry's first half
         if (ce_hi) issue_v<D, W>(rv, ce.j * kBlock + kSub, vptr(1), wave, dma);
         if (ne_ok) issue_k<D, W>(rk, ne.j * kBlock, kptr((2 * E3 + 2) % 3), wave, dma);
-        if (ce.j >= 0) tile(kptr(k0), vptr(0), ce.j * kBlock, ce.lw);
+        if (ce.j >= 0 && active) tile(kptr(k0), vptr(0), ce.j * kBlock, ce.lw);
         if (ne_ok) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
         // second half: V of the next entry's first half, K of its second half
         if (ne_ok) issue_v<D, W>(rv, ne.j * kBlock, vptr(0), wave, dma);
         if (ne_hi) issue_k<D, W>(rk, ne.j * kBlock + kSub, kptr((2 * E3 + 3) % 3), wave, dma);
-        if (ce_hi) tile(kptr(k1), vptr(1), ce.j * kBlock + kSub, ce.lw);
+        if (ce_hi && active) tile(kptr(k1), vptr(1), ce.j * kBlock + kSub, ce.lw);
         if (ne_hi) wait_loads_and_sync<KL>(); else wait_loads_and_sync<0>();
         ce = ne;
         ne = nn;
@@ -663,6 +669,7 @@ __device__ __forceinline__ void attend_bf16_body(
     const auto lr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
     const float lsum = __uint_as_float(lr[0]) + __uint_as_float(lr[1]);
     const float inv = (lsum > 0.f && qvalid) ? 1.f / lsum : 0.f;
+    if (!active) return;
     uint16_t *orow = out + (bh * N_pad + qrow) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -680,8 +687,7 @@ __device__ __forceinline__ void attend_bf16_body(
 }
 
 
-// One query block per workgroup: sparse lists, and dense at an odd number of
-// query blocks per head.
+// One query block per workgroup: sparse lists, and dense at head_dim 64.
 template <int D, bool full>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
@@ -692,8 +698,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     attend_bf16_body<D, full, 1>(q, k, vt, idx, cnt, w, order, out, N, N_pad, NB, cap, scale_log2, xcd_ranges);
 }
 
-// Dense, two query blocks of one head per workgroup (an even number of query
-// blocks per head): they share the K and V staging.
+// Dense, two query blocks of one head per workgroup: they share the K and V
+// staging (the last pair of a head with an odd number of query blocks has one).
 template <int D>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_dense_pair_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
@@ -1263,10 +1269,9 @@ hipError_t launch_attend_t(const void *q, const void *k, const void *v, int dtyp
             order = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + vt_bytes(B, H, N_pad, D));
             order_kernel<<<dim3(8), dim3(kOrderThreads), 0, s>>>(cnt, G, cap, 1, order);
         }
-        if (D == 128 && full && NB % 2 == 0) {
-            // dense, an even number of query blocks per head: two query blocks of
-            // one head per workgroup share the K and V staging
-            attend_dense_pair_kernel<128><<<dim3((unsigned)(G / 2)), dim3(2 * kThreads), 0, s>>>(
+        if (D == 128 && full) {
+            // dense: two query blocks of one head per workgroup share the K and V staging
+            attend_dense_pair_kernel<128><<<dim3((unsigned)((long)B * H * ((NB + 1) / 2))), dim3(2 * kThreads), 0, s>>>(
                 (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)out, N, N_pad, NB, sl2,
                 attend_xcd_ranges(B, H, N_pad, D));
         } else if (D == 128) {
